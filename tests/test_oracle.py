@@ -1,0 +1,370 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: each test checks it against a
+printed figure, a hand-derived value, a library routine (numpy / torch number
+conversions), an algebraic invariant of the trellis, or exhaustive search.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LUT = workload.lut_fp16(0)
+
+
+def golden_rows(name: str) -> list[list[str]]:
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def lut_pair(idx: int, neg: int) -> tuple[int, int]:
+    p0, p1 = int(LUT[idx, 0]), int(LUT[idx, 1])
+    if neg:
+        p0 ^= 0x8000
+        p1 ^= 0x8000
+    return p0, p1
+
+
+# ---------------------------------------------------------------------------
+# storage: b + 16/d bits per parameter (onedev.kr, "How it works")
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("kv", [3, 4, 5, 6])
+def test_record_size_is_rate_plus_one_scale(d, kv):
+    R = oracle.record_bytes(d, kv)
+    b = kv / 2  # V = 2 outputs per kv-bit step
+    assert R * 8 == b * d + 16
+    assert R * 8 / d == pytest.approx(b + 16 / d, abs=0)
+
+
+def test_record_sizes_of_the_workloads():
+    assert [oracle.record_bytes(64, 4), oracle.record_bytes(256, 4), oracle.record_bytes(512, 4)] == [18, 66, 130]
+    assert [oracle.record_bytes(512, kv) for kv in (3, 4, 5, 6)] == [98, 130, 162, 194]
+    # whole-byte codes only for records
+    assert oracle.record_bytes(10, 4) == 0 and oracle.code_bits(10, 4) == 20
+    assert oracle.code_bits(6, 4) == 0  # fewer code bits than one window
+
+
+def test_storage_figures_printed_on_the_pages():
+    g = {k: float(v) for k, v in golden_rows("storage.txt")}
+    ratio = g["original_gb"] / g["cp_gb"]
+    # an FP8 table at b + 16/d bits per parameter shrinks by 8/(2 + 16/d) < 4,
+    # approaching 4 for long rows: the printed 202.7 -> 50.7 GB is just under 4x
+    for d in (64, 256, 512, 4096):
+        r = g["original_bits_per_param"] / (oracle.record_bytes(d, 4) * 8 / d)
+        assert 3.5 < r < 4.0
+        # against 16-bit originals the same code gives just under 8x
+        assert 7.0 < 2 * r < 8.0
+    assert 3.9 < ratio <= 4.0
+    assert g["compression_low"] <= ratio * (1 + 1e-3) and 2 * ratio <= g["compression_high"]
+    # 50.7 GB over 4 GPUs is the 12.7 GB per GPU the pages print, and the one-GPU
+    # workload's 97,690,000 records of 130 bytes reproduce it
+    assert g["cp_gb"] / g["gpus"] == pytest.approx(g["per_gpu_gb_4gpu"], abs=0.05)
+    cfg = workload.CONFIGS["gpu_d512"]
+    assert cfg.rows * oracle.record_bytes(512, 4) / 1e9 == pytest.approx(g["per_gpu_gb_4gpu"], abs=0.01)
+
+
+# ---------------------------------------------------------------------------
+# number formats: against numpy / torch conversions
+# ---------------------------------------------------------------------------
+
+def test_fp16_values_match_numpy_exhaustively():
+    vals = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float64)
+    got = np.array([oracle.fp16_to_double(h) for h in range(65536)])
+    same = (got == vals) | (np.isnan(got) & np.isnan(vals))
+    assert same.all()
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0])
+
+
+def test_bf16_values_match_torch_exhaustively():
+    ref = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16_to_double(b) for b in range(65536)])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+    # every finite pattern survives value -> bf16
+    back = np.array([oracle.bf16_from_double(v) for v in got])
+    finite = ~np.isnan(got)
+    assert (back[finite] == np.arange(65536)[finite]).all()
+
+
+def test_bf16_rounding_matches_torch_on_float32_inputs():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32)
+    # force exact ties on a third of them, and subnormals on some
+    bits[::3] = (bits[::3] & 0xFFFF0000) | 0x8000
+    bits[1::7] &= 0x807FFFFF
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_from_double(float(v)) for v in x], dtype=np.uint16)
+    assert (got == ref).all()
+
+
+def test_bf16_rounding_is_single_from_the_exact_value():
+    # 1 + 2^-8 + 2^-30 lies above the midpoint of 1 and 1 + 2^-7; a detour
+    # through float32 would make it a tie and round down to 1.0
+    assert oracle.bf16_from_double(1 + 2**-8 + 2**-30) == 0x3F81
+    assert oracle.bf16_from_double(1 + 2**-8) == 0x3F80          # tie -> even
+    assert oracle.bf16_from_double(1 + 3 * 2**-8) == 0x3F82      # tie -> even (up)
+    assert oracle.bf16_from_double(-0.0) == 0x8000
+    assert oracle.bf16_from_double(2.0**-133) == 0x0001          # smallest subnormal
+    assert oracle.bf16_from_double(2.0**-134) == 0x0000          # tie -> even (zero)
+    assert oracle.bf16_from_double(3 * 2.0**-134) == 0x0002      # tie -> even (up)
+    assert oracle.bf16_from_double(3.4e38) == 0x7F80             # rounds past the largest finite
+    assert oracle.bf16_from_double(float.fromhex("0x1.fep127")) == 0x7F7F
+
+
+# ---------------------------------------------------------------------------
+# the trellis rule: hand-derived windows and closed forms
+# ---------------------------------------------------------------------------
+
+def test_worked_windows():
+    for d, kv, code_hex, t, s_hex, idx, neg in golden_rows("worked_windows.txt"):
+        d, kv, t, idx, neg = int(d), int(kv), int(t), int(idx), int(neg)
+        code = np.frombuffer(bytes.fromhex(code_hex), dtype=np.uint8)
+        s = oracle.window(code, d, kv, t)
+        assert s == int(s_hex, 16), (code_hex, t)
+        assert oracle.hash_window(s) == (idx, neg)
+        f = oracle.decode_code(LUT, code, d, kv)
+        assert (int(f[2 * t]), int(f[2 * t + 1])) == lut_pair(idx, neg)
+
+
+@pytest.mark.parametrize("d", [64, 512])
+def test_constant_nibble_codes_give_one_pair(d):
+    for p, idx, neg in golden_rows("constant_codes_kv4.txt"):
+        p, idx, neg = int(p), int(idx), int(neg)
+        code = np.full(d // 4, p | (p << 4), dtype=np.uint8)
+        f = oracle.decode_code(LUT, code, d, 4)
+        p0, p1 = lut_pair(idx, neg)
+        assert (f[0::2] == p0).all() and (f[1::2] == p1).all(), p
+
+
+def test_hash_invariants_exhaustive():
+    idx = np.empty(65536, dtype=np.int64)
+    neg = np.empty(65536, dtype=np.int64)
+    for s in range(65536):
+        idx[s], neg[s] = oracle.hash_window(s)
+    # every output index is reached by 128 windows, every signed output by 64
+    assert (np.bincount(idx, minlength=512) == 128).all()
+    assert (np.bincount(idx * 2 + neg, minlength=1024) == 64).all()
+    s = np.arange(65536)
+    # flipping the top bit flips the sign and bit 8 of the index
+    assert (idx[s ^ 0x8000] == idx ^ 256).all() and (neg[s ^ 0x8000] == 1 - neg).all()
+    # the complement window selects the same entry with the other sign
+    assert (idx[s ^ 0xFFFF] == idx).all() and (neg[s ^ 0xFFFF] == 1 - neg).all()
+    # negation is bit 15 of the window
+    assert (neg == (s >> 15)).all()
+
+
+def _code_int(code: np.ndarray) -> int:
+    return int.from_bytes(code.tobytes(), "little")
+
+
+def _int_code(v: int, nbytes: int) -> np.ndarray:
+    return np.frombuffer(v.to_bytes(nbytes, "little"), dtype=np.uint8).copy()
+
+
+shapes = st.sampled_from([(16, 4), (32, 3), (64, 4), (64, 3), (64, 5), (64, 6), (128, 5),
+                          (256, 4), (512, 3), (512, 6)])
+
+
+@settings(max_examples=60, deadline=None)
+@given(shape=shapes, seed=st.integers(0, 2**32 - 1))
+def test_complement_code_negates_the_row(shape, seed):
+    d, kv = shape
+    nb = oracle.code_bits(d, kv) // 8
+    code = np.random.default_rng(seed).integers(0, 256, nb, dtype=np.uint8)
+    f = oracle.decode_code(LUT, code, d, kv)
+    g = oracle.decode_code(LUT, code ^ 0xFF, d, kv)
+    assert (g == (f ^ 0x8000)).all()
+
+
+@settings(max_examples=60, deadline=None)
+@given(shape=shapes, seed=st.integers(0, 2**32 - 1), r=st.integers(0, 300))
+def test_rotating_the_code_rotates_the_row(shape, seed, r):
+    # tail-biting: the trellis has no start; rotating the code by whole steps
+    # rotates the output by the same number of steps
+    d, kv = shape
+    N = oracle.code_bits(d, kv)
+    T = d // 2
+    r %= T
+    code = np.random.default_rng(seed).integers(0, 256, N // 8, dtype=np.uint8)
+    v = _code_int(code)
+    sh = kv * r
+    rot = ((v >> sh) | (v << (N - sh))) & ((1 << N) - 1)
+    f = oracle.decode_code(LUT, code, d, kv)
+    g = oracle.decode_code(LUT, _int_code(rot, N // 8), d, kv)
+    assert (g == np.roll(f, -2 * r)).all()
+
+
+def test_single_bit_touches_only_its_windows():
+    # a bitshift trellis: code bit j enters exactly the 16 / kv windows that
+    # cover it, i.e. steps whose window [kv(t+1)-16, kv(t+1)) contains j
+    for d, kv in [(64, 4), (64, 3), (512, 6)]:
+        N = oracle.code_bits(d, kv)
+        base = np.zeros(N // 8, dtype=np.uint8)
+        f0 = oracle.decode_code(LUT, base, d, kv)
+        for j in (0, 1, N // 2 + 3, N - 1):
+            c = base.copy()
+            c[j >> 3] |= 1 << (j & 7)
+            f1 = oracle.decode_code(LUT, c, d, kv)
+            changed = set(np.nonzero((f1 != f0).reshape(-1, 2).any(axis=1))[0].tolist())
+            covering = {t for t in range(d // 2)
+                        if any(((kv * (t + 1) - 16 + m) % N) == j for m in range(16))}
+            assert changed <= covering
+            assert len(covering) in (16 // kv, 16 // kv + 1)
+
+
+# ---------------------------------------------------------------------------
+# scaled rows: exact product, one round-to-nearest-even (against torch)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,kv", [(64, 4), (256, 4), (512, 3), (512, 6)])
+def test_scaled_rows_match_torch_fp32_product(d, kv):
+    recs = workload.random_records(64, d, kv, seed=11)
+    nb = oracle.code_bits(d, kv) // 8
+    # include a few special scales: 1, a power of two, negative, zero
+    specials = [0x3F80, 0x4100, 0xBF00, 0x0000, 0x8000]
+    for i, a in enumerate(specials):
+        recs[i, nb] = a & 0xFF
+        recs[i, nb + 1] = a >> 8
+    for rec in recs:
+        y = oracle.decode_record(LUT, rec, d, kv)
+        f = torch.from_numpy(oracle.decode_code(LUT, rec[:nb], d, kv).astype(np.int16)).view(torch.float16)
+        a = int(rec[nb]) | (int(rec[nb + 1]) << 8)
+        alpha = torch.tensor([a], dtype=torch.int32).to(torch.int16).view(torch.bfloat16).float()
+        ref = (f.float() * alpha).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert (y == ref).all()
+
+
+# ---------------------------------------------------------------------------
+# the lookup: requested rows, in the original order
+# ---------------------------------------------------------------------------
+
+def test_lookup_returns_requested_rows_in_order():
+    d, kv, rows = 64, 4, 300
+    recs = workload.random_records(rows, d, kv, seed=12)
+    ids = np.array([5, 299, 0, 5, 5, 17, -1, 300, 1 << 40, 123, 0], dtype=np.int64)
+    for raw in (False, True):
+        out, bad = oracle.lookup_decode(LUT, recs, rows, d, kv, ids, raw=raw, nthreads=3)
+        assert bad == 3
+        for j, i in enumerate(ids):
+            if 0 <= i < rows:
+                exp = (oracle.decode_code(LUT, recs[i, : kv * d // 16], d, kv) if raw
+                       else oracle.decode_record(LUT, recs[i], d, kv))
+                assert (out[j] == exp).all()
+            else:
+                assert (out[j] == 0).all()
+    out, bad = oracle.lookup_decode(LUT, recs, rows, d, kv, np.zeros(0, np.int64))
+    assert out.shape == (0, d) and bad == 0
+
+
+def test_lookup_reads_only_its_own_record():
+    # records are independently addressable: garbage in the neighbours of a
+    # record does not change its row
+    d, kv, rows = 256, 4, 9
+    recs = workload.random_records(rows, d, kv, seed=13)
+    ids = np.array([4], dtype=np.int64)
+    a, _ = oracle.lookup_decode(LUT, recs, rows, d, kv, ids)
+    recs2 = recs.copy()
+    recs2[3] ^= 0xA5
+    recs2[5] ^= 0x5A
+    b, _ = oracle.lookup_decode(LUT, recs2, rows, d, kv, ids)
+    assert (a == b).all()
+
+
+# ---------------------------------------------------------------------------
+# encoder: brute force, planted codewords, tail-biting, the norm rule
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,kv", [(8, 4), (10, 4), (12, 4), (12, 3), (16, 3), (8, 5), (8, 6)])
+def test_exact_tcq_equals_exhaustive_search(d, kv):
+    rng = np.random.default_rng(1000 + 10 * d + kv)
+    for _ in range(2):
+        z = rng.standard_normal(d)
+        best, _ = oracle.bruteforce_min(z, d, kv, LUT)
+        enc = oracle.tcq_encode(z, d, kv, LUT, oracle.ENC_EXACT)
+        assert enc.certified
+        assert enc.cost == pytest.approx(best, rel=1e-12, abs=1e-15)
+        # the path metric is the distortion of the code as the decoder reads it
+        assert oracle.distortion(z, LUT, enc.code, d, kv) == pytest.approx(enc.cost, rel=1e-12)
+        heur = oracle.tcq_encode(z, d, kv, LUT, oracle.ENC_HEURISTIC)
+        assert heur.cost >= best * (1 - 1e-12)
+        assert oracle.distortion(z, LUT, heur.code, d, kv) == pytest.approx(heur.cost, rel=1e-12)
+
+
+@pytest.mark.parametrize("d,kv,mode", [(64, 4, oracle.ENC_EXACT), (64, 3, oracle.ENC_EXACT),
+                                       (256, 4, oracle.ENC_HEURISTIC),
+                                       (512, 6, oracle.ENC_HEURISTIC)])
+def test_planted_codeword_is_recovered(d, kv, mode):
+    rng = np.random.default_rng(d + kv)
+    N = oracle.code_bits(d, kv)
+    code = rng.integers(0, 256, N // 8, dtype=np.uint8)
+    z = np.array([oracle.fp16_to_double(h) for h in oracle.decode_code(LUT, code, d, kv)])
+    enc = oracle.tcq_encode(z, d, kv, LUT, mode)
+    assert enc.cost == 0.0
+    z2 = np.array([oracle.fp16_to_double(h) for h in oracle.decode_code(LUT, enc.code, d, kv)])
+    assert (z2 == z).all()
+
+
+@pytest.mark.parametrize("d,kv", [(64, 4), (256, 4), (64, 6)])
+def test_heuristic_codes_are_consistent_tail_biting_paths(d, kv):
+    rng = np.random.default_rng(3)
+    for _ in range(3):
+        z = rng.standard_normal(d)
+        enc = oracle.tcq_encode(z, d, kv, LUT, oracle.ENC_HEURISTIC)
+        assert oracle.distortion(z, LUT, enc.code, d, kv) == pytest.approx(enc.cost, rel=1e-12)
+        ex = oracle.tcq_encode(z, d, kv, LUT, oracle.ENC_EXACT, max_starts=4)
+        assert ex.cost <= enc.cost
+        assert oracle.distortion(z, LUT, ex.code, d, kv) == pytest.approx(ex.cost, rel=1e-12)
+
+
+def test_norm_restoring_scale():
+    # alpha = ||e|| / ||f(c)|| (onedev.kr, "How it differs"): with the exact
+    # alpha the rebuilt row has the original norm; with the stored bf16 alpha
+    # and bf16 outputs the norm is off by at most 2^-9 (alpha) + 2^-9 (outputs)
+    d, kv = 256, 4
+    e = workload.gaussian_rows(16, d, seed=21)
+    recs, infos = oracle.encode_rows(e, d, kv, LUT, oracle.ENC_HEURISTIC)
+    for i in range(e.shape[0]):
+        rec, _, alpha = oracle.encode_row(e[i], d, kv, LUT, oracle.ENC_HEURISTIC)
+        assert (rec == recs[i]).all()
+        nb = oracle.code_bits(d, kv) // 8
+        f = np.array([oracle.fp16_to_double(h) for h in oracle.decode_code(LUT, rec[:nb], d, kv)])
+        ne = np.linalg.norm(e[i])
+        assert np.linalg.norm(alpha * f) == pytest.approx(ne, rel=1e-12)
+        a_bits = int(rec[nb]) | (int(rec[nb + 1]) << 8)
+        assert a_bits == oracle.bf16_from_double(alpha)
+        y = np.array([oracle.bf16_to_double(b) for b in oracle.decode_record(LUT, rec, d, kv)])
+        assert abs(np.linalg.norm(y) / ne - 1) <= 2.0**-8
+
+
+def test_zero_row_encodes_to_zero_scale():
+    rec, info, alpha = oracle.encode_row(np.zeros(64), 64, 4, LUT)
+    assert alpha == 0.0 and (rec == 0).all()
+
+
+def test_distortion_between_rate_distortion_bound_and_scalar_quantiser():
+    # sanity of the encoder at 2 bits per element on N(0,1) data: per-element
+    # MSE of z above the Gaussian rate-distortion bound 2^-4 and below the
+    # 2-bit Lloyd-Max scalar quantiser's 0.1175
+    d, kv = 256, 4
+    e = workload.gaussian_rows(24, d, seed=22)
+    z = e / np.linalg.norm(e, axis=1, keepdims=True) * np.sqrt(d)
+    costs = [oracle.tcq_encode(zi, d, kv, LUT, oracle.ENC_HEURISTIC).cost for zi in z]
+    mse = float(np.mean(costs)) / d
+    assert 0.0625 < mse < 0.1175, mse

@@ -1,0 +1,237 @@
+"""Seeded synthetic inputs for Conditional Program (CP) lookup tables.
+
+This module only draws random numbers and lays bytes out in the record
+format; it holds none of the method's arithmetic (no trellis, no hash, no
+decoding, no scaling). The CPU oracle and the HIP library both take what it
+produces as plain inputs.
+
+Record format (the pages describe each row as an independently addressable
+record holding a code and one 16-bit scale; the byte layout is this
+library's choice): N/8 code bytes, then the scale as bf16 little endian,
+packed with no padding, N = kv * d / 2 code bits.
+
+Workloads stand in for the pages' lookup replay (a 4,096-token sequence, 48
+rows per token, 2 memory layers) whose text, tokenizer and trained tables are
+not available: ids are drawn Zipf(1.1) over a seeded permutation of the rows,
+table rows are N(0,1) directions times a lognormal(0, 0.5) norm, and the
+shared codebook is 512 x 2 N(0,1) values stored as fp16.
+"""
+from __future__ import annotations
+
+import hashlib
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+LUT_SEED = 0
+TOKENS, ROWS_PER_TOKEN, LAYERS = 4096, 48, 2
+REPLAY_IDS = TOKENS * ROWS_PER_TOKEN * LAYERS  # 393,216
+ZIPF_S = 1.1
+CHUNK_ROWS = 1 << 20
+
+
+def record_bytes(d: int, kv: int) -> int:
+    """Bytes of one packed record: kv*d/2 code bits, then a 2-byte scale."""
+    return kv * d // 16 + 2
+
+
+def lut_fp16(seed: int = LUT_SEED) -> np.ndarray:
+    """512 x 2 codebook entries drawn N(0,1), stored as fp16 bit patterns."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((512, 2)).astype(np.float16).view(np.uint16).copy()
+
+
+def gaussian_rows(n: int, d: int, seed: int) -> np.ndarray:
+    """n rows e = rho * g / ||g||, g ~ N(0, I_d), rho ~ LogNormal(0, 0.5)."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((n, d))
+    rho = rng.lognormal(0.0, 0.5, size=n)
+    return g / np.linalg.norm(g, axis=1, keepdims=True) * rho[:, None]
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 (ties to even) of each value's float32, as uint16."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def random_record_chunk(d: int, kv: int, seed: int, chunk: int, nrows: int) -> np.ndarray:
+    """Rows of chunk `chunk` (CHUNK_ROWS rows each) of a random-code table:
+    uniform code bytes (every bit string is a valid tail-biting code) and a
+    scale drawn LogNormal(0, 0.5) stored as bf16. Each chunk has its own
+    stream, so any chunk can be regenerated alone."""
+    nb = kv * d // 16
+    rng = np.random.default_rng([seed, chunk])
+    out = np.empty((nrows, nb + 2), dtype=np.uint8)
+    words = rng.integers(0, 2**64 - 1, size=(nrows * nb + 7) // 8, dtype=np.uint64,
+                         endpoint=True)
+    out[:, :nb] = words.view(np.uint8)[: nrows * nb].reshape(nrows, nb)
+    a = _bf16_bits(rng.lognormal(0.0, 0.5, size=nrows))
+    out[:, nb] = (a & 0xFF).astype(np.uint8)
+    out[:, nb + 1] = (a >> 8).astype(np.uint8)
+    return out
+
+
+def random_records(rows: int, d: int, kv: int, seed: int, first: int = 0,
+                   count: int | None = None, out: np.ndarray | None = None,
+                   threads: int | None = None) -> np.ndarray:
+    """Rows [first, first+count) of a random-code table, chunk-deterministic
+    (the bytes do not depend on first/count or on the thread count)."""
+    if count is None:
+        count = rows - first
+    R = record_bytes(d, kv)
+    if out is None:
+        out = np.empty((count, R), dtype=np.uint8)
+    assert out.shape == (count, R) and out.dtype == np.uint8
+    if count == 0:
+        return out
+    c_lo, c_hi = first // CHUNK_ROWS, (first + count - 1) // CHUNK_ROWS
+
+    def fill(c: int) -> None:
+        c0 = c * CHUNK_ROWS
+        blk = random_record_chunk(d, kv, seed, c, min(CHUNK_ROWS, rows - c0))
+        lo, hi = max(first, c0), min(first + count, c0 + blk.shape[0])
+        out[lo - first:hi - first] = blk[lo - c0:hi - c0]
+
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    if c_hi == c_lo or threads <= 1:
+        for c in range(c_lo, c_hi + 1):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, range(c_lo, c_hi + 1)))
+    return out
+
+
+_M64 = np.uint64(0xFFFFFFFFFFFFFFFF)
+
+
+def _mix64(x: np.ndarray) -> np.ndarray:
+    """A 64-bit finaliser (multiply / xor-shift) used as a Feistel round
+    function; any fixed keyed mixing would do."""
+    x = x ^ (x >> np.uint64(30))
+    x = x * np.uint64(0xBF58476D1CE4E5B9)
+    x = x ^ (x >> np.uint64(27))
+    x = x * np.uint64(0x94D049BB133111EB)
+    return x ^ (x >> np.uint64(31))
+
+
+def keyed_permutation(x: np.ndarray, rows: int, seed: int) -> np.ndarray:
+    """A seeded pseudo-random bijection of [0, rows), evaluated at x only: a
+    4-round balanced Feistel network on 2h bits (2^2h >= rows), cycle-walked
+    until the value falls inside [0, rows)."""
+    h = max(1, (int(rows - 1).bit_length() + 1) // 2)
+    mask = np.uint64((1 << h) - 1)
+    keys = np.random.default_rng([seed, 0x5EED]).integers(0, 2**63, size=4, dtype=np.uint64)
+    v = np.asarray(x, dtype=np.uint64).copy()
+    todo = np.ones(v.shape, dtype=bool)
+    with np.errstate(over="ignore"):
+        while todo.any():
+            w = v[todo]
+            left, right = w >> np.uint64(h), w & mask
+            for k in keys:
+                left, right = right, left ^ (_mix64(right ^ k) & mask)
+            w = (left << np.uint64(h)) | right
+            v[todo] = w
+            todo[todo] = w >= np.uint64(rows)
+    return v.astype(np.int64)
+
+
+def zipf_ids(rows: int, n: int, seed: int, s: float = ZIPF_S) -> np.ndarray:
+    """n ids: rank r ~ Zipf(s) truncated to [1, rows] by rejection, id =
+    perm(r - 1) for a seeded pseudo-random permutation perm of the rows."""
+    rng = np.random.default_rng(seed)
+    ranks = np.empty(0, dtype=np.int64)
+    while ranks.size < n:
+        draw = rng.zipf(s, size=n)
+        ranks = np.concatenate([ranks, draw[draw <= rows]])
+    return keyed_permutation(ranks[:n] - 1, rows, seed)
+
+
+def uniform_ids(rows: int, n: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, rows, size=n, dtype=np.int64)
+
+
+def ids_digest(ids: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(ids, dtype=np.int64).tobytes()).hexdigest()[:16]
+
+
+@dataclass(frozen=True)
+class TableConfig:
+    """One workload: a table shape, how its records are made, and its ids."""
+    name: str
+    rows: int
+    d: int
+    kv: int
+    table_seed: int
+    ids_kind: str              # "uniform" or "zipf"
+    n_ids: int
+    ids_seed: int
+    encoded_rows: int          # rows 0..encoded_rows-1 are oracle-encoded Gaussian rows
+    host_resident: bool = False
+    uniform_seed: int | None = None
+    description: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def R(self) -> int:
+        return record_bytes(self.d, self.kv)
+
+    @property
+    def table_bytes(self) -> int:
+        return self.rows * self.R
+
+    def ids(self) -> np.ndarray:
+        if self.ids_kind == "uniform":
+            return uniform_ids(self.rows, self.n_ids, self.ids_seed)
+        return zipf_ids(self.rows, self.n_ids, self.ids_seed)
+
+    def uniform_variant_ids(self) -> np.ndarray:
+        assert self.uniform_seed is not None
+        return uniform_ids(self.rows, self.n_ids, self.uniform_seed)
+
+
+CONFIGS = {
+    "tiny_d64": TableConfig(
+        "tiny_d64", 4096, 64, 4, 100, "uniform", 1024, 300, encoded_rows=4096,
+        description="4,096 x d64 table, every row TCQ-encoded; 1,024 uniform ids"),
+    "small_d256": TableConfig(
+        "small_d256", 1 << 20, 256, 4, 101, "zipf", REPLAY_IDS, 201, encoded_rows=1024,
+        description="1,048,576 x d256 table (66-byte records); 393,216-id Zipf(1.1) replay"),
+    "gpu_d512": TableConfig(
+        "gpu_d512", 97_690_000, 512, 4, 102, "zipf", REPLAY_IDS, 202, encoded_rows=0,
+        uniform_seed=302,
+        description="97,690,000 x d512 table (130-byte records, 12.70 GB in HBM); "
+                    "393,216-id Zipf(1.1) replay"),
+    "host_d512": TableConfig(
+        "host_d512", 97_690_000, 512, 4, 102, "zipf", REPLAY_IDS, 202, encoded_rows=0,
+        host_resident=True,
+        description="the 12.70 GB d512 table in pinned host memory, read over PCIe"),
+}
+for _kv in (3, 4, 5, 6):
+    CONFIGS[f"rate_d512_kv{_kv}"] = TableConfig(
+        f"rate_d512_kv{_kv}", 1 << 22, 512, _kv, 103, "zipf", REPLAY_IDS, 203,
+        encoded_rows=256,
+        description=f"4,194,304 x d512 table at {_kv} bits per step "
+                    f"({_kv / 2:g} bits per element)")
+
+
+def build_records(cfg: TableConfig, encode_fn=None, first: int = 0,
+                  count: int | None = None) -> np.ndarray:
+    """Records [first, first+count) of a config's table. Rows below
+    cfg.encoded_rows are produced by encode_fn(e[n, d]) -> uint8[n, R] (the
+    oracle's encoder, passed in by the caller); all other rows are random
+    codes. With encode_fn None, every row is a random code."""
+    if count is None:
+        count = cfg.rows - first
+    out = random_records(cfg.rows, cfg.d, cfg.kv, cfg.table_seed, first, count)
+    enc_hi = min(cfg.encoded_rows, first + count)
+    if encode_fn is not None and first < enc_hi:
+        e = gaussian_rows(cfg.encoded_rows, cfg.d, cfg.table_seed + 1000)
+        out[: enc_hi - first] = encode_fn(e[first:enc_hi])
+    return out
