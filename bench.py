@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the CP fused gather-and-decode on one GPU.
+
+Workload (default): the 393,216-lookup replay (4,096 tokens x 48 rows x 2
+memory layers, ids Zipf(1.1) over a permuted table) into the 97,690,000 x d512
+table of 130-byte records (12.70 GB, kv = 4, i.e. 2 bits per element plus one
+bf16 scale per row) resident in HBM. One step = one cp_lookup_decode call over
+the whole replay: gather every requested record, walk the trellis, scale, and
+write the 393,216 x 512 bf16 rows in lookup order.
+
+Prints one JSON line. value = decoded rows/s over the K timed steps (inputs
+resident in HBM before timing starts); roofline = effective bytes per launch
+(records read + bf16 rows written, n * (R + 2d)) over the average launch time
+measured with events on the launch stream, against the 8 TB/s HBM peak;
+cpu_baseline = the CPU oracle decoding a sample of the same replay.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decoded rows/s + effective GB/s (% of HBM peak), 393,216-lookup replay"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "trellis_coded_row_amd", "csrc", "cp_decode.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def read_counter_summary(config: str, ids_kind: str) -> dict | None:
+    """HBM traffic per launch from a committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"counters_gather_decode_{config}_{ids_kind}.txt")
+    if not os.path.exists(path):
+        return None
+    vals: dict[str, str] = {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#") and ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        fetch = float(vals["FETCH_SIZE_KiB_per_dispatch"]) * 1024 * float(vals["fetch_scale"])
+        write = float(vals["WRITE_SIZE_KiB_per_dispatch"]) * 1024 * float(vals["write_scale"])
+    except (KeyError, ValueError):
+        return None
+    return {"fetch_bytes": fetch, "write_bytes": write, "bytes": fetch + write, "file": os.path.basename(path)}
+
+
+def time_launches(fn, steps: int, torch, before=None):
+    """Runs fn() `steps` times on the current stream; returns (total ms of the
+    bracketed region, mean ms of the individual launches)."""
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for k in range(steps):
+        if before is not None:
+            before()
+        starts[k].record(stream)
+        fn()
+        ends[k].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return t0.elapsed_time(t1), sum(per) / len(per), per
+
+
+def probes(torch, mib: int = 1024) -> dict:
+    """Achievable HBM bandwidth of a plain copy and a plain fill (torch's own
+    kernels) of `mib` MiB, for context next to the 8 TB/s peak."""
+    n = mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.int32, device="cuda")
+    b = torch.empty(n, dtype=torch.int32, device="cuda")
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    _, copy_ms, _ = time_launches(lambda: b.copy_(a), 10, torch)
+    _, fill_ms, _ = time_launches(lambda: b.fill_(7), 10, torch)
+    nbytes = n * 4
+    out = {"copy_GBps": 2 * nbytes / copy_ms / 1e6, "fill_GBps": nbytes / fill_ms / 1e6, "MiB": mib}
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="gpu_d512",
+                    help="workload: gpu_d512 (default), host_d512, small_d256, rate_d512_kv{3,4,5,6}, tiny_d64")
+    ap.add_argument("--ids", default=None, choices=["zipf", "uniform", "slice96"],
+                    help="id stream (default: the config's own)")
+    ap.add_argument("--noncoherent", action="store_true", help="host_d512: non-coherent pinned memory")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time with L2/MALL flushed before every launch, and run copy/fill probes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "multi-GPU runs are not part of this build", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import trellis_coded_row_amd as cp
+    import workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    cfg = workload.CONFIGS[args.config]
+    ids_kind = args.ids or cfg.ids_kind
+    lut = workload.lut_fp16(0)
+
+    t_gen = time.time()
+    # every row a random code: the decode cost does not depend on how codes
+    # were chosen (any bit string is a valid tail-biting code)
+    records = workload.random_records(cfg.rows, cfg.d, cfg.kv, cfg.table_seed)
+    if ids_kind == "zipf":
+        ids_np = workload.zipf_ids(cfg.rows, cfg.n_ids, cfg.ids_seed)
+    elif ids_kind == "uniform":
+        ids_np = workload.uniform_ids(cfg.rows, cfg.n_ids, cfg.uniform_seed or cfg.ids_seed + 100)
+    else:
+        ids_np = workload.zipf_ids(cfg.rows, cfg.n_ids, cfg.ids_seed)[:96]
+    gen_s = time.time() - t_gen
+
+    residency = cp.CP_RESIDENCY_HOST_MAPPED if cfg.host_resident else cp.CP_RESIDENCY_DEVICE
+    flags = cp.CP_FLAG_HOST_NONCOHERENT if args.noncoherent else 0
+    t_up = time.time()
+    table = cp.Table(cfg.rows, cfg.d, cfg.kv, lut, residency=residency, flags=flags)
+    chunk = 1 << 22
+    for r0 in range(0, cfg.rows, chunk):
+        table.upload(records[r0:r0 + chunk], first_row=r0)
+    upload_s = time.time() - t_up
+
+    n = ids_np.shape[0]
+    ids = torch.from_numpy(ids_np).cuda()
+    out = torch.empty((n, cfg.d), dtype=torch.bfloat16, device="cuda")
+    step = lambda: table.lookup_decode(ids, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not table.check():
+        print("an id was out of range", file=sys.stderr)
+        return 1
+
+    # timed region: K steps back to back, bracketed by synchronisation
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    total_ms, launch_ms, per = time_launches(step, args.steps, torch)
+    wall_s = time.perf_counter() - wall0
+    ms_per_step = total_ms / args.steps
+
+    R = cfg.R
+    algo_bytes = n * (R + 2 * cfg.d)
+    rows_per_s = n * args.steps / (total_ms / 1e3)
+    achieved = algo_bytes / (launch_ms / 1e3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {n:,} lookups ({ids_kind} ids) into a {cfg.rows:,} x d{cfg.d} CP table, "
+                        f"{cfg.kv / 2:g} bits/element + bf16 scale ({R}-byte records, "
+                        f"{cfg.table_bytes / 1e9:.2f} GB, {'pinned host memory' if cfg.host_resident else 'HBM'})",
+            "rows": cfg.rows, "d": cfg.d, "bits_per_step": cfg.kv, "record_bytes": R, "lookups": n,
+            "ids": ids_kind, "ids_sha256_16": workload.ids_digest(ids_np),
+            "residency": "host" + ("-noncoherent" if args.noncoherent else "") if cfg.host_resident else "hbm",
+        },
+        "effective_GBps": n * (R + 2 * cfg.d) * args.steps / (total_ms / 1e3) / 1e9,
+        "pct_hbm_peak": 100.0 * n * (R + 2 * cfg.d) * args.steps / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+        "launch_ms_mean": launch_ms,
+        "launch_ms_min": min(per),
+        "launch_ms_max": max(per),
+        "wall_s_timed_region": wall_s,
+        "setup_s": {"generate": round(gen_s, 2), "upload": round(upload_s, 2)},
+    }
+    if cfg.host_resident:
+        # the records cross PCIe: report that rate too (the HBM roofline does not bound it)
+        res["pcie_record_GBps"] = n * R / (launch_ms / 1e3) / 1e9
+    counters = read_counter_summary(cfg.name, ids_kind)
+    res["roofline"] = {
+        "bound": "hbm",
+        "achieved": achieved,
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": achieved / HBM_PEAK_GBPS,
+        "traffic": counters["bytes"] if counters else None,
+        "algorithmic_bytes_per_launch": algo_bytes,
+        "kernel": f"gather_decode<{cfg.d},{cfg.kv}>",
+    }
+
+    if args.extra:
+        flush = torch.empty(512 << 18, dtype=torch.int32, device="cuda")  # 512 MiB > L2 + MALL
+        _, flushed_ms, _ = time_launches(step, max(5, args.steps // 2), torch, before=lambda: flush.fill_(0))
+        res["flushed_launch_ms_mean"] = flushed_ms
+        res["flushed_rows_per_s"] = n / (flushed_ms / 1e3)
+        res["flushed_pct_hbm_peak"] = 100.0 * algo_bytes / (flushed_ms / 1e3) / 1e9 / HBM_PEAK_GBPS
+        del flush
+        torch.cuda.empty_cache()
+        res["probes"] = probes(torch)
+
+    if not args.no_cpu_baseline:
+        import oracle  # CPU baseline leg only
+
+        threads = max(1, min(16, os.cpu_count() or 1))
+        cal = min(n, 2048)
+        t = time.perf_counter()
+        oracle.lookup_decode(lut, records, cfg.rows, cfg.d, cfg.kv, ids_np[:cal], nthreads=threads)
+        per_row = (time.perf_counter() - t) / cal
+        sample = int(min(n, max(cal, args.cpu_seconds / max(per_row, 1e-9))))
+        t = time.perf_counter()
+        exp, _ = oracle.lookup_decode(lut, records, cfg.rows, cfg.d, cfg.kv, ids_np[:sample], nthreads=threads)
+        cpu_s = time.perf_counter() - t
+        got = out[:sample].view(torch.int16).cpu().numpy().view(np.uint16)
+        res["cpu_baseline"] = {
+            "value": sample / cpu_s,
+            "unit": "rows/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {sample:,} of the {n:,} replay ids ({cpu_s:.1f} s, {threads} threads, "
+                      f"plain C oracle, bit-by-bit trellis walk, fp64 scaling)",
+            "gpu_rows_matching_oracle": int((got == exp).all(axis=1).sum()),
+        }
+    table.close()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

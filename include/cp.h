@@ -1,0 +1,153 @@
+/*
+ * cp.h - C interface of the Conditional Program (CP) row-decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * CP stores each row e_i of a hashed n-gram lookup table as an independently
+ * addressable record {c_i, alpha_i}: a short trellis code and one bf16 scale.
+ * One reconstruction rule f, shared by the whole table, rebuilds a requested
+ * row as e_hat_i = alpha_i * f(c_i); only the rows a batch asks for are
+ * fetched and decoded, and they come back in the order they were asked for.
+ *   - reconstruction and storage cost (b + 16/d bits per parameter):
+ *     "2비트 코드와 공유 트렐리스로 n-gram 룩업 테이블을 4~8배 압축한다"
+ *     (onedev.kr paper digest), section "How it works" (어떻게 동작하나);
+ *   - tail-biting Gaussian HYB bitshift trellis, no rotation, norm-restoring
+ *     scale, records fetched and decoded by a fused kernel and returned in
+ *     lookup order: same page, section "How it differs" (무엇과 다른가);
+ *   - the scale is a bf16: same page, section "How it is used" (어떻게 쓰나).
+ *
+ * The pages name the trellis but do not give its parameters. This library
+ * reads it as follows (the same reading is stated wherever it is used):
+ *   - d outputs per row, V = 2 outputs per step, T = d/2 steps, kv code bits
+ *     per step ("bits_per_step"; kv/2 bits per element), N = kv*T code bits;
+ *   - the code is one little-endian N-bit integer (bit j = bit j&7 of byte
+ *     j>>3); step t reads the 16-bit window s_t = bits [kv(t+1)-16, kv(t+1))
+ *     of the circular code, oldest bit lowest (tail-biting: indices mod N);
+ *   - h = (s*s + s) mod 2^32, idx = (h >> 7) & 511; outputs 2t and 2t+1 are
+ *     LUT[idx][0] and LUT[idx][1] (fp16), both negated when bit 15 of s is 1;
+ *   - e_hat = bf16_rne(alpha * f), the product formed exactly (bf16 x fp16
+ *     fits in fp32) and rounded once to nearest even.
+ *
+ * Record layout (this library's choice): N/8 code bytes, then alpha as a
+ * little-endian bf16; records packed back to back with no padding, record i
+ * at byte offset i * cp_record_bytes(d, kv).
+ *
+ * Error convention: every call returns a cp_status; nothing aborts. A status
+ * of CP_ERR_HIP keeps the HIP error code for cp_last_hip_error() (per
+ * thread). Ids outside [0, rows) do not fault: their output row is written
+ * as zeros (like a lookup into a removed table, which the pages use as a
+ * baseline, "How it is used") and a sticky per-table flag is raised, which
+ * cp_table_check() reports and clears.
+ *
+ * Threading: lookups only read the table and may run concurrently on any
+ * streams. cp_table_upload and cp_table_destroy must not overlap lookups on
+ * the same table; the caller synchronises.
+ */
+#ifndef CP_H
+#define CP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct cp_table cp_table; /* opaque; owned by the library */
+
+typedef enum {
+    CP_OK = 0,
+    CP_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, size mismatch, bad descriptor */
+    CP_ERR_UNSUPPORTED = 2,      /* (d, bits_per_step) has no compiled kernel */
+    CP_ERR_OUT_OF_MEMORY = 3,    /* device or pinned host allocation failed */
+    CP_ERR_HIP = 4,              /* a HIP runtime call failed; see cp_last_hip_error */
+    CP_ERR_ID_OUT_OF_RANGE = 5   /* reported by cp_table_check: some id was outside [0, rows) */
+} cp_status;
+
+typedef enum {
+    CP_RESIDENCY_DEVICE = 0,     /* records in device memory (HBM) */
+    CP_RESIDENCY_HOST_MAPPED = 1 /* records in pinned host memory, read by the kernel over PCIe */
+} cp_residency;
+
+enum {
+    /* with CP_RESIDENCY_HOST_MAPPED: allocate the pinned memory non-coherent,
+     * so the GPU may cache records it has read */
+    CP_FLAG_HOST_NONCOHERENT = 1u << 0
+};
+
+typedef struct {
+    uint32_t struct_size;   /* sizeof(cp_table_desc) */
+    uint32_t d;             /* outputs per row: 64, 128, 256 or 512 */
+    uint32_t bits_per_step; /* kv: 3, 4, 5 or 6 (1.5, 2, 2.5, 3 bits per element) */
+    uint32_t residency;     /* cp_residency */
+    uint64_t rows;          /* records in the table, >= 1 */
+    uint32_t flags;         /* CP_FLAG_* */
+    uint32_t reserved;      /* 0 */
+} cp_table_desc;
+
+/* Bytes of one record: kv*d/16 code bytes + 2 scale bytes, i.e. b + 16/d bits
+ * per parameter at b = kv/2 ("How it works"). Returns 0 when (d, kv) cannot
+ * form a whole-byte code of at least 16 bits. */
+uint64_t cp_record_bytes(uint32_t d, uint32_t bits_per_step);
+
+/* 1 when a kernel for (d, bits_per_step) is compiled in, else 0. */
+int cp_supported(uint32_t d, uint32_t bits_per_step);
+
+/* Creates a table on the current HIP device.
+ *   desc     - shape and residency; copied.
+ *   lut_fp16 - host pointer to the shared codebook, 512 x 2 fp16 bit patterns
+ *              (entry idx: lut_fp16[2*idx], lut_fp16[2*idx+1]); copied.
+ *   out      - receives the table handle (NULL on failure).
+ * The records are uninitialised until cp_table_upload fills them; device
+ * memory is rows * R bytes (+ a small zeroed tail), pinned host memory the
+ * same for CP_RESIDENCY_HOST_MAPPED.
+ * Errors: INVALID_ARGUMENT (NULL pointers, struct_size, rows == 0, unknown
+ * residency or flags), UNSUPPORTED, OUT_OF_MEMORY, HIP. */
+cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, cp_table **out);
+
+/* Copies records [first_row, first_row + nrows) from host memory `src`
+ * (nrows * R bytes, packed records) into the table. Synchronous: the data
+ * has landed when it returns. nrows == 0 is a no-op.
+ * Errors: INVALID_ARGUMENT (NULL table/src, range beyond rows), HIP. */
+cp_status cp_table_upload(cp_table *table, uint64_t first_row, uint64_t nrows, const void *src);
+
+/* The hot path: for j in [0, n), out[j][0..d) = bf16 bits of
+ * alpha_{ids[j]} * f(c_{ids[j]}) ("How it works", "How it differs").
+ *   ids    - device-accessible int64[n], row ids in lookup order; read only.
+ *   out    - device-accessible uint16[n][d] (bf16 bit patterns), row-major,
+ *            16-byte aligned; fully overwritten.
+ *   stream - hipStream_t to launch on (NULL: the null stream). Asynchronous:
+ *            returns after the launch; synchronise the stream before reading.
+ * Duplicate ids decode once per occurrence. n == 0 launches nothing.
+ * Errors: INVALID_ARGUMENT (NULL table, NULL ids/out with n > 0, misaligned
+ * out), HIP (launch failure). Bad ids: see the error convention above. */
+cp_status cp_lookup_decode(const cp_table *table, const int64_t *ids, uint64_t n, uint16_t *out,
+                           void *stream);
+
+/* As cp_lookup_decode, but writes the unscaled f(c) as fp16 bit patterns
+ * (exactly the shared-codebook values, sign applied); used to check the
+ * trellis walk bit for bit. */
+cp_status cp_lookup_decode_raw(const cp_table *table, const int64_t *ids, uint64_t n,
+                               uint16_t *out_fp16, void *stream);
+
+/* Synchronises `stream`, then returns CP_ERR_ID_OUT_OF_RANGE and clears the
+ * table's flag if any lookup since the last check saw an id outside
+ * [0, rows); otherwise CP_OK. Errors: INVALID_ARGUMENT, HIP. */
+cp_status cp_table_check(cp_table *table, void *stream);
+
+/* Reads back the table's shape. Errors: INVALID_ARGUMENT. */
+cp_status cp_table_describe(const cp_table *table, cp_table_desc *desc_out);
+
+/* Frees the table (no pending lookups may use it). NULL is a no-op (CP_OK). */
+cp_status cp_table_destroy(cp_table *table);
+
+/* Static text for a status code. */
+const char *cp_status_string(cp_status status);
+
+/* hipError_t of the last CP_ERR_HIP on the calling thread (0 if none). */
+int cp_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_H */

@@ -1,0 +1,87 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times: every output of each 393,216-lookup replay is compared with
+the CPU oracle (raw f(c) bit-exact, scaled rows within 1 bf16 ulp)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import trellis_coded_row_amd as cp
+import workload
+from parity import check_lookup, make_table, say
+
+pytestmark = pytest.mark.gpu
+
+LUT = workload.lut_fp16(0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    torch.cuda.init()
+
+
+def encoder(cfg):
+    return lambda e: oracle.encode_rows(e, cfg.d, cfg.kv, LUT, oracle.ENC_HEURISTIC)[0]
+
+
+def test_small_d256_replay():
+    cfg = workload.CONFIGS["small_d256"]
+    say("building the 1,048,576 x d256 table")
+    recs = workload.build_records(cfg, encode_fn=encoder(cfg))
+    t = make_table(LUT, recs, cfg.d, cfg.kv)
+    try:
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), "small_d256 zipf replay")
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, np.arange(cfg.encoded_rows, dtype=np.int64),
+                     "small_d256 encoded rows")
+    finally:
+        t.close()
+
+
+@pytest.mark.parametrize("kv", [3, 4, 5, 6])
+def test_rate_sweep_replay(kv):
+    cfg = workload.CONFIGS[f"rate_d512_kv{kv}"]
+    say(f"building the 4,194,304 x d512 table at kv={kv}")
+    recs = workload.build_records(cfg, encode_fn=encoder(cfg))
+    t = make_table(LUT, recs, cfg.d, cfg.kv)
+    try:
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), f"rate kv{kv} zipf replay")
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, np.arange(cfg.encoded_rows, dtype=np.int64),
+                     f"rate kv{kv} encoded rows")
+    finally:
+        t.close()
+
+
+@pytest.fixture(scope="module")
+def big_records():
+    cfg = workload.CONFIGS["gpu_d512"]
+    say("generating the 97,690,000 x d512 records (12.70 GB)")
+    recs = workload.build_records(cfg)
+    yield cfg, recs
+    del recs
+
+
+def test_gpu_d512_replays(big_records):
+    cfg, recs = big_records
+    t = make_table(LUT, recs, cfg.d, cfg.kv)
+    try:
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), "gpu_d512 zipf replay")
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.uniform_variant_ids(), "gpu_d512 uniform replay")
+    finally:
+        t.close()
+        torch.cuda.empty_cache()
+
+
+def test_host_d512_replay(big_records):
+    cfg, recs = big_records
+    hcfg = workload.CONFIGS["host_d512"]
+    t = make_table(LUT, recs, cfg.d, cfg.kv, residency=cp.CP_RESIDENCY_HOST_MAPPED)
+    try:
+        ids = hcfg.ids()
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, ids, "host_d512 zipf replay")
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, ids[:96], "host_d512 one-token slice")
+    finally:
+        t.close()

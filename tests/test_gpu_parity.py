@@ -1,0 +1,144 @@
+"""GPU parity of the HIP gather-decode against the CPU oracle: every compiled
+(d, kv) instance, ragged batch sizes, alignment, order, duplicates, bad ids,
+record independence, and the 4,096 x d64 table of oracle-encoded rows."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import trellis_coded_row_amd as cp
+import workload
+from parity import assert_bf16_within_ulp, check_lookup, device_lookup, make_table, say
+
+pytestmark = pytest.mark.gpu
+
+LUT = workload.lut_fp16(0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    torch.cuda.init()
+
+
+@pytest.fixture(scope="module")
+def tiny_table():
+    cfg = workload.CONFIGS["tiny_d64"]
+    say("encoding the 4,096 x d64 table with the oracle")
+    recs = workload.build_records(
+        cfg, encode_fn=lambda e: oracle.encode_rows(e, cfg.d, cfg.kv, LUT, oracle.ENC_EXACT,
+                                                    max_starts=8)[0])
+    t = make_table(LUT, recs, cfg.d, cfg.kv)
+    yield cfg, recs, t
+    t.close()
+
+
+def test_tiny_d64_encoded_table(tiny_table):
+    cfg, recs, t = tiny_table
+    check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), "tiny_d64 uniform ids")
+    check_lookup(t, LUT, recs, cfg.d, cfg.kv, np.arange(cfg.rows, dtype=np.int64), "tiny_d64 every row")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("kv", [3, 4, 5, 6])
+def test_every_instance_ragged_batches(d, kv):
+    rows = 3001
+    recs = workload.random_records(rows, d, kv, seed=500 + d + kv)
+    t = make_table(LUT, recs, d, kv)
+    rng = np.random.default_rng(d * 10 + kv)
+    try:
+        for n in (1, 2, 7, 64, 1000, 4099):
+            ids = rng.integers(0, rows, n, dtype=np.int64)
+            check_lookup(t, LUT, recs, d, kv, ids, f"d{d} kv{kv} n{n}")
+    finally:
+        t.close()
+
+
+@pytest.mark.parametrize("d,kv", [(64, 4), (256, 4), (512, 4), (512, 3), (512, 6)])
+def test_order_duplicates_alignment_and_table_ends(d, kv):
+    rows = 1001  # odd: the last record starts at an offset = 2 (mod 4)
+    recs = workload.random_records(rows, d, kv, seed=600 + d + kv)
+    t = make_table(LUT, recs, d, kv)
+    try:
+        cases = {
+            "reversed": np.arange(rows - 1, -1, -1, dtype=np.int64),
+            "all same": np.full(777, 123, dtype=np.int64),
+            "ends": np.array([0, rows - 1, 1, rows - 2, rows - 1, 0], dtype=np.int64),
+            "odd ids": np.arange(1, rows, 2, dtype=np.int64),
+            "even ids": np.arange(0, rows, 2, dtype=np.int64),
+        }
+        for name, ids in cases.items():
+            check_lookup(t, LUT, recs, d, kv, ids, f"d{d} kv{kv} {name}")
+    finally:
+        t.close()
+
+
+@pytest.mark.parametrize("d,kv", [(64, 4), (512, 4), (512, 5)])
+def test_out_of_range_ids_give_zero_rows_and_raise_the_flag(d, kv):
+    rows = 200
+    recs = workload.random_records(rows, d, kv, seed=700 + d)
+    t = make_table(LUT, recs, d, kv)
+    try:
+        ids = np.array([3, -1, 199, 200, 2**62, 5, -(2**63), 7], dtype=np.int64)
+        check_lookup(t, LUT, recs, d, kv, ids, f"d{d} kv{kv} bad ids", expect_bad=4)
+        # the flag was cleared by the check: a clean batch reports clean
+        out = device_lookup(t, np.array([1, 2], dtype=np.int64))
+        assert out.shape == (2, d)
+        assert t.check()
+    finally:
+        t.close()
+
+
+def test_empty_batch_launches_nothing():
+    d, kv, rows = 512, 4, 10
+    recs = workload.random_records(rows, d, kv, seed=800)
+    t = make_table(LUT, recs, d, kv)
+    try:
+        ids = torch.empty(0, dtype=torch.int64, device="cuda")
+        out = t.lookup_decode(ids)
+        assert tuple(out.shape) == (0, d)
+        assert t.check()
+    finally:
+        t.close()
+
+
+def test_records_are_independent():
+    # poisoning the neighbours of a record (and everything else) leaves its row unchanged
+    d, kv, rows = 512, 4, 64
+    recs = workload.random_records(rows, d, kv, seed=900)
+    ids = np.array([31, 32, 33], dtype=np.int64)
+    t = make_table(LUT, recs, d, kv)
+    try:
+        before = device_lookup(t, ids)
+        poisoned = recs.copy()
+        keep = set(ids.tolist())
+        for r in range(rows):
+            if r not in keep:
+                poisoned[r] ^= 0xFF
+        t.upload(poisoned)
+        after = device_lookup(t, ids)
+        assert (before == after).all()
+        check_lookup(t, LUT, poisoned, d, kv, np.arange(rows, dtype=np.int64), "poisoned table")
+    finally:
+        t.close()
+
+
+def test_caller_stream_is_used():
+    d, kv, rows = 256, 4, 500
+    recs = workload.random_records(rows, d, kv, seed=901)
+    t = make_table(LUT, recs, d, kv)
+    try:
+        ids_np = np.random.default_rng(0).integers(0, rows, 5000, dtype=np.int64)
+        exp, _ = oracle.lookup_decode(LUT, recs, rows, d, kv, ids_np)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            ids = torch.from_numpy(ids_np).cuda()
+            out = t.lookup_decode(ids, stream=s)
+        s.synchronize()
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert_bf16_within_ulp(got, exp, "side stream")
+    finally:
+        t.close()

@@ -1,0 +1,259 @@
+"""Conditional Program (CP) row decode for AMD Instinct MI355X (gfx950).
+
+Python binding of ``libcp.so`` (C interface in ``include/cp.h``). This module
+only marshals arguments: every step of a lookup (record gather, trellis walk,
+codebook lookup, scaling, ordered write) runs in the library's HIP kernels.
+PyTorch supplies device memory and streams. There is no fallback: if the
+library cannot be loaded, importing this package raises.
+
+The functions below carry the C names; ``Table`` wraps them for torch
+tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+__all__ = [
+    "CPError", "Table", "load_library",
+    "cp_record_bytes", "cp_supported", "cp_table_create", "cp_table_upload", "cp_lookup_decode",
+    "cp_lookup_decode_raw", "cp_table_check", "cp_table_describe", "cp_table_destroy",
+    "cp_status_string", "cp_last_hip_error",
+    "CP_OK", "CP_ERR_INVALID_ARGUMENT", "CP_ERR_UNSUPPORTED", "CP_ERR_OUT_OF_MEMORY", "CP_ERR_HIP",
+    "CP_ERR_ID_OUT_OF_RANGE", "CP_RESIDENCY_DEVICE", "CP_RESIDENCY_HOST_MAPPED",
+    "CP_FLAG_HOST_NONCOHERENT",
+]
+
+CP_OK = 0
+CP_ERR_INVALID_ARGUMENT = 1
+CP_ERR_UNSUPPORTED = 2
+CP_ERR_OUT_OF_MEMORY = 3
+CP_ERR_HIP = 4
+CP_ERR_ID_OUT_OF_RANGE = 5
+CP_RESIDENCY_DEVICE = 0
+CP_RESIDENCY_HOST_MAPPED = 1
+CP_FLAG_HOST_NONCOHERENT = 1
+
+
+class cp_table_desc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("d", ctypes.c_uint32),
+        ("bits_per_step", ctypes.c_uint32),
+        ("residency", ctypes.c_uint32),
+        ("rows", ctypes.c_uint64),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+_lib: ctypes.CDLL | None = None
+
+
+def library_path() -> str:
+    # CP_LIBRARY lets a tuning run load a differently-built copy of the library
+    return os.environ.get("CP_LIBRARY") or _build.LIB
+
+
+def load_library() -> ctypes.CDLL:
+    """Loads libcp.so, building it first only if it does not exist."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        if path != _build.LIB:
+            raise ImportError(f"CP_LIBRARY={path} does not exist")
+        _build.build()
+    L = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    sig = {
+        "cp_record_bytes": (ctypes.c_uint64, [ctypes.c_uint32, ctypes.c_uint32]),
+        "cp_supported": (ctypes.c_int, [ctypes.c_uint32, ctypes.c_uint32]),
+        "cp_table_create": (ctypes.c_int, [ctypes.POINTER(cp_table_desc), vp, ctypes.POINTER(vp)]),
+        "cp_table_upload": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp]),
+        "cp_lookup_decode": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
+        "cp_lookup_decode_raw": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
+        "cp_table_check": (ctypes.c_int, [vp, vp]),
+        "cp_table_describe": (ctypes.c_int, [vp, ctypes.POINTER(cp_table_desc)]),
+        "cp_table_destroy": (ctypes.c_int, [vp]),
+        "cp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "cp_last_hip_error": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+_L = load_library()
+
+
+class CPError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = f"{what}: {cp_status_string(status)}"
+        if status == CP_ERR_HIP:
+            msg += f" (hipError {cp_last_hip_error()})"
+        super().__init__(msg)
+
+
+# --------------------------------------------------------------------------
+# the C functions, same names, raw pointers and integers
+# --------------------------------------------------------------------------
+
+def cp_record_bytes(d: int, bits_per_step: int) -> int:
+    return int(_L.cp_record_bytes(d, bits_per_step))
+
+
+def cp_supported(d: int, bits_per_step: int) -> bool:
+    return bool(_L.cp_supported(d, bits_per_step))
+
+
+def cp_table_create(desc: cp_table_desc, lut_ptr: int) -> tuple[int, int]:
+    """Returns (status, table handle or 0)."""
+    h = ctypes.c_void_p()
+    st = _L.cp_table_create(ctypes.byref(desc), lut_ptr, ctypes.byref(h))
+    return st, (h.value or 0)
+
+
+def cp_table_upload(table: int, first_row: int, nrows: int, src_ptr: int) -> int:
+    return _L.cp_table_upload(table, first_row, nrows, src_ptr)
+
+
+def cp_lookup_decode(table: int, ids_ptr: int, n: int, out_ptr: int, stream: int | None) -> int:
+    return _L.cp_lookup_decode(table, ids_ptr, n, out_ptr, stream)
+
+
+def cp_lookup_decode_raw(table: int, ids_ptr: int, n: int, out_ptr: int, stream: int | None) -> int:
+    return _L.cp_lookup_decode_raw(table, ids_ptr, n, out_ptr, stream)
+
+
+def cp_table_check(table: int, stream: int | None) -> int:
+    return _L.cp_table_check(table, stream)
+
+
+def cp_table_describe(table: int) -> tuple[int, cp_table_desc]:
+    desc = cp_table_desc()
+    st = _L.cp_table_describe(table, ctypes.byref(desc))
+    return st, desc
+
+
+def cp_table_destroy(table: int) -> int:
+    return _L.cp_table_destroy(table)
+
+
+def cp_status_string(status: int) -> str:
+    return _L.cp_status_string(status).decode()
+
+
+def cp_last_hip_error() -> int:
+    return int(_L.cp_last_hip_error())
+
+
+# --------------------------------------------------------------------------
+# torch convenience wrapper
+# --------------------------------------------------------------------------
+
+def _stream_handle(stream) -> int | None:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Table:
+    """A CP table on the current device (or in pinned host memory).
+
+    lut_fp16: uint16[512, 2] codebook bit patterns. Records are uploaded
+    with ``upload`` (packed bytes, ``record_bytes`` each)."""
+
+    def __init__(self, rows: int, d: int, bits_per_step: int, lut_fp16: np.ndarray,
+                 residency: int = CP_RESIDENCY_DEVICE, flags: int = 0):
+        lut = np.ascontiguousarray(lut_fp16, dtype=np.uint16).reshape(-1)
+        if lut.size != 1024:
+            raise ValueError("the codebook has 512 entries of 2 fp16 values")
+        desc = cp_table_desc(ctypes.sizeof(cp_table_desc), d, bits_per_step, residency, rows, flags, 0)
+        st, h = cp_table_create(desc, lut.ctypes.data)
+        if st != CP_OK:
+            raise CPError(st, "cp_table_create")
+        self.handle = h
+        self.rows, self.d, self.bits_per_step = rows, d, bits_per_step
+        self.residency = residency
+        self.record_bytes = cp_record_bytes(d, bits_per_step)
+
+    def upload(self, records: np.ndarray, first_row: int = 0) -> None:
+        rec = np.ascontiguousarray(records, dtype=np.uint8)
+        if rec.ndim != 2 or rec.shape[1] != self.record_bytes:
+            raise ValueError(f"records must be uint8[nrows, {self.record_bytes}]")
+        st = cp_table_upload(self.handle, first_row, rec.shape[0], rec.ctypes.data)
+        if st != CP_OK:
+            raise CPError(st, "cp_table_upload")
+
+    def _check_io(self, ids, out, dtype):
+        import torch
+
+        if not (ids.is_cuda and ids.dtype == torch.int64 and ids.dim() == 1 and ids.is_contiguous()):
+            raise ValueError("ids must be a contiguous 1-D int64 device tensor")
+        n = ids.shape[0]
+        if out is None:
+            out = torch.empty((n, self.d), dtype=dtype, device=ids.device)
+        if not (out.is_cuda and out.dtype == dtype and tuple(out.shape) == (n, self.d)
+                and out.is_contiguous()):
+            raise ValueError(f"out must be a contiguous {dtype} device tensor of shape ({n}, {self.d})")
+        return n, out
+
+    def lookup_decode(self, ids, out=None, stream=None):
+        """bf16[n, d]: alpha * f(c) of rows ids[j], in lookup order."""
+        import torch
+
+        n, out = self._check_io(ids, out, torch.bfloat16)
+        st = cp_lookup_decode(self.handle, ids.data_ptr(), n, out.data_ptr(), _stream_handle(stream))
+        if st != CP_OK:
+            raise CPError(st, "cp_lookup_decode")
+        return out
+
+    def lookup_decode_raw(self, ids, out=None, stream=None):
+        """fp16[n, d]: the unscaled f(c) of rows ids[j], in lookup order."""
+        import torch
+
+        n, out = self._check_io(ids, out, torch.float16)
+        st = cp_lookup_decode_raw(self.handle, ids.data_ptr(), n, out.data_ptr(), _stream_handle(stream))
+        if st != CP_OK:
+            raise CPError(st, "cp_lookup_decode_raw")
+        return out
+
+    def check(self, stream=None) -> bool:
+        """Synchronises; False (and the flag cleared) if an id was out of range."""
+        st = cp_table_check(self.handle, _stream_handle(stream))
+        if st == CP_ERR_ID_OUT_OF_RANGE:
+            return False
+        if st != CP_OK:
+            raise CPError(st, "cp_table_check")
+        return True
+
+    def close(self) -> None:
+        if getattr(self, "handle", 0):
+            st = cp_table_destroy(self.handle)
+            self.handle = 0
+            if st != CP_OK:
+                raise CPError(st, "cp_table_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

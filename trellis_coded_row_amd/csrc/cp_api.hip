@@ -1,0 +1,201 @@
+// cp_api.hip - the C ABI of the CP row-decode library (declared in
+// include/cp.h): argument checks, table memory, upload, launch, error flag.
+// All arithmetic of the lookup runs in the kernels of cp_decode.hip.
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/cp.h"
+#include "cp_internal.h"
+
+struct cp_table {
+    cp_table_desc desc;
+    uint64_t record_bytes;
+    uint64_t alloc_bytes;
+    uint8_t *records;      // hipMalloc'd (device) or hipHostMalloc'd (host)
+    uint8_t *records_dev;  // device-accessible address of the same memory
+    uint32_t *lut_dev;
+    int *err_dev;
+    int device;
+    int num_cus;
+};
+
+static thread_local int g_last_hip_error = 0;
+
+static cp_status hip_fail(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) ? CP_ERR_OUT_OF_MEMORY
+                                                                         : CP_ERR_HIP;
+}
+
+// Bytes after the last record that loads of the last record may touch
+// (aligned dwords straddling the record end); zeroed at creation.
+static const uint64_t kTailPad = 64;
+
+extern "C" {
+
+uint64_t cp_record_bytes(uint32_t d, uint32_t bits_per_step)
+{
+    if (d == 0 || (d & 1u) || bits_per_step < 1 || bits_per_step > 15) return 0;
+    const uint64_t nbits = (uint64_t)bits_per_step * (d / 2);
+    if (nbits < 16 || nbits % 8) return 0;
+    return nbits / 8 + 2;
+}
+
+int cp_supported(uint32_t d, uint32_t bits_per_step)
+{
+    return cp_record_bytes(d, bits_per_step) != 0 && cpk::supported(d, bits_per_step);
+}
+
+const char *cp_status_string(cp_status s)
+{
+    switch (s) {
+    case CP_OK: return "ok";
+    case CP_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case CP_ERR_UNSUPPORTED: return "unsupported (d, bits_per_step)";
+    case CP_ERR_OUT_OF_MEMORY: return "out of memory";
+    case CP_ERR_HIP: return "HIP runtime error";
+    case CP_ERR_ID_OUT_OF_RANGE: return "a lookup id was outside [0, rows)";
+    }
+    return "unknown status";
+}
+
+int cp_last_hip_error(void) { return g_last_hip_error; }
+
+static void release(cp_table *t)
+{
+    if (!t) return;
+    if (t->records) {
+        if (t->desc.residency == CP_RESIDENCY_HOST_MAPPED)
+            (void)hipHostFree(t->records);
+        else
+            (void)hipFree(t->records);
+    }
+    if (t->lut_dev) (void)hipFree(t->lut_dev);
+    if (t->err_dev) (void)hipFree(t->err_dev);
+    free(t);
+}
+
+cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, cp_table **out)
+{
+    if (out) *out = nullptr;
+    if (!desc || !lut_fp16 || !out) return CP_ERR_INVALID_ARGUMENT;
+    if (desc->struct_size != sizeof(cp_table_desc) || desc->rows == 0 || desc->reserved != 0)
+        return CP_ERR_INVALID_ARGUMENT;
+    if (desc->residency != CP_RESIDENCY_DEVICE && desc->residency != CP_RESIDENCY_HOST_MAPPED)
+        return CP_ERR_INVALID_ARGUMENT;
+    if (desc->flags & ~(uint32_t)CP_FLAG_HOST_NONCOHERENT) return CP_ERR_INVALID_ARGUMENT;
+    const uint64_t R = cp_record_bytes(desc->d, desc->bits_per_step);
+    if (R == 0) return CP_ERR_INVALID_ARGUMENT;
+    if (!cpk::supported(desc->d, desc->bits_per_step)) return CP_ERR_UNSUPPORTED;
+    if (desc->rows > (UINT64_MAX - kTailPad) / R) return CP_ERR_INVALID_ARGUMENT;
+
+    cp_table *t = (cp_table *)calloc(1, sizeof(cp_table));
+    if (!t) return CP_ERR_OUT_OF_MEMORY;
+    t->desc = *desc;
+    t->record_bytes = R;
+    t->alloc_bytes = desc->rows * R + kTailPad;
+
+    hipError_t e = hipGetDevice(&t->device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&t->num_cus, hipDeviceAttributeMultiprocessorCount, t->device);
+    if (e != hipSuccess) {
+        release(t);
+        return hip_fail(e);
+    }
+    if (desc->residency == CP_RESIDENCY_HOST_MAPPED) {
+        unsigned flags = hipHostMallocMapped;
+        if (desc->flags & CP_FLAG_HOST_NONCOHERENT) flags |= hipHostMallocNonCoherent;
+        e = hipHostMalloc((void **)&t->records, t->alloc_bytes, flags);
+        if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&t->records_dev, t->records, 0);
+        if (e == hipSuccess) memset(t->records + desc->rows * R, 0, kTailPad);
+    } else {
+        e = hipMalloc((void **)&t->records, t->alloc_bytes);
+        t->records_dev = t->records;
+        if (e == hipSuccess) e = hipMemset(t->records + desc->rows * R, 0, kTailPad);
+    }
+    if (e == hipSuccess) e = hipMalloc((void **)&t->lut_dev, 512 * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemcpy(t->lut_dev, lut_fp16, 512 * sizeof(uint32_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMalloc((void **)&t->err_dev, sizeof(int));
+    if (e == hipSuccess) e = hipMemset(t->err_dev, 0, sizeof(int));
+    if (e != hipSuccess) {
+        release(t);
+        return hip_fail(e);
+    }
+    *out = t;
+    return CP_OK;
+}
+
+cp_status cp_table_upload(cp_table *t, uint64_t first_row, uint64_t nrows, const void *src)
+{
+    if (!t) return CP_ERR_INVALID_ARGUMENT;
+    if (nrows == 0) return CP_OK;
+    if (!src || first_row > t->desc.rows || nrows > t->desc.rows - first_row)
+        return CP_ERR_INVALID_ARGUMENT;
+    const uint64_t off = first_row * t->record_bytes, bytes = nrows * t->record_bytes;
+    if (t->desc.residency == CP_RESIDENCY_HOST_MAPPED) {
+        memcpy(t->records + off, src, bytes);
+        return CP_OK;
+    }
+    hipError_t e = hipMemcpy(t->records + off, src, bytes, hipMemcpyHostToDevice);
+    return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
+static cp_status lookup(const cp_table *t, const int64_t *ids, uint64_t n, uint16_t *out, void *stream,
+                        bool raw)
+{
+    if (!t) return CP_ERR_INVALID_ARGUMENT;
+    if (n == 0) return CP_OK;
+    if (!ids || !out || ((uintptr_t)out & 15u) || ((uintptr_t)ids & 7u)) return CP_ERR_INVALID_ARGUMENT;
+    cpk::LaunchArgs a;
+    a.records = t->records_dev;
+    a.rows = t->desc.rows;
+    a.lut = t->lut_dev;
+    a.ids = ids;
+    a.n = n;
+    a.out = reinterpret_cast<uint32_t *>(out);
+    a.err = t->err_dev;
+    a.num_cus = t->num_cus;
+    a.stream = (hipStream_t)stream;
+    hipError_t e = cpk::launch(t->desc.d, t->desc.bits_per_step, raw, a);
+    return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
+cp_status cp_lookup_decode(const cp_table *t, const int64_t *ids, uint64_t n, uint16_t *out, void *stream)
+{
+    return lookup(t, ids, n, out, stream, false);
+}
+
+cp_status cp_lookup_decode_raw(const cp_table *t, const int64_t *ids, uint64_t n, uint16_t *out_fp16,
+                               void *stream)
+{
+    return lookup(t, ids, n, out_fp16, stream, true);
+}
+
+cp_status cp_table_check(cp_table *t, void *stream)
+{
+    if (!t) return CP_ERR_INVALID_ARGUMENT;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    int flag = 0;
+    if (e == hipSuccess) e = hipMemcpy(&flag, t->err_dev, sizeof(int), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && flag) e = hipMemset(t->err_dev, 0, sizeof(int));
+    if (e != hipSuccess) return hip_fail(e);
+    return flag ? CP_ERR_ID_OUT_OF_RANGE : CP_OK;
+}
+
+cp_status cp_table_describe(const cp_table *t, cp_table_desc *desc_out)
+{
+    if (!t || !desc_out) return CP_ERR_INVALID_ARGUMENT;
+    *desc_out = t->desc;
+    return CP_OK;
+}
+
+cp_status cp_table_destroy(cp_table *t)
+{
+    if (!t) return CP_OK;
+    hipError_t e = hipSetDevice(t->device);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    release(t);
+    return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,248 @@
+// cp_decode.hip - fused gather-and-decode of Conditional Program (CP) rows
+// for CDNA4 (gfx950).
+//
+// For every id of a lookup batch the kernel fetches that row's record (a
+// tail-biting trellis code and one bf16 scale), walks the shared trellis to
+// rebuild f(c), multiplies by the scale and writes the row at the id's
+// position in the batch. The pages describe exactly this fused step: only
+// requested records are fetched, restored by one kernel and handed on in the
+// original lookup order ("2비트 코드와 공유 트렐리스로 n-gram 룩업 테이블을
+// 4~8배 압축한다", onedev.kr, sections "How it works" and "How it differs").
+//
+// Trellis reading (the pages name a tail-biting Gaussian HYB bitshift trellis
+// without parameters): code = little-endian N-bit integer, N = kv * d / 2;
+// step t reads the 16-bit window of the circular code ending at bit kv(t+1);
+// h = s*s + s (mod 2^32), idx = (h >> 7) & 511, outputs 2t, 2t+1 =
+// LUT[idx] (fp16 pair), sign bits flipped when bit 15 of s is set; the row
+// is alpha * f rounded once to bf16 (nearest, ties to even).
+//
+// Work mapping (memory-bound gather + streaming write; no MFMA):
+//   - a row is handled by d/8 lanes (a full wave64 at d = 512); lane l makes
+//     outputs [8l, 8l+8): steps 4l .. 4l+3, one 16-byte store;
+//   - lane l loads the 4kv code bits its steps introduce (one aligned dword
+//     at kv = 4, two otherwise); the 16-kv older bits each window also needs
+//     come from the neighbouring lane(s) through a lane shuffle, circular
+//     within the row, which is exactly the tail-biting wrap;
+//   - records are 2-byte aligned (R = kv*d/16 + 2 is even), so every load is
+//     an aligned dword and bits are taken out with shifts;
+//   - the 2 KB codebook is staged in LDS once per workgroup, optionally
+//     replicated COPIES times so that lane k reads copy k % COPIES: with 32
+//     copies, lanes 0-31 and 32-63 hit 32 distinct banks whatever the
+//     indices are;
+//   - the grid is persistent (a few workgroups per CU) so the staging is paid
+//     once per workgroup; each wave sweeps U consecutive rows per group per
+//     iteration so record loads of several rows are in flight together;
+//   - outputs are written with nontemporal stores: they are not re-read, and
+//     keeping them out of the caches leaves room for hot (Zipf) records.
+#include <type_traits>
+
+#include "cp_internal.h"
+
+namespace cpk {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t ld32(const uint8_t *p)
+{
+    return *reinterpret_cast<const uint32_t *>(p);
+}
+
+// One output pair: e = LUT entry (fp16 lo = element 2t, hi = element 2t+1),
+// negmask = 0x80008000 when the window's bit 15 is set. Scaled: bf16 pair of
+// alpha * value; the product of a bf16 and an fp16 is exact in fp32 and the
+// conversion rounds to nearest even, which is symmetric in sign, so the sign
+// flip can be applied to the packed result.
+template <bool RAW>
+__device__ __forceinline__ uint32_t emit_pair(uint32_t e, uint32_t negmask, float alpha)
+{
+    if constexpr (RAW) {
+        return e ^ negmask;
+    } else {
+        f32x2 v;
+        v.x = alpha * (float)__builtin_bit_cast(_Float16, (uint16_t)(e & 0xFFFFu));
+        v.y = alpha * (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
+        bf16x2 b = __builtin_convertvector(v, bf16x2);
+        return __builtin_bit_cast(uint32_t, b) ^ negmask;
+    }
+}
+
+// Code bits a lane needs for its 4 windows: 16 + 3kv; they fit in 32 bits up
+// to kv = 5.
+template <int KV>
+using field_t = typename std::conditional<(16 + 3 * KV <= 32), uint32_t, uint64_t>::type;
+
+template <int D, int KV, bool RAW, int COPIES, int BLOCK, int U>
+__global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict__ tab, const uint64_t rows,
+                                                       const uint32_t *__restrict__ lut,
+                                                       const int64_t *__restrict__ ids, const uint64_t n,
+                                                       uint32_t *__restrict__ out, int *__restrict__ err)
+{
+    constexpr int LANES = D / 8;        // lanes per row
+    constexpr int GROUPS = 64 / LANES;  // rows per wave
+    constexpr int NB = KV * D / 16;     // code bytes per record
+    constexpr int R = NB + 2;           // record bytes
+    constexpr int M = 16 - KV;          // history bits of a window
+    constexpr int NEWB = 4 * KV;        // code bits introduced by one lane's 4 steps
+    constexpr int WAVES = BLOCK / 64;
+    static_assert(LANES >= 2 && LANES <= 64 && (LANES & (LANES - 1)) == 0, "d/8 lanes");
+    static_assert((KV * D) % 64 == 0, "code must be whole dwords");
+    static_assert(NEWB <= 32 && 2 * NEWB >= M, "history within two lanes");
+    static_assert(COPIES >= 1 && COPIES <= 64 && (COPIES & (COPIES - 1)) == 0, "LDS copies");
+    using F = field_t<KV>;
+
+    __shared__ uint32_t s_lut[512 * COPIES];
+    for (int i = threadIdx.x; i < 512 * COPIES; i += BLOCK) s_lut[i] = lut[i / COPIES];
+    __syncthreads();
+
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t l = lane % LANES;
+    const uint32_t g = lane / LANES;
+    const uint32_t lds_off = (lane % COPIES) * 4u;
+    // wave index made provably uniform so that per-row values of a one-row
+    // wave (d = 512) stay scalar: ids and scales then come by scalar loads
+    const uint64_t wave =
+        (uint64_t)blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t stride = (uint64_t)gridDim.x * WAVES * GROUPS * U;
+    bool bad = false;
+
+    for (uint64_t base = wave * GROUPS * U; base < n; base += stride) {
+        F field[U];
+        float alpha[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t j = base + (uint64_t)g * U + u;
+            const int64_t id = ids[j < n ? j : n - 1];
+            ok[u] = (uint64_t)id < rows;  // negative ids wrap above rows
+            bad |= (j < n) && !ok[u];
+            const uint64_t o = ok[u] ? (uint64_t)id * R : 0;  // record byte offset (even)
+            uint32_t newbits;
+            if constexpr (KV == 4) {
+                // 16 new bits = code half-word l, inside one aligned dword
+                const uint32_t hw = (uint32_t)((o >> 1) & 1u) + l;
+                const uint32_t dw = ld32(tab + (o & ~(uint64_t)3) + 4u * (hw >> 1));
+                newbits = (dw >> ((hw & 1u) << 4)) & 0xFFFFu;
+            } else {
+                const uint64_t bit = o * 8 + (uint64_t)NEWB * l;
+                const uint8_t *p = tab + ((bit >> 5) << 2);
+                const uint64_t both = ((uint64_t)ld32(p + 4) << 32) | ld32(p);
+                newbits = (uint32_t)(both >> (bit & 31)) & ((1u << NEWB) - 1u);
+            }
+            const uint64_t ao = o + NB;  // scale: bf16 at bytes [NB, NB + 2)
+            const uint32_t adw = ld32(tab + (ao & ~(uint64_t)3));
+            alpha[u] = __builtin_bit_cast(float, ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16);
+            // older bits from the previous lane(s) of the same row; lane 0
+            // takes them from the last lane: the circular (tail-biting) wrap
+            uint32_t prev;
+            if constexpr (LANES == 64)
+                prev = __builtin_amdgcn_update_dpp(0u, newbits, 0x13C /* wave_ror:1 */, 0xF, 0xF, false);
+            else
+                prev = __shfl(newbits, (int)((l + LANES - 1) % LANES), LANES);
+            F hist;
+            if constexpr (NEWB < M) {
+                // kv = 3: 13 history bits span the two previous lanes
+                const uint32_t prev2 = __shfl(newbits, (int)((l + LANES - 2) % LANES), LANES);
+                hist = (F)((((uint64_t)prev << NEWB) | prev2) >> (2 * NEWB - M));
+            } else {
+                hist = (F)(prev >> (NEWB - M));
+            }
+            field[u] = ((F)newbits << M) | hist;  // bit 0 = code bit NEWB*l - M
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t j = base + (uint64_t)g * U + u;
+            u32x4 v;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // x's low 16 bits are the window s; bits 7..15 of x*x + x
+                // only depend on them, so the higher bits need no masking
+                const uint32_t x = (uint32_t)(field[u] >> (KV * k));
+                const uint32_t h = __umul24(x, x) + x;
+                const uint32_t e = *reinterpret_cast<const uint32_t *>(
+                    reinterpret_cast<const char *>(s_lut) + ((h >> 7) & 511u) * (4u * COPIES) + lds_off);
+                const uint32_t negmask = (x & 0x8000u) ? 0x80008000u : 0u;
+                v[k] = emit_pair<RAW>(e, negmask, alpha[u]);
+            }
+            if (!ok[u]) v = (u32x4){0u, 0u, 0u, 0u};
+            if (j < n) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out + j * (D / 2)) + l);
+        }
+    }
+    if (bad) atomicOr(err, 1);
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+
+#ifndef CPK_COPIES
+#define CPK_COPIES 32
+#endif
+#ifndef CPK_BLOCK
+#define CPK_BLOCK 1024
+#endif
+#ifndef CPK_UNROLL
+#define CPK_UNROLL 2
+#endif
+#ifndef CPK_BLOCKS_PER_CU
+#define CPK_BLOCKS_PER_CU 2
+#endif
+
+// Launch shape: 32 LUT copies = 64 KB of LDS per workgroup, so two
+// 1024-thread workgroups (32 waves) per CU.
+template <int D, int KV>
+struct Tune {
+    static constexpr int COPIES = CPK_COPIES;
+    static constexpr int BLOCK = CPK_BLOCK;
+    static constexpr int U = CPK_UNROLL;
+    static constexpr int BLOCKS_PER_CU = CPK_BLOCKS_PER_CU;
+};
+
+template <int D, int KV, bool RAW>
+static hipError_t launch_one(const LaunchArgs &a)
+{
+    using T = Tune<D, KV>;
+    constexpr int GROUPS = 64 / (D / 8);
+    const uint64_t rows_per_block = (uint64_t)(T::BLOCK / 64) * GROUPS * T::U;
+    uint64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
+    const uint64_t cap = (uint64_t)T::BLOCKS_PER_CU * (a.num_cus > 0 ? a.num_cus : 256);
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL((gather_decode<D, KV, RAW, T::COPIES, T::BLOCK, T::U>), dim3((unsigned)blocks),
+                       dim3(T::BLOCK), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err);
+    return hipGetLastError();
+}
+
+typedef hipError_t (*launch_fn)(const LaunchArgs &);
+
+struct Entry {
+    uint32_t d, kv;
+    launch_fn scaled, raw;
+};
+
+#define CPK_ENTRY(D, KV) {D, KV, &launch_one<D, KV, false>, &launch_one<D, KV, true>}
+
+static const Entry kTable[] = {
+    CPK_ENTRY(64, 3),  CPK_ENTRY(64, 4),  CPK_ENTRY(64, 5),  CPK_ENTRY(64, 6),
+    CPK_ENTRY(128, 3), CPK_ENTRY(128, 4), CPK_ENTRY(128, 5), CPK_ENTRY(128, 6),
+    CPK_ENTRY(256, 3), CPK_ENTRY(256, 4), CPK_ENTRY(256, 5), CPK_ENTRY(256, 6),
+    CPK_ENTRY(512, 3), CPK_ENTRY(512, 4), CPK_ENTRY(512, 5), CPK_ENTRY(512, 6),
+};
+
+static const Entry *find(uint32_t d, uint32_t kv)
+{
+    for (const Entry &e : kTable)
+        if (e.d == d && e.kv == kv) return &e;
+    return nullptr;
+}
+
+bool supported(uint32_t d, uint32_t kv) { return find(d, kv) != nullptr; }
+
+hipError_t launch(uint32_t d, uint32_t kv, bool raw, const LaunchArgs &a)
+{
+    const Entry *e = find(d, kv);
+    if (!e) return hipErrorInvalidValue;
+    return raw ? e->raw(a) : e->scaled(a);
+}
+
+}  // namespace cpk
