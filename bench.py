@@ -61,26 +61,37 @@ def read_counter_summary(config: str, ids_kind: str) -> dict | None:
     return {"fetch_bytes": fetch, "write_bytes": write, "bytes": fetch + write, "file": os.path.basename(path)}
 
 
-def time_launches(fn, steps: int, torch, before=None):
-    """Runs fn() `steps` times on the current stream; returns (total ms of the
-    bracketed region, mean ms of the individual launches)."""
+def time_region(fn, steps: int, torch) -> float:
+    """ms of `steps` back-to-back calls of fn() on the current stream, between
+    one pair of events (synchronised before and after)."""
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    for k in range(steps):
-        if before is not None:
-            before()
-        starts[k].record(stream)
+    for _ in range(steps):
         fn()
-        ends[k].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return t0.elapsed_time(t1), sum(per) / len(per), per
+    return t0.elapsed_time(t1)
+
+
+def time_each(fn, steps: int, torch, before=None) -> list[float]:
+    """ms of each call of fn(), each between its own pair of events; before()
+    runs outside the timed pairs."""
+    stream = torch.cuda.current_stream()
+    out = []
+    for _ in range(steps):
+        if before is not None:
+            before()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
 
 
 def probes(torch, mib: int = 1024) -> dict:
@@ -92,8 +103,8 @@ def probes(torch, mib: int = 1024) -> dict:
     a.fill_(1)
     for _ in range(3):
         b.copy_(a)
-    _, copy_ms, _ = time_launches(lambda: b.copy_(a), 10, torch)
-    _, fill_ms, _ = time_launches(lambda: b.fill_(7), 10, torch)
+    copy_ms = time_region(lambda: b.copy_(a), 10, torch) / 10
+    fill_ms = time_region(lambda: b.fill_(7), 10, torch) / 10
     nbytes = n * 4
     out = {"copy_GBps": 2 * nbytes / copy_ms / 1e6, "fill_GBps": nbytes / fill_ms / 1e6, "MiB": mib}
     del a, b
@@ -170,12 +181,14 @@ def main() -> int:
         print("an id was out of range", file=sys.stderr)
         return 1
 
-    # timed region: K steps back to back, bracketed by synchronisation
+    # timed region: K steps back to back, bracketed by synchronisation; the
+    # events sit on the stream the kernels are launched on
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    total_ms, launch_ms, per = time_launches(step, args.steps, torch)
+    total_ms = time_region(step, args.steps, torch)
     wall_s = time.perf_counter() - wall0
     ms_per_step = total_ms / args.steps
+    launch_ms = ms_per_step  # one kernel launch per step
 
     R = cfg.R
     algo_bytes = n * (R + 2 * cfg.d)
@@ -205,8 +218,6 @@ def main() -> int:
         "effective_GBps": n * (R + 2 * cfg.d) * args.steps / (total_ms / 1e3) / 1e9,
         "pct_hbm_peak": 100.0 * n * (R + 2 * cfg.d) * args.steps / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
         "launch_ms_mean": launch_ms,
-        "launch_ms_min": min(per),
-        "launch_ms_max": max(per),
         "wall_s_timed_region": wall_s,
         "setup_s": {"generate": round(gen_s, 2), "upload": round(upload_s, 2)},
     }
@@ -227,7 +238,8 @@ def main() -> int:
 
     if args.extra:
         flush = torch.empty(512 << 18, dtype=torch.int32, device="cuda")  # 512 MiB > L2 + MALL
-        _, flushed_ms, _ = time_launches(step, max(5, args.steps // 2), torch, before=lambda: flush.fill_(0))
+        per = time_each(step, max(5, args.steps // 2), torch, before=lambda: flush.fill_(0))
+        flushed_ms = sum(per) / len(per)
         res["flushed_launch_ms_mean"] = flushed_ms
         res["flushed_rows_per_s"] = n / (flushed_ms / 1e3)
         res["flushed_pct_hbm_peak"] = 100.0 * algo_bytes / (flushed_ms / 1e3) / 1e9 / HBM_PEAK_GBPS

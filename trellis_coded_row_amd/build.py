@@ -17,7 +17,7 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed fp32 math: keep float code on plain (scalar-lane) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-parameter",
+    "-Wall", "-Wno-unused-parameter", "-Wundef",
 ]
 
 

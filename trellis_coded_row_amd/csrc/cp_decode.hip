@@ -25,18 +25,41 @@
 //     within the row, which is exactly the tail-biting wrap;
 //   - records are 2-byte aligned (R = kv*d/16 + 2 is even), so every load is
 //     an aligned dword and bits are taken out with shifts;
-//   - the 2 KB codebook is staged in LDS once per workgroup, optionally
-//     replicated COPIES times so that lane k reads copy k % COPIES: with 32
-//     copies, lanes 0-31 and 32-63 hit 32 distinct banks whatever the
-//     indices are;
-//   - the grid is persistent (a few workgroups per CU) so the staging is paid
-//     once per workgroup; each wave sweeps U consecutive rows per group per
-//     iteration so record loads of several rows are in flight together;
+//   - the 2 KB codebook is staged in LDS once per workgroup, replicated
+//     COPIES times so that lane k reads copy k % COPIES, which spreads the
+//     random codebook reads over more banks;
+//   - a wave takes a chunk of consecutive lookups: one load brings all their
+//     ids (one per lane), then every record of the chunk is requested before
+//     any is decoded and the next chunk's ids are requested before decoding,
+//     so a whole chunk of record loads is in flight per wave;
+//   - the scale, the window hash and the fp16 -> fp32 widening run on the
+//     scalar unit, v_mad_u32_u24 and v_fma_mix_f32 respectively;
 //   - outputs are written with nontemporal stores: they are not re-read, and
 //     keeping them out of the caches leaves room for hot (Zipf) records.
 #include <type_traits>
 
 #include "cp_internal.h"
+
+// Launch-shape knobs (overridable at build time for tuning).
+#ifndef CPK_COPIES
+#define CPK_COPIES 8
+#endif
+#ifndef CPK_BLOCK
+#define CPK_BLOCK 512
+#endif
+#ifndef CPK_NT_STORE
+#define CPK_NT_STORE 1
+#endif
+#ifndef CPK_FMA_MIX
+#define CPK_FMA_MIX 1
+#endif
+#ifndef CPK_BLOCKS_PER_CU
+#define CPK_BLOCKS_PER_CU 0
+#endif
+#ifndef CPK_CHUNK
+#define CPK_CHUNK 16
+#endif
+
 
 namespace cpk {
 
@@ -49,11 +72,27 @@ __device__ __forceinline__ uint32_t ld32(const uint8_t *p)
     return *reinterpret_cast<const uint32_t *>(p);
 }
 
+// alpha * (fp16 half of e) in one v_fma_mix_f32: the half is widened exactly,
+// the product of a bf16 and an fp16 is exact in fp32, and adding -0 leaves
+// every product (signed zeros included) unchanged.
+__device__ __forceinline__ float mix_lo(uint32_t e, float a, float negz)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(e), "v"(a), "v"(negz));
+    return r;
+}
+
+__device__ __forceinline__ float mix_hi(uint32_t e, float a, float negz)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(e), "v"(a), "v"(negz));
+    return r;
+}
+
 // One output pair: e = LUT entry (fp16 lo = element 2t, hi = element 2t+1),
 // negmask = 0x80008000 when the window's bit 15 is set. Scaled: bf16 pair of
-// alpha * value; the product of a bf16 and an fp16 is exact in fp32 and the
-// conversion rounds to nearest even, which is symmetric in sign, so the sign
-// flip can be applied to the packed result.
+// alpha * value, rounded to nearest even; that rounding is symmetric in sign,
+// so the sign flip can be applied to the packed result.
 template <bool RAW>
 __device__ __forceinline__ uint32_t emit_pair(uint32_t e, uint32_t negmask, float alpha)
 {
@@ -61,11 +100,27 @@ __device__ __forceinline__ uint32_t emit_pair(uint32_t e, uint32_t negmask, floa
         return e ^ negmask;
     } else {
         f32x2 v;
+#if CPK_FMA_MIX
+        const float negz = __builtin_bit_cast(float, 0x80000000u);
+        v.x = mix_lo(e, alpha, negz);
+        v.y = mix_hi(e, alpha, negz);
+#else
         v.x = alpha * (float)__builtin_bit_cast(_Float16, (uint16_t)(e & 0xFFFFu));
         v.y = alpha * (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
+#endif
         bf16x2 b = __builtin_convertvector(v, bf16x2);
         return __builtin_bit_cast(uint32_t, b) ^ negmask;
     }
+}
+
+// h = x*x + x (mod 2^32) on the low 24 bits of x. Bits 7..15 of h, the only
+// bits the output rule reads, depend on bits 0..15 of x alone (the higher
+// bits only add multiples of 2^16), so x may carry the following code bits.
+__device__ __forceinline__ uint32_t hash_mad(uint32_t x)
+{
+    uint32_t h;
+    asm("v_mad_u32_u24 %0, %1, %1, %1" : "=v"(h) : "v"(x));
+    return h;
 }
 
 // Code bits a lane needs for its 4 windows: 16 + 3kv; they fit in 32 bits up
@@ -73,23 +128,33 @@ __device__ __forceinline__ uint32_t emit_pair(uint32_t e, uint32_t negmask, floa
 template <int KV>
 using field_t = typename std::conditional<(16 + 3 * KV <= 32), uint32_t, uint64_t>::type;
 
-template <int D, int KV, bool RAW, int COPIES, int BLOCK, int U>
+// What one lane has loaded for one row before decoding it.
+struct Fetched {
+    uint32_t lo, hi;   // aligned code dword(s) holding the lane's new code bits
+    uint32_t shift;    // bit offset of those bits in {hi, lo}
+    uint32_t alpha;    // scale as fp32 bits (bf16 << 16)
+    bool ok;           // a valid row (id inside the table)
+};
+
+template <int D, int KV, bool RAW, int COPIES, int BLOCK, int CHUNK>
 __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict__ tab, const uint64_t rows,
                                                        const uint32_t *__restrict__ lut,
                                                        const int64_t *__restrict__ ids, const uint64_t n,
                                                        uint32_t *__restrict__ out, int *__restrict__ err)
 {
     constexpr int LANES = D / 8;        // lanes per row
-    constexpr int GROUPS = 64 / LANES;  // rows per wave
+    constexpr int GROUPS = 64 / LANES;  // rows decoded side by side in a wave
     constexpr int NB = KV * D / 16;     // code bytes per record
     constexpr int R = NB + 2;           // record bytes
     constexpr int M = 16 - KV;          // history bits of a window
     constexpr int NEWB = 4 * KV;        // code bits introduced by one lane's 4 steps
     constexpr int WAVES = BLOCK / 64;
+    constexpr int CI = CHUNK / GROUPS;  // rows per lane group per chunk
     static_assert(LANES >= 2 && LANES <= 64 && (LANES & (LANES - 1)) == 0, "d/8 lanes");
     static_assert((KV * D) % 64 == 0, "code must be whole dwords");
     static_assert(NEWB <= 32 && 2 * NEWB >= M, "history within two lanes");
     static_assert(COPIES >= 1 && COPIES <= 64 && (COPIES & (COPIES - 1)) == 0, "LDS copies");
+    static_assert(CHUNK <= 64 && CI >= 1 && CI * GROUPS == CHUNK, "one id per lane per chunk");
     using F = field_t<KV>;
 
     __shared__ uint32_t s_lut[512 * COPIES];
@@ -101,72 +166,107 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     const uint32_t g = lane / LANES;
     const uint32_t lds_off = (lane % COPIES) * 4u;
     // wave index made provably uniform so that per-row values of a one-row
-    // wave (d = 512) stay scalar: ids and scales then come by scalar loads
+    // wave (d = 512) stay scalar
     const uint64_t wave =
         (uint64_t)blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint64_t stride = (uint64_t)gridDim.x * WAVES * GROUPS * U;
+    const uint64_t waves = (uint64_t)gridDim.x * WAVES;
+    const uint64_t nchunks = (n + CHUNK - 1) / CHUNK;
     bool bad = false;
 
-    for (uint64_t base = wave * GROUPS * U; base < n; base += stride) {
-        F field[U];
-        float alpha[U];
-        bool ok[U];
+    // A wave takes chunks of CHUNK consecutive lookups; lane k holds the id of
+    // the chunk's row k, and group g decodes rows g*CI .. g*CI + CI - 1. All
+    // records of a chunk are requested before any is decoded, and the next
+    // chunk's ids are requested before the decoding starts, so a wave keeps
+    // a whole chunk of record loads in flight.
+    auto load_ids = [&](uint64_t c) -> int64_t {
+        const uint64_t j = c * CHUNK + lane;
+        return (c < nchunks && lane < CHUNK && j < n) ? ids[j] : 0;
+    };
+    int64_t my_id = load_ids(wave);
+    for (uint64_t c = wave; c < nchunks; c += waves) {
+        const uint64_t c0 = c * CHUNK;
+        const uint32_t cn = (uint32_t)((n - c0) < CHUNK ? (n - c0) : CHUNK);
+        Fetched f[CI];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint64_t j = base + (uint64_t)g * U + u;
-            const int64_t id = ids[j < n ? j : n - 1];
-            ok[u] = (uint64_t)id < rows;  // negative ids wrap above rows
-            bad |= (j < n) && !ok[u];
-            const uint64_t o = ok[u] ? (uint64_t)id * R : 0;  // record byte offset (even)
-            uint32_t newbits;
+        for (int i = 0; i < CI; ++i) {
+            const uint32_t r = g * CI + i;  // row within the chunk
+            int64_t id;
+            if constexpr (GROUPS == 1) {
+                const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)my_id, r);
+                const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)my_id >> 32), r);
+                id = (int64_t)(((uint64_t)hi << 32) | lo);
+            } else {
+                id = __shfl(my_id, (int)r, 64);
+            }
+            const bool in = r < cn;
+            const bool ok = in && (uint64_t)id < rows;  // negative ids wrap above rows
+            bad |= in && !ok;
+            const uint64_t o = ok ? (uint64_t)id * R : 0;  // record byte offset (even)
             if constexpr (KV == 4) {
                 // 16 new bits = code half-word l, inside one aligned dword
                 const uint32_t hw = (uint32_t)((o >> 1) & 1u) + l;
-                const uint32_t dw = ld32(tab + (o & ~(uint64_t)3) + 4u * (hw >> 1));
-                newbits = (dw >> ((hw & 1u) << 4)) & 0xFFFFu;
+                f[i].lo = ld32(tab + (o & ~(uint64_t)3) + 4u * (hw >> 1));
+                f[i].hi = 0;
+                f[i].shift = (hw & 1u) << 4;
             } else {
                 const uint64_t bit = o * 8 + (uint64_t)NEWB * l;
                 const uint8_t *p = tab + ((bit >> 5) << 2);
-                const uint64_t both = ((uint64_t)ld32(p + 4) << 32) | ld32(p);
-                newbits = (uint32_t)(both >> (bit & 31)) & ((1u << NEWB) - 1u);
+                f[i].lo = ld32(p);
+                f[i].hi = ld32(p + 4);
+                f[i].shift = (uint32_t)(bit & 31);
             }
             const uint64_t ao = o + NB;  // scale: bf16 at bytes [NB, NB + 2)
             const uint32_t adw = ld32(tab + (ao & ~(uint64_t)3));
-            alpha[u] = __builtin_bit_cast(float, ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16);
+            f[i].alpha = ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16;
+            f[i].ok = ok;
+        }
+        my_id = load_ids(c + waves);
+
+#pragma unroll
+        for (int i = 0; i < CI; ++i) {
+            const uint32_t r = g * CI + i;
+            uint32_t newbits;
+            if constexpr (KV == 4)
+                newbits = (f[i].lo >> f[i].shift) & 0xFFFFu;
+            else
+                newbits = (uint32_t)((((uint64_t)f[i].hi << 32) | f[i].lo) >> f[i].shift) &
+                          ((1u << NEWB) - 1u);
             // older bits from the previous lane(s) of the same row; lane 0
             // takes them from the last lane: the circular (tail-biting) wrap
             uint32_t prev;
             if constexpr (LANES == 64)
                 prev = __builtin_amdgcn_update_dpp(0u, newbits, 0x13C /* wave_ror:1 */, 0xF, 0xF, false);
             else
-                prev = __shfl(newbits, (int)((l + LANES - 1) % LANES), LANES);
+                prev = __shfl(newbits, (int)(g * LANES + (l + LANES - 1) % LANES), 64);
             F hist;
             if constexpr (NEWB < M) {
                 // kv = 3: 13 history bits span the two previous lanes
-                const uint32_t prev2 = __shfl(newbits, (int)((l + LANES - 2) % LANES), LANES);
+                const uint32_t prev2 = __shfl(newbits, (int)(g * LANES + (l + LANES - 2) % LANES), 64);
                 hist = (F)((((uint64_t)prev << NEWB) | prev2) >> (2 * NEWB - M));
             } else {
                 hist = (F)(prev >> (NEWB - M));
             }
-            field[u] = ((F)newbits << M) | hist;  // bit 0 = code bit NEWB*l - M
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint64_t j = base + (uint64_t)g * U + u;
+            const F field = ((F)newbits << M) | hist;  // bit 0 = code bit NEWB*l - M
+            const float alpha = __builtin_bit_cast(float, f[i].alpha);
             u32x4 v;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                // x's low 16 bits are the window s; bits 7..15 of x*x + x
-                // only depend on them, so the higher bits need no masking
-                const uint32_t x = (uint32_t)(field[u] >> (KV * k));
-                const uint32_t h = __umul24(x, x) + x;
+                const uint32_t x = (uint32_t)(field >> (KV * k));  // low 16 bits: window s_t
+                const uint32_t h = hash_mad(x);
                 const uint32_t e = *reinterpret_cast<const uint32_t *>(
                     reinterpret_cast<const char *>(s_lut) + ((h >> 7) & 511u) * (4u * COPIES) + lds_off);
                 const uint32_t negmask = (x & 0x8000u) ? 0x80008000u : 0u;
-                v[k] = emit_pair<RAW>(e, negmask, alpha[u]);
+                v[k] = emit_pair<RAW>(e, negmask, alpha);
             }
-            if (!ok[u]) v = (u32x4){0u, 0u, 0u, 0u};
-            if (j < n) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out + j * (D / 2)) + l);
+            if (r < cn) {
+                u32x4 *dst = reinterpret_cast<u32x4 *>(out + (c0 + r) * (D / 2)) + l;
+                if (!f[i].ok) v = (u32x4){0u, 0u, 0u, 0u};
+#if CPK_NT_STORE
+                __builtin_nontemporal_store(v, dst);
+#else
+                *dst = v;
+#endif
+            }
         }
     }
     if (bad) atomicOr(err, 1);
@@ -176,27 +276,17 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
 // dispatch
 // ---------------------------------------------------------------------------
 
-#ifndef CPK_COPIES
-#define CPK_COPIES 32
-#endif
-#ifndef CPK_BLOCK
-#define CPK_BLOCK 1024
-#endif
-#ifndef CPK_UNROLL
-#define CPK_UNROLL 2
-#endif
-#ifndef CPK_BLOCKS_PER_CU
-#define CPK_BLOCKS_PER_CU 2
-#endif
-
-// Launch shape: 32 LUT copies = 64 KB of LDS per workgroup, so two
-// 1024-thread workgroups (32 waves) per CU.
+// Launch shape (measured on MI355X, d = 512 replay): 8 LUT copies (16 KB of
+// LDS) in 512-thread workgroups, so LDS does not limit residency (4
+// workgroups = 32 waves per CU); one wave holds a chunk of 16 lookups; the grid
+// covers all chunks (no persistent cap), which balances the tail better than
+// a fixed number of workgroups per CU.
 template <int D, int KV>
 struct Tune {
     static constexpr int COPIES = CPK_COPIES;
     static constexpr int BLOCK = CPK_BLOCK;
-    static constexpr int U = CPK_UNROLL;
     static constexpr int BLOCKS_PER_CU = CPK_BLOCKS_PER_CU;
+    static constexpr int CHUNK = CPK_CHUNK;
 };
 
 template <int D, int KV, bool RAW>
@@ -204,11 +294,15 @@ static hipError_t launch_one(const LaunchArgs &a)
 {
     using T = Tune<D, KV>;
     constexpr int GROUPS = 64 / (D / 8);
-    const uint64_t rows_per_block = (uint64_t)(T::BLOCK / 64) * GROUPS * T::U;
-    uint64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
-    const uint64_t cap = (uint64_t)T::BLOCKS_PER_CU * (a.num_cus > 0 ? a.num_cus : 256);
-    if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL((gather_decode<D, KV, RAW, T::COPIES, T::BLOCK, T::U>), dim3((unsigned)blocks),
+    // lookups per wave chunk: a multiple of the rows decoded side by side, <= 64
+    constexpr int CHUNK = (T::CHUNK / GROUPS > 0 ? T::CHUNK / GROUPS : 1) * GROUPS;
+    const uint64_t nchunks = (a.n + CHUNK - 1) / CHUNK;
+    uint64_t blocks = (nchunks + T::BLOCK / 64 - 1) / (T::BLOCK / 64);
+    if (T::BLOCKS_PER_CU > 0) {  // persistent grid: at most this many workgroups per CU
+        const uint64_t cap = (uint64_t)T::BLOCKS_PER_CU * (a.num_cus > 0 ? a.num_cus : 256);
+        if (blocks > cap) blocks = cap;
+    }
+    hipLaunchKernelGGL((gather_decode<D, KV, RAW, T::COPIES, T::BLOCK, CHUNK>), dim3((unsigned)blocks),
                        dim3(T::BLOCK), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err);
     return hipGetLastError();
 }
