@@ -122,8 +122,10 @@ def main() -> int:
     ap.add_argument("--ids", default=None, choices=["zipf", "uniform", "slice96"],
                     help="id stream (default: the config's own)")
     ap.add_argument("--noncoherent", action="store_true", help="host_d512: non-coherent pinned memory")
-    ap.add_argument("--extra", action="store_true",
-                    help="also time with L2/MALL flushed before every launch, and run copy/fill probes")
+    ap.add_argument("--flushed", action="store_true",
+                    help="also time launches with L2/MALL flushed (512 MiB written) before each")
+    ap.add_argument("--probes", action="store_true", help="also run 1 GiB copy and fill probes")
+    ap.add_argument("--extra", action="store_true", help="--flushed and --probes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     args = ap.parse_args()
@@ -236,7 +238,7 @@ def main() -> int:
         "kernel": f"gather_decode<{cfg.d},{cfg.kv}>",
     }
 
-    if args.extra:
+    if args.extra or args.flushed:
         flush = torch.empty(512 << 18, dtype=torch.int32, device="cuda")  # 512 MiB > L2 + MALL
         per = time_each(step, max(5, args.steps // 2), torch, before=lambda: flush.fill_(0))
         flushed_ms = sum(per) / len(per)
@@ -245,6 +247,7 @@ def main() -> int:
         res["flushed_pct_hbm_peak"] = 100.0 * algo_bytes / (flushed_ms / 1e3) / 1e9 / HBM_PEAK_GBPS
         del flush
         torch.cuda.empty_cache()
+    if args.extra or args.probes:
         res["probes"] = probes(torch)
 
     if not args.no_cpu_baseline:
