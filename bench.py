@@ -112,6 +112,21 @@ def probes(torch, mib: int = 1024) -> dict:
     return out
 
 
+def pcie_probe(torch, mib: int = 1024) -> dict:
+    """Host-to-device bandwidth from pinned host memory (torch copy of `mib`
+    MiB), the denominator for a table read over PCIe."""
+    n = mib * (1 << 20) // 4
+    h = torch.empty(n, dtype=torch.int32, pin_memory=True)
+    d = torch.empty(n, dtype=torch.int32, device="cuda")
+    h.fill_(3)
+    for _ in range(2):
+        d.copy_(h, non_blocking=True)
+    ms = time_region(lambda: d.copy_(h, non_blocking=True), 5, torch) / 5
+    del h, d
+    torch.cuda.empty_cache()
+    return {"h2d_GBps": n * 4 / ms / 1e6, "MiB": mib}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,8 +239,12 @@ def main() -> int:
         "setup_s": {"generate": round(gen_s, 2), "upload": round(upload_s, 2)},
     }
     if cfg.host_resident:
-        # the records cross PCIe: report that rate too (the HBM roofline does not bound it)
+        # the records cross PCIe: report that rate against a measured
+        # pinned host-to-device copy (the HBM roofline does not bound it)
         res["pcie_record_GBps"] = n * R / (launch_ms / 1e3) / 1e9
+        probe = pcie_probe(torch)
+        res["pcie_probe"] = probe
+        res["pcie_frac"] = res["pcie_record_GBps"] / probe["h2d_GBps"]
     counters = read_counter_summary(cfg.name, ids_kind)
     res["roofline"] = {
         "bound": "hbm",
