@@ -142,3 +142,26 @@ def test_caller_stream_is_used():
         assert_bf16_within_ulp(got, exp, "side stream")
     finally:
         t.close()
+
+
+def test_record_offsets_beyond_2_and_4_gib():
+    # records whose byte offset id * R passes 2^31 and 2^32: the kernel's
+    # offsets and addresses must stay 64-bit unsigned all the way
+    d, kv = 512, 4
+    R = cp.cp_record_bytes(d, kv)
+    rows = (1 << 32) // R + 4096
+    say(f"generating a {rows:,}-row table ({rows * R / 2**30:.2f} GiB)")
+    recs = workload.random_records(rows, d, kv, seed=4242)
+    t = make_table(LUT, recs, d, kv)
+    try:
+        b31, b32 = (1 << 31) // R, (1 << 32) // R
+        edge = [b31 - 1, b31, b31 + 1, b32 - 1, b32, b32 + 1, rows - 1, 0]
+        rng = np.random.default_rng(11)
+        ids = np.concatenate([np.array(edge * 3, dtype=np.int64),
+                              rng.integers(b31 - 2000, b31 + 2000, 500, dtype=np.int64),
+                              rng.integers(b32 - 2000, rows, 500, dtype=np.int64)])
+        check_lookup(t, LUT, recs, d, kv, ids, "offsets across 2 and 4 GiB")
+    finally:
+        t.close()
+        del recs
+        torch.cuda.empty_cache()

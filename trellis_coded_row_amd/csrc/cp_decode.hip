@@ -67,6 +67,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// 64-bit value of lane `lane` (wave-uniform result). The builtin works on
+// int; both halves go through uint32_t so the low half is not sign-extended.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, uint32_t lane)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, (int)lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), (int)lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ uint32_t ld32(const uint8_t *p)
 {
     return *reinterpret_cast<const uint32_t *>(p);
@@ -89,11 +98,27 @@ __device__ __forceinline__ float mix_hi(uint32_t e, float a, float negz)
     return r;
 }
 
+// The same with the scale in an SGPR (uniform per row when a row fills the
+// wave), which saves moving it into a VGPR for every row.
+__device__ __forceinline__ float mix_lo_s(uint32_t e, float a, float negz)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(e), "s"(a), "v"(negz));
+    return r;
+}
+
+__device__ __forceinline__ float mix_hi_s(uint32_t e, float a, float negz)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(e), "s"(a), "v"(negz));
+    return r;
+}
+
 // One output pair: e = LUT entry (fp16 lo = element 2t, hi = element 2t+1),
 // negmask = 0x80008000 when the window's bit 15 is set. Scaled: bf16 pair of
 // alpha * value, rounded to nearest even; that rounding is symmetric in sign,
 // so the sign flip can be applied to the packed result.
-template <bool RAW>
+template <bool RAW, bool SALPHA = false>
 __device__ __forceinline__ uint32_t emit_pair(uint32_t e, uint32_t negmask, float alpha)
 {
     if constexpr (RAW) {
@@ -102,8 +127,13 @@ __device__ __forceinline__ uint32_t emit_pair(uint32_t e, uint32_t negmask, floa
         f32x2 v;
 #if CPK_FMA_MIX
         const float negz = __builtin_bit_cast(float, 0x80000000u);
-        v.x = mix_lo(e, alpha, negz);
-        v.y = mix_hi(e, alpha, negz);
+        if constexpr (SALPHA) {
+            v.x = mix_lo_s(e, alpha, negz);
+            v.y = mix_hi_s(e, alpha, negz);
+        } else {
+            v.x = mix_lo(e, alpha, negz);
+            v.y = mix_hi(e, alpha, negz);
+        }
 #else
         v.x = alpha * (float)__builtin_bit_cast(_Float16, (uint16_t)(e & 0xFFFFu));
         v.y = alpha * (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
@@ -128,13 +158,54 @@ __device__ __forceinline__ uint32_t hash_mad(uint32_t x)
 template <int KV>
 using field_t = typename std::conditional<(16 + 3 * KV <= 32), uint32_t, uint64_t>::type;
 
-// What one lane has loaded for one row before decoding it.
-struct Fetched {
-    uint32_t lo, hi;   // aligned code dword(s) holding the lane's new code bits
-    uint32_t shift;    // bit offset of those bits in {hi, lo}
-    uint32_t alpha;    // scale as fp32 bits (bf16 << 16)
-    bool ok;           // a valid row (id inside the table)
-};
+// Decodes one row's 8 outputs of this lane from `newbits` (the lane's 4kv
+// new code bits) and the row's scale, and returns them packed (4 dwords).
+template <int D, int KV, bool RAW, int COPIES, bool SALPHA>
+__device__ __forceinline__ u32x4 decode_lane(uint32_t newbits, uint32_t alpha_bits, uint32_t l, uint32_t g,
+                                             const uint32_t *s_lut, uint32_t lds_off)
+{
+    constexpr int LANES = D / 8;
+    constexpr int M = 16 - KV;
+    constexpr int NEWB = 4 * KV;
+    using F = field_t<KV>;
+    // older bits from the previous lane(s) of the same row; lane 0 takes them
+    // from the last lane: the circular (tail-biting) wrap
+    uint32_t prev;
+    if constexpr (LANES == 64)
+        prev = __builtin_amdgcn_update_dpp(0u, newbits, 0x13C /* wave_ror:1 */, 0xF, 0xF, false);
+    else
+        prev = __shfl(newbits, (int)(g * LANES + (l + LANES - 1) % LANES), 64);
+    F hist;
+    if constexpr (NEWB < M) {
+        // kv = 3: 13 history bits span the two previous lanes
+        const uint32_t prev2 = __shfl(newbits, (int)(g * LANES + (l + LANES - 2) % LANES), 64);
+        hist = (F)((((uint64_t)prev << NEWB) | prev2) >> (2 * NEWB - M));
+    } else {
+        hist = (F)(prev >> (NEWB - M));
+    }
+    const F field = ((F)newbits << M) | hist;  // bit 0 = code bit NEWB*l - M
+    const float alpha = __builtin_bit_cast(float, alpha_bits);
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t x = (uint32_t)(field >> (KV * k));  // low 16 bits: window s_t
+        const uint32_t h = hash_mad(x);
+        const uint32_t e = *reinterpret_cast<const uint32_t *>(
+            reinterpret_cast<const char *>(s_lut) + ((h >> 7) & 511u) * (4u * COPIES) + lds_off);
+        const uint32_t negmask = (x & 0x8000u) ? 0x80008000u : 0u;
+        v[k] = emit_pair<RAW, SALPHA>(e, negmask, alpha);
+    }
+    return v;
+}
+
+__device__ __forceinline__ void store16(uint32_t *dst, u32x4 v)
+{
+#if CPK_NT_STORE
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
+#else
+    *reinterpret_cast<u32x4 *>(dst) = v;
+#endif
+}
 
 template <int D, int KV, bool RAW, int COPIES, int BLOCK, int CHUNK>
 __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict__ tab, const uint64_t rows,
@@ -146,16 +217,14 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     constexpr int GROUPS = 64 / LANES;  // rows decoded side by side in a wave
     constexpr int NB = KV * D / 16;     // code bytes per record
     constexpr int R = NB + 2;           // record bytes
-    constexpr int M = 16 - KV;          // history bits of a window
     constexpr int NEWB = 4 * KV;        // code bits introduced by one lane's 4 steps
     constexpr int WAVES = BLOCK / 64;
     constexpr int CI = CHUNK / GROUPS;  // rows per lane group per chunk
     static_assert(LANES >= 2 && LANES <= 64 && (LANES & (LANES - 1)) == 0, "d/8 lanes");
     static_assert((KV * D) % 64 == 0, "code must be whole dwords");
-    static_assert(NEWB <= 32 && 2 * NEWB >= M, "history within two lanes");
+    static_assert(NEWB <= 32 && 2 * NEWB >= 16 - KV, "history within two lanes");
     static_assert(COPIES >= 1 && COPIES <= 64 && (COPIES & (COPIES - 1)) == 0, "LDS copies");
     static_assert(CHUNK <= 64 && CI >= 1 && CI * GROUPS == CHUNK, "one id per lane per chunk");
-    using F = field_t<KV>;
 
     __shared__ uint32_t s_lut[512 * COPIES];
     for (int i = threadIdx.x; i < 512 * COPIES; i += BLOCK) s_lut[i] = lut[i / COPIES];
@@ -173,99 +242,85 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     const uint64_t nchunks = (n + CHUNK - 1) / CHUNK;
     bool bad = false;
 
-    // A wave takes chunks of CHUNK consecutive lookups; lane k holds the id of
-    // the chunk's row k, and group g decodes rows g*CI .. g*CI + CI - 1. All
-    // records of a chunk are requested before any is decoded, and the next
-    // chunk's ids are requested before the decoding starts, so a wave keeps
-    // a whole chunk of record loads in flight.
-    auto load_ids = [&](uint64_t c) -> int64_t {
+    // A wave takes chunks of CHUNK consecutive lookups. Lane k loads the id of
+    // the chunk's row k and works out, once for the whole chunk, whether it is
+    // valid and where its record starts; rows then read those from lane k.
+    // Every record of a chunk is requested before any is decoded, and the next
+    // chunk's ids before the decoding starts.
+    auto load_id = [&](uint64_t c) -> int64_t {
         const uint64_t j = c * CHUNK + lane;
         return (c < nchunks && lane < CHUNK && j < n) ? ids[j] : 0;
     };
-    int64_t my_id = load_ids(wave);
+    int64_t my_id = load_id(wave);
     for (uint64_t c = wave; c < nchunks; c += waves) {
         const uint64_t c0 = c * CHUNK;
         const uint32_t cn = (uint32_t)((n - c0) < CHUNK ? (n - c0) : CHUNK);
-        Fetched f[CI];
-#pragma unroll
-        for (int i = 0; i < CI; ++i) {
-            const uint32_t r = g * CI + i;  // row within the chunk
-            int64_t id;
-            if constexpr (GROUPS == 1) {
-                const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)my_id, r);
-                const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)my_id >> 32), r);
-                id = (int64_t)(((uint64_t)hi << 32) | lo);
-            } else {
-                id = __shfl(my_id, (int)r, 64);
-            }
-            const bool in = r < cn;
-            const bool ok = in && (uint64_t)id < rows;  // negative ids wrap above rows
-            bad |= in && !ok;
-            const uint64_t o = ok ? (uint64_t)id * R : 0;  // record byte offset (even)
-            if constexpr (KV == 4) {
-                // 16 new bits = code half-word l, inside one aligned dword
-                const uint32_t hw = (uint32_t)((o >> 1) & 1u) + l;
-                f[i].lo = ld32(tab + (o & ~(uint64_t)3) + 4u * (hw >> 1));
-                f[i].hi = 0;
-                f[i].shift = (hw & 1u) << 4;
-            } else {
-                const uint64_t bit = o * 8 + (uint64_t)NEWB * l;
-                const uint8_t *p = tab + ((bit >> 5) << 2);
-                f[i].lo = ld32(p);
-                f[i].hi = ld32(p + 4);
-                f[i].shift = (uint32_t)(bit & 31);
-            }
-            const uint64_t ao = o + NB;  // scale: bf16 at bytes [NB, NB + 2)
-            const uint32_t adw = ld32(tab + (ao & ~(uint64_t)3));
-            f[i].alpha = ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16;
-            f[i].ok = ok;
-        }
-        my_id = load_ids(c + waves);
+        const bool in = lane < cn;
+        const bool ok = in && (uint64_t)my_id < rows;  // negative ids wrap above rows
+        bad |= in && !ok;
+        const uint64_t my_off = ok ? (uint64_t)my_id * R : 0;  // record byte offset (even)
+        const uint64_t okmask = __ballot(ok);
+        my_id = load_id(c + waves);
 
+        if constexpr (GROUPS == 1) {
+            // d = 512: one row at a time across the whole wave; the row's
+            // record offset is uniform (scalar), the scale comes by a scalar load
+            uint32_t nb[CI], ab[CI];
 #pragma unroll
-        for (int i = 0; i < CI; ++i) {
-            const uint32_t r = g * CI + i;
-            uint32_t newbits;
-            if constexpr (KV == 4)
-                newbits = (f[i].lo >> f[i].shift) & 0xFFFFu;
-            else
-                newbits = (uint32_t)((((uint64_t)f[i].hi << 32) | f[i].lo) >> f[i].shift) &
-                          ((1u << NEWB) - 1u);
-            // older bits from the previous lane(s) of the same row; lane 0
-            // takes them from the last lane: the circular (tail-biting) wrap
-            uint32_t prev;
-            if constexpr (LANES == 64)
-                prev = __builtin_amdgcn_update_dpp(0u, newbits, 0x13C /* wave_ror:1 */, 0xF, 0xF, false);
-            else
-                prev = __shfl(newbits, (int)(g * LANES + (l + LANES - 1) % LANES), 64);
-            F hist;
-            if constexpr (NEWB < M) {
-                // kv = 3: 13 history bits span the two previous lanes
-                const uint32_t prev2 = __shfl(newbits, (int)(g * LANES + (l + LANES - 2) % LANES), 64);
-                hist = (F)((((uint64_t)prev << NEWB) | prev2) >> (2 * NEWB - M));
-            } else {
-                hist = (F)(prev >> (NEWB - M));
+            for (int i = 0; i < CI; ++i) {
+                const uint64_t o = readlane_u64(my_off, (uint32_t)i);
+                const uint8_t *rec = tab + o;
+                if constexpr (KV == 4) {
+                    // lane l's 16 new bits are code half-word l (records are 2-byte aligned)
+                    nb[i] = *reinterpret_cast<const uint16_t *>(rec + 2u * l);
+                } else {
+                    const uint64_t bit = o * 8 + (uint64_t)NEWB * l;
+                    const uint8_t *p = tab + ((bit >> 5) << 2);
+                    const uint64_t both = ((uint64_t)ld32(p + 4) << 32) | ld32(p);
+                    nb[i] = (uint32_t)(both >> (bit & 31)) & ((1u << NEWB) - 1u);
+                }
+                const uint64_t ao = o + NB;  // scale: bf16 at bytes [NB, NB + 2)
+                const uint32_t adw = ld32(tab + (ao & ~(uint64_t)3));
+                ab[i] = ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16;
             }
-            const F field = ((F)newbits << M) | hist;  // bit 0 = code bit NEWB*l - M
-            const float alpha = __builtin_bit_cast(float, f[i].alpha);
-            u32x4 v;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t x = (uint32_t)(field >> (KV * k));  // low 16 bits: window s_t
-                const uint32_t h = hash_mad(x);
-                const uint32_t e = *reinterpret_cast<const uint32_t *>(
-                    reinterpret_cast<const char *>(s_lut) + ((h >> 7) & 511u) * (4u * COPIES) + lds_off);
-                const uint32_t negmask = (x & 0x8000u) ? 0x80008000u : 0u;
-                v[k] = emit_pair<RAW>(e, negmask, alpha);
+            for (int i = 0; i < CI; ++i) {
+                // decoded whatever the row's validity, so that the loads above
+                // stay ahead of their uses; only the store depends on it
+                const u32x4 v = decode_lane<D, KV, RAW, COPIES, true>(nb[i], ab[i], l, g, s_lut, lds_off);
+                if ((uint32_t)i < cn) {
+                    uint32_t *dst = out + (c0 + i) * (D / 2) + 4u * l;
+                    if ((okmask >> i) & 1u)
+                        store16(dst, v);
+                    else
+                        store16(dst, (u32x4){0u, 0u, 0u, 0u});
+                }
             }
-            if (r < cn) {
-                u32x4 *dst = reinterpret_cast<u32x4 *>(out + (c0 + r) * (D / 2)) + l;
-                if (!f[i].ok) v = (u32x4){0u, 0u, 0u, 0u};
-#if CPK_NT_STORE
-                __builtin_nontemporal_store(v, dst);
-#else
-                *dst = v;
-#endif
+        } else {
+            // several rows side by side: group g decodes rows g*CI .. g*CI+CI-1
+            uint32_t nb[CI], ab[CI];
+#pragma unroll
+            for (int i = 0; i < CI; ++i) {
+                const int r = (int)(g * CI + i);
+                const uint64_t o = __shfl(my_off, r, 64);
+                if constexpr (KV == 4) {
+                    nb[i] = *reinterpret_cast<const uint16_t *>(tab + o + 2u * l);
+                } else {
+                    const uint64_t bit = o * 8 + (uint64_t)NEWB * l;
+                    const uint8_t *p = tab + ((bit >> 5) << 2);
+                    const uint64_t both = ((uint64_t)ld32(p + 4) << 32) | ld32(p);
+                    nb[i] = (uint32_t)(both >> (bit & 31)) & ((1u << NEWB) - 1u);
+                }
+                const uint64_t ao = o + NB;
+                const uint32_t adw = ld32(tab + (ao & ~(uint64_t)3));
+                ab[i] = ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16;
+            }
+#pragma unroll
+            for (int i = 0; i < CI; ++i) {
+                const uint32_t r = g * CI + i;
+                u32x4 v = decode_lane<D, KV, RAW, COPIES, false>(nb[i], ab[i], l, g, s_lut, lds_off);
+                if (!((okmask >> r) & 1u)) v = (u32x4){0u, 0u, 0u, 0u};
+                if (r < cn) store16(out + (c0 + r) * (D / 2) + 4u * l, v);
             }
         }
     }
