@@ -42,10 +42,10 @@
 
 // Launch-shape knobs (overridable at build time for tuning).
 #ifndef CPK_COPIES
-#define CPK_COPIES 8
+#define CPK_COPIES 16
 #endif
 #ifndef CPK_BLOCK
-#define CPK_BLOCK 512
+#define CPK_BLOCK 1024
 #endif
 #ifndef CPK_NT_STORE
 #define CPK_NT_STORE 1
@@ -153,6 +153,15 @@ __device__ __forceinline__ uint32_t hash_mad(uint32_t x)
     return h;
 }
 
+// (a & mask) | b in one v_and_or_b32 (kept as written: the compiler otherwise
+// reassociates the LDS address into more instructions).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(b));
+    return r;
+}
+
 // Code bits a lane needs for its 4 windows: 16 + 3kv; they fit in 32 bits up
 // to kv = 5.
 template <int KV>
@@ -172,7 +181,7 @@ __device__ __forceinline__ u32x4 decode_lane(uint32_t newbits, uint32_t alpha_bi
     // from the last lane: the circular (tail-biting) wrap
     uint32_t prev;
     if constexpr (LANES == 64)
-        prev = __builtin_amdgcn_update_dpp(0u, newbits, 0x13C /* wave_ror:1 */, 0xF, 0xF, false);
+        prev = __builtin_amdgcn_update_dpp(newbits, newbits, 0x13C /* wave_ror:1 */, 0xF, 0xF, false);
     else
         prev = __shfl(newbits, (int)(g * LANES + (l + LANES - 1) % LANES), 64);
     F hist;
@@ -190,10 +199,12 @@ __device__ __forceinline__ u32x4 decode_lane(uint32_t newbits, uint32_t alpha_bi
     for (int k = 0; k < 4; ++k) {
         const uint32_t x = (uint32_t)(field >> (KV * k));  // low 16 bits: window s_t
         const uint32_t h = hash_mad(x);
+        // LDS block of entry idx = (h >> 7) & 511 starts at byte idx * 128,
+        // i.e. h & 0xFF80; bit 15 of the window (the sign) picks the negated
+        // half (+64 bytes); the lane picks one of the 16 copies
         const uint32_t e = *reinterpret_cast<const uint32_t *>(
-            reinterpret_cast<const char *>(s_lut) + ((h >> 7) & 511u) * (4u * COPIES) + lds_off);
-        const uint32_t negmask = (x & 0x8000u) ? 0x80008000u : 0u;
-        v[k] = emit_pair<RAW, SALPHA>(e, negmask, alpha);
+            reinterpret_cast<const char *>(s_lut) + and_or(h, 0xFF80u, and_or(x >> 9, 0x40u, lds_off)));
+        v[k] = emit_pair<RAW, SALPHA>(e, 0u, alpha);
     }
     return v;
 }
@@ -223,17 +234,24 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     static_assert(LANES >= 2 && LANES <= 64 && (LANES & (LANES - 1)) == 0, "d/8 lanes");
     static_assert((KV * D) % 64 == 0, "code must be whole dwords");
     static_assert(NEWB <= 32 && 2 * NEWB >= 16 - KV, "history within two lanes");
-    static_assert(COPIES >= 1 && COPIES <= 64 && (COPIES & (COPIES - 1)) == 0, "LDS copies");
+    static_assert(COPIES == 16, "the LDS layout holds 16 copies per sign");
     static_assert(CHUNK <= 64 && CI >= 1 && CI * GROUPS == CHUNK, "one id per lane per chunk");
 
-    __shared__ uint32_t s_lut[512 * COPIES];
-    for (int i = threadIdx.x; i < 512 * COPIES; i += BLOCK) s_lut[i] = lut[i / COPIES];
+    // codebook in LDS: per entry a 128-byte block of 16 copies of the fp16
+    // pair followed by 16 copies of its negation (both sign bits flipped)
+    __shared__ __attribute__((aligned(16))) uint32_t s_lut[512 * 32];
+    for (int u = threadIdx.x; u < 4096; u += BLOCK) {
+        // 16-byte unit u holds 4 copies of entry u >> 3, negated when bit 2 of
+        // u is set; consecutive lanes write consecutive units (no bank conflicts)
+        const uint32_t v = lut[u >> 3] ^ ((u & 4) ? 0x80008000u : 0u);
+        reinterpret_cast<u32x4 *>(s_lut)[u] = (u32x4){v, v, v, v};
+    }
     __syncthreads();
 
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t l = lane % LANES;
     const uint32_t g = lane / LANES;
-    const uint32_t lds_off = (lane % COPIES) * 4u;
+    const uint32_t lds_off = (lane & 15u) * 4u;
     // wave index made provably uniform so that per-row values of a one-row
     // wave (d = 512) stay scalar
     const uint64_t wave =
@@ -247,14 +265,19 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     // valid and where its record starts; rows then read those from lane k.
     // Every record of a chunk is requested before any is decoded, and the next
     // chunk's ids before the decoding starts.
+    // row index of row i of chunk c (a wave writes its chunk's rows as one
+    // contiguous run of output)
+    auto row_of = [&](uint64_t c, uint32_t i) -> uint64_t { return c * CHUNK + i; };
     auto load_id = [&](uint64_t c) -> int64_t {
-        const uint64_t j = c * CHUNK + lane;
+        const uint64_t j = row_of(c, lane);
         return (c < nchunks && lane < CHUNK && j < n) ? ids[j] : 0;
     };
     int64_t my_id = load_id(wave);
     for (uint64_t c = wave; c < nchunks; c += waves) {
-        const uint64_t c0 = c * CHUNK;
-        const uint32_t cn = (uint32_t)((n - c0) < CHUNK ? (n - c0) : CHUNK);
+        // rows in this chunk
+        uint32_t cn = __builtin_amdgcn_readfirstlane((uint32_t)((n - c * CHUNK) < CHUNK ? (n - c * CHUNK) : CHUNK));
+        // opaque to the optimiser so that the per-row checks stay 32-bit scalar
+        asm volatile("" : "+s"(cn));
         const bool in = lane < cn;
         const bool ok = in && (uint64_t)my_id < rows;  // negative ids wrap above rows
         bad |= in && !ok;
@@ -285,16 +308,10 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
             }
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                // decoded whatever the row's validity, so that the loads above
-                // stay ahead of their uses; only the store depends on it
+                // every row is decoded (an invalid id reads record 0), so the
+                // loads above stay ahead of their uses
                 const u32x4 v = decode_lane<D, KV, RAW, COPIES, true>(nb[i], ab[i], l, g, s_lut, lds_off);
-                if ((uint32_t)i < cn) {
-                    uint32_t *dst = out + (c0 + i) * (D / 2) + 4u * l;
-                    if ((okmask >> i) & 1u)
-                        store16(dst, v);
-                    else
-                        store16(dst, (u32x4){0u, 0u, 0u, 0u});
-                }
+                if ((uint32_t)i < cn) store16(out + row_of(c, i) * (D / 2) + 4u * l, v);
             }
         } else {
             // several rows side by side: group g decodes rows g*CI .. g*CI+CI-1
@@ -318,9 +335,21 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
                 const uint32_t r = g * CI + i;
-                u32x4 v = decode_lane<D, KV, RAW, COPIES, false>(nb[i], ab[i], l, g, s_lut, lds_off);
-                if (!((okmask >> r) & 1u)) v = (u32x4){0u, 0u, 0u, 0u};
-                if (r < cn) store16(out + (c0 + r) * (D / 2) + 4u * l, v);
+                const u32x4 v = decode_lane<D, KV, RAW, COPIES, false>(nb[i], ab[i], l, g, s_lut, lds_off);
+                if (r < cn) store16(out + row_of(c, r) * (D / 2) + 4u * l, v);
+            }
+        }
+        // Rows with an id outside the table were decoded from record 0 above;
+        // overwrite them with zeros. Rare, so kept off the main path; the wait
+        // orders the two stores to the same address.
+        const uint64_t badmask = __ballot(in) & ~okmask;
+        if (badmask) {
+            __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+            for (int i = 0; i < CI; ++i) {
+                const uint32_t r = g * CI + i;
+                if ((badmask >> r) & 1u)
+                    store16(out + row_of(c, r) * (D / 2) + 4u * l, (u32x4){0u, 0u, 0u, 0u});
             }
         }
     }
@@ -331,11 +360,11 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
 // dispatch
 // ---------------------------------------------------------------------------
 
-// Launch shape (measured on MI355X, d = 512 replay): 8 LUT copies (16 KB of
-// LDS) in 512-thread workgroups, so LDS does not limit residency (4
-// workgroups = 32 waves per CU); one wave holds a chunk of 16 lookups; the grid
-// covers all chunks (no persistent cap), which balances the tail better than
-// a fixed number of workgroups per CU.
+// Launch shape (measured on MI355X, d = 512 replay): the codebook in LDS as
+// 16 copies x 2 signs (64 KB) in 1024-thread workgroups (2 per CU = 32
+// waves); one wave
+// holds a chunk of 16 lookups; the grid covers all chunks (no persistent cap),
+// which balances the tail better than a fixed number of workgroups per CU.
 template <int D, int KV>
 struct Tune {
     static constexpr int COPIES = CPK_COPIES;
