@@ -130,8 +130,8 @@ def pcie_probe(torch, mib: int = 1024) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="gpu_d512",
                     help="workload: gpu_d512 (default), host_d512, small_d256, rate_d512_kv{3,4,5,6}, tiny_d64")
     ap.add_argument("--ids", default=None, choices=["zipf", "uniform", "slice96"],
