@@ -137,6 +137,8 @@ def main() -> int:
     ap.add_argument("--ids", default=None, choices=["zipf", "uniform", "slice96"],
                     help="id stream (default: the config's own)")
     ap.add_argument("--noncoherent", action="store_true", help="host_d512: non-coherent pinned memory")
+    ap.add_argument("--dedup", action="store_true",
+                    help="use cp_lookup_decode_dedup (each distinct record fetched once)")
     ap.add_argument("--flushed", action="store_true",
                     help="also time launches with L2/MALL flushed (512 MiB written) before each")
     ap.add_argument("--probes", action="store_true", help="also run 1 GiB copy and fill probes")
@@ -189,7 +191,11 @@ def main() -> int:
     n = ids_np.shape[0]
     ids = torch.from_numpy(ids_np).cuda()
     out = torch.empty((n, cfg.d), dtype=torch.bfloat16, device="cuda")
-    step = lambda: table.lookup_decode(ids, out)
+    if args.dedup:
+        workspace = torch.empty(table.dedup_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+        step = lambda: table.lookup_decode_dedup(ids, out, workspace=workspace)
+    else:
+        step = lambda: table.lookup_decode(ids, out)
 
     for _ in range(args.warmup):
         step()
@@ -231,6 +237,7 @@ def main() -> int:
             "rows": cfg.rows, "d": cfg.d, "bits_per_step": cfg.kv, "record_bytes": R, "lookups": n,
             "ids": ids_kind, "ids_sha256_16": workload.ids_digest(ids_np),
             "residency": "host" + ("-noncoherent" if args.noncoherent else "") if cfg.host_resident else "hbm",
+            "entry_point": "cp_lookup_decode_dedup" if args.dedup else "cp_lookup_decode",
         },
         "effective_GBps": n * (R + 2 * cfg.d) * args.steps / (total_ms / 1e3) / 1e9,
         "pct_hbm_peak": 100.0 * n * (R + 2 * cfg.d) * args.steps / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,

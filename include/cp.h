@@ -129,6 +129,30 @@ cp_status cp_lookup_decode(const cp_table *table, const int64_t *ids, uint64_t n
 cp_status cp_lookup_decode_raw(const cp_table *table, const int64_t *ids, uint64_t n,
                                uint16_t *out_fp16, void *stream);
 
+/* Device workspace bytes that cp_lookup_decode_dedup needs for a batch of n
+ * lookups on this table (0 for a NULL table). About 36 bytes per lookup plus
+ * n records: 71 MB for n = 393,216 at d = 512, kv = 4. */
+uint64_t cp_dedup_workspace_bytes(const cp_table *table, uint64_t n);
+
+/* Same result as cp_lookup_decode, fetching each distinct record of the batch
+ * only once: the valid ids are deduplicated in a hash table in `workspace`,
+ * each distinct record is copied once from the table into a staging area in
+ * `workspace`, and the rows are decoded from there in the original lookup
+ * order. Meant for a table in pinned host memory, where every record read
+ * crosses PCIe (the pages find that regime dominated by the fetch and the
+ * row-wise layout's advantage growing there: "Assumptions and limits").
+ *   workspace       - device memory, 256-byte aligned, at least
+ *                     cp_dedup_workspace_bytes(table, n) bytes, caller-owned;
+ *                     its contents are scratch (undefined after the call).
+ *                     Calls that share a workspace must not overlap.
+ *   ids, out, stream - as in cp_lookup_decode; n < 2^31.
+ * Asynchronous on `stream` (several kernels, no allocation, no host sync).
+ * Out-of-range ids give zero rows and raise the table's sticky flag.
+ * Errors: INVALID_ARGUMENT (as cp_lookup_decode, or workspace NULL, unaligned
+ * or too small), HIP. */
+cp_status cp_lookup_decode_dedup(const cp_table *table, const int64_t *ids, uint64_t n, uint16_t *out,
+                                 void *workspace, uint64_t workspace_bytes, void *stream);
+
 /* Synchronises `stream`, then returns CP_ERR_ID_OUT_OF_RANGE and clears the
  * table's flag if any lookup since the last check saw an id outside
  * [0, rows); otherwise CP_OK. Errors: INVALID_ARGUMENT, HIP. */

@@ -59,9 +59,12 @@ def assert_bit_exact(got: np.ndarray, exp: np.ndarray, label: str) -> None:
                              f"got {got[tuple(i)]:#06x} want {exp[tuple(i)]:#06x}")
 
 
-def device_lookup(table: cp.Table, ids: np.ndarray, raw: bool = False) -> np.ndarray:
+def device_lookup(table: cp.Table, ids: np.ndarray, raw: bool = False, dedup: bool = False) -> np.ndarray:
     dev_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int64)).cuda()
-    out = table.lookup_decode_raw(dev_ids) if raw else table.lookup_decode(dev_ids)
+    if dedup:
+        out = table.lookup_decode_dedup(dev_ids)
+    else:
+        out = table.lookup_decode_raw(dev_ids) if raw else table.lookup_decode(dev_ids)
     torch.cuda.synchronize()
     return out.view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -76,7 +79,7 @@ def make_table(lut: np.ndarray, records: np.ndarray, d: int, kv: int,
 
 
 def check_lookup(table: cp.Table, lut: np.ndarray, records: np.ndarray, d: int, kv: int,
-                 ids: np.ndarray, label: str, expect_bad: int = 0) -> None:
+                 ids: np.ndarray, label: str, expect_bad: int = 0, dedup: bool = False) -> None:
     """Raw and scaled outputs of the HIP path against the oracle, every element."""
     say(f"{label}: n={ids.shape[0]} d={d} kv={kv} rows={records.shape[0]}")
     rows = records.shape[0]
@@ -89,4 +92,9 @@ def check_lookup(table: cp.Table, lut: np.ndarray, records: np.ndarray, d: int, 
     got = device_lookup(table, ids, raw=False)
     assert table.check() == (expect_bad == 0), label
     ndiff = assert_bf16_within_ulp(got, exp, label + " rows")
-    say(f"{label}: ok (f(c) bit-exact; scaled rows differing from the oracle: {ndiff})")
+    if dedup:
+        got_d = device_lookup(table, ids, dedup=True)
+        assert table.check() == (expect_bad == 0), label
+        assert_bit_exact(got_d, got, label + " dedup path")
+    say(f"{label}: ok (f(c) bit-exact; scaled rows differing from the oracle: {ndiff}"
+        f"{'; dedup path identical' if dedup else ''})")

@@ -103,3 +103,8 @@ def test_product_code_does_not_reach_the_oracle():
                 text = open(os.path.join(root, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "cp_oracle" not in text and "cpo_" not in text, f
+
+
+def test_dedup_workspace_query_without_a_table():
+    assert cp.cp_dedup_workspace_bytes(0, 1000) == 0
+    assert cp.cp_lookup_decode_dedup(0, 8, 1, 16, 256, 1 << 20, None) == cp.CP_ERR_INVALID_ARGUMENT

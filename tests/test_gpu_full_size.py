@@ -68,7 +68,7 @@ def test_gpu_d512_replays(big_records):
     cfg, recs = big_records
     t = make_table(LUT, recs, cfg.d, cfg.kv)
     try:
-        check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), "gpu_d512 zipf replay")
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), "gpu_d512 zipf replay", dedup=True)
         check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.uniform_variant_ids(), "gpu_d512 uniform replay")
     finally:
         t.close()
@@ -81,7 +81,7 @@ def test_host_d512_replay(big_records):
     t = make_table(LUT, recs, cfg.d, cfg.kv, residency=cp.CP_RESIDENCY_HOST_MAPPED)
     try:
         ids = hcfg.ids()
-        check_lookup(t, LUT, recs, cfg.d, cfg.kv, ids, "host_d512 zipf replay")
-        check_lookup(t, LUT, recs, cfg.d, cfg.kv, ids[:96], "host_d512 one-token slice")
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, ids, "host_d512 zipf replay", dedup=True)
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, ids[:96], "host_d512 one-token slice", dedup=True)
     finally:
         t.close()

@@ -165,3 +165,43 @@ def test_record_offsets_beyond_2_and_4_gib():
         t.close()
         del recs
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d,kv", [(64, 4), (256, 4), (512, 4), (512, 3), (512, 6)])
+def test_dedup_path_matches(d, kv):
+    rows = 2000
+    recs = workload.random_records(rows, d, kv, seed=1000 + d + kv)
+    t = make_table(LUT, recs, d, kv)
+    rng = np.random.default_rng(5)
+    try:
+        cases = {
+            "zipf": workload.zipf_ids(rows, 5000, seed=7),
+            "all same": np.full(300, 17, dtype=np.int64),
+            "all distinct": rng.permutation(rows).astype(np.int64),
+            "one": np.array([rows - 1], dtype=np.int64),
+        }
+        for name, ids in cases.items():
+            check_lookup(t, LUT, recs, d, kv, ids, f"d{d} kv{kv} dedup {name}", dedup=True)
+        bad = np.array([3, -1, 3, rows, 3, 2**62, 5], dtype=np.int64)
+        check_lookup(t, LUT, recs, d, kv, bad, f"d{d} kv{kv} dedup bad ids", expect_bad=3, dedup=True)
+    finally:
+        t.close()
+
+
+def test_dedup_rejects_a_small_workspace():
+    d, kv, rows = 512, 4, 100
+    recs = workload.random_records(rows, d, kv, seed=1100)
+    t = make_table(LUT, recs, d, kv)
+    try:
+        ids = torch.arange(50, dtype=torch.int64, device="cuda")
+        need = t.dedup_workspace_bytes(50)
+        small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+        with pytest.raises(cp.CPError):
+            t.lookup_decode_dedup(ids, workspace=small)
+        ok = torch.empty(need, dtype=torch.uint8, device="cuda")
+        out = t.lookup_decode_dedup(ids, workspace=ok)
+        torch.cuda.synchronize()
+        exp, _ = oracle.lookup_decode(LUT, recs, rows, d, kv, np.arange(50))
+        assert (out.view(torch.int16).cpu().numpy().view(np.uint16) == exp).all()
+    finally:
+        t.close()

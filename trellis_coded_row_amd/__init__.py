@@ -21,7 +21,8 @@ from . import build as _build
 __all__ = [
     "CPError", "Table", "load_library",
     "cp_record_bytes", "cp_supported", "cp_table_create", "cp_table_upload", "cp_lookup_decode",
-    "cp_lookup_decode_raw", "cp_table_check", "cp_table_describe", "cp_table_destroy",
+    "cp_lookup_decode_raw", "cp_dedup_workspace_bytes", "cp_lookup_decode_dedup",
+    "cp_table_check", "cp_table_describe", "cp_table_destroy",
     "cp_status_string", "cp_last_hip_error",
     "CP_OK", "CP_ERR_INVALID_ARGUMENT", "CP_ERR_UNSUPPORTED", "CP_ERR_OUT_OF_MEMORY", "CP_ERR_HIP",
     "CP_ERR_ID_OUT_OF_RANGE", "CP_RESIDENCY_DEVICE", "CP_RESIDENCY_HOST_MAPPED",
@@ -78,6 +79,8 @@ def load_library() -> ctypes.CDLL:
         "cp_table_upload": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp]),
         "cp_lookup_decode": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
         "cp_lookup_decode_raw": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
+        "cp_dedup_workspace_bytes": (ctypes.c_uint64, [vp, ctypes.c_uint64]),
+        "cp_lookup_decode_dedup": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp]),
         "cp_table_check": (ctypes.c_int, [vp, vp]),
         "cp_table_describe": (ctypes.c_int, [vp, ctypes.POINTER(cp_table_desc)]),
         "cp_table_destroy": (ctypes.c_int, [vp]),
@@ -133,6 +136,15 @@ def cp_lookup_decode(table: int, ids_ptr: int, n: int, out_ptr: int, stream: int
 
 def cp_lookup_decode_raw(table: int, ids_ptr: int, n: int, out_ptr: int, stream: int | None) -> int:
     return _L.cp_lookup_decode_raw(table, ids_ptr, n, out_ptr, stream)
+
+
+def cp_dedup_workspace_bytes(table: int, n: int) -> int:
+    return int(_L.cp_dedup_workspace_bytes(table, n))
+
+
+def cp_lookup_decode_dedup(table: int, ids_ptr: int, n: int, out_ptr: int, workspace_ptr: int,
+                           workspace_bytes: int, stream: int | None) -> int:
+    return _L.cp_lookup_decode_dedup(table, ids_ptr, n, out_ptr, workspace_ptr, workspace_bytes, stream)
 
 
 def cp_table_check(table: int, stream: int | None) -> int:
@@ -228,6 +240,26 @@ class Table:
         st = cp_lookup_decode_raw(self.handle, ids.data_ptr(), n, out.data_ptr(), _stream_handle(stream))
         if st != CP_OK:
             raise CPError(st, "cp_lookup_decode_raw")
+        return out
+
+    def dedup_workspace_bytes(self, n: int) -> int:
+        return cp_dedup_workspace_bytes(self.handle, n)
+
+    def lookup_decode_dedup(self, ids, out=None, workspace=None, stream=None):
+        """bf16[n, d] like lookup_decode, each distinct record fetched once.
+        workspace: a uint8 device tensor of at least dedup_workspace_bytes(n)
+        bytes (allocated here when None); scratch, reusable across calls that
+        do not overlap."""
+        import torch
+
+        n, out = self._check_io(ids, out, torch.bfloat16)
+        need = self.dedup_workspace_bytes(n)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ids.device)
+        st = cp_lookup_decode_dedup(self.handle, ids.data_ptr(), n, out.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream_handle(stream))
+        if st != CP_OK:
+            raise CPError(st, "cp_lookup_decode_dedup")
         return out
 
     def check(self, stream=None) -> bool:

@@ -152,6 +152,7 @@ static cp_status lookup(const cp_table *t, const int64_t *ids, uint64_t n, uint1
     a.lut = t->lut_dev;
     a.ids = ids;
     a.n = n;
+    a.by_offset = false;
     a.out = reinterpret_cast<uint32_t *>(out);
     a.err = t->err_dev;
     a.num_cus = t->num_cus;
@@ -169,6 +170,49 @@ cp_status cp_lookup_decode_raw(const cp_table *t, const int64_t *ids, uint64_t n
                                void *stream)
 {
     return lookup(t, ids, n, out_fp16, stream, true);
+}
+
+uint64_t cp_dedup_workspace_bytes(const cp_table *t, uint64_t n)
+{
+    if (!t) return 0;
+    return cpk::dedup_layout(n, t->record_bytes, kTailPad).total;
+}
+
+cp_status cp_lookup_decode_dedup(const cp_table *t, const int64_t *ids, uint64_t n, uint16_t *out,
+                                 void *workspace, uint64_t workspace_bytes, void *stream)
+{
+    if (!t) return CP_ERR_INVALID_ARGUMENT;
+    if (n == 0) return CP_OK;
+    if (!ids || !out || ((uintptr_t)out & 15u) || ((uintptr_t)ids & 7u)) return CP_ERR_INVALID_ARGUMENT;
+    if (n > 0x7FFFFFFFull) return CP_ERR_INVALID_ARGUMENT;  // staging indices are 32-bit
+    const cpk::DedupLayout L = cpk::dedup_layout(n, t->record_bytes, kTailPad);
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total) return CP_ERR_INVALID_ARGUMENT;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    cpk::DedupArgs d;
+    d.records = t->records_dev;
+    d.rows = t->desc.rows;
+    d.record_bytes = t->record_bytes;
+    d.ids = ids;
+    d.n = n;
+    d.workspace = ws;
+    d.layout = L;
+    d.num_cus = t->num_cus;
+    d.stream = (hipStream_t)stream;
+    hipError_t e = cpk::dedup_prepare(d);
+    if (e != hipSuccess) return hip_fail(e);
+    cpk::LaunchArgs a;
+    a.records = ws + L.staging;
+    a.rows = n;  // unused with by_offset
+    a.lut = t->lut_dev;
+    a.ids = reinterpret_cast<const int64_t *>(ws + L.staged_ids);  // record byte offsets in the staging area
+    a.n = n;
+    a.by_offset = true;
+    a.out = reinterpret_cast<uint32_t *>(out);
+    a.err = t->err_dev;
+    a.num_cus = t->num_cus;
+    a.stream = (hipStream_t)stream;
+    e = cpk::launch(t->desc.d, t->desc.bits_per_step, false, a);
+    return e == hipSuccess ? CP_OK : hip_fail(e);
 }
 
 cp_status cp_table_check(cp_table *t, void *stream)

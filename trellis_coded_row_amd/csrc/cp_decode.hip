@@ -222,7 +222,8 @@ template <int D, int KV, bool RAW, int COPIES, int BLOCK, int CHUNK>
 __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict__ tab, const uint64_t rows,
                                                        const uint32_t *__restrict__ lut,
                                                        const int64_t *__restrict__ ids, const uint64_t n,
-                                                       uint32_t *__restrict__ out, int *__restrict__ err)
+                                                       uint32_t *__restrict__ out, int *__restrict__ err,
+                                                       const bool by_offset)
 {
     constexpr int LANES = D / 8;        // lanes per row
     constexpr int GROUPS = 64 / LANES;  // rows decoded side by side in a wave
@@ -279,9 +280,11 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
         // opaque to the optimiser so that the per-row checks stay 32-bit scalar
         asm volatile("" : "+s"(cn));
         const bool in = lane < cn;
-        const bool ok = in && (uint64_t)my_id < rows;  // negative ids wrap above rows
+        // a row id in [0, rows) (negative ids wrap above rows), or with
+        // by_offset a record's byte offset in a staging area (-1: invalid)
+        const bool ok = in && (by_offset ? my_id >= 0 : (uint64_t)my_id < rows);
         bad |= in && !ok;
-        const uint64_t my_off = ok ? (uint64_t)my_id * R : 0;  // record byte offset (even)
+        const uint64_t my_off = !ok ? 0 : by_offset ? (uint64_t)my_id : (uint64_t)my_id * R;  // even
         const uint64_t okmask = __ballot(ok);
         my_id = load_id(c + waves);
 
@@ -387,7 +390,8 @@ static hipError_t launch_one(const LaunchArgs &a)
         if (blocks > cap) blocks = cap;
     }
     hipLaunchKernelGGL((gather_decode<D, KV, RAW, T::COPIES, T::BLOCK, CHUNK>), dim3((unsigned)blocks),
-                       dim3(T::BLOCK), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err);
+                       dim3(T::BLOCK), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err,
+                       a.by_offset);
     return hipGetLastError();
 }
 

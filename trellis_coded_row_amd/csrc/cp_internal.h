@@ -12,13 +12,39 @@ struct LaunchArgs {
     const uint8_t *records;   // device-accessible base of the packed records
     uint64_t rows;
     const uint32_t *lut;      // device copy of the 512-entry codebook (fp16 pairs)
-    const int64_t *ids;
+    const int64_t *ids;       // row ids, or (by_offset) record byte offsets, -1 = invalid
     uint64_t n;
+    bool by_offset;           // ids hold byte offsets of records (a staging area)
     uint32_t *out;            // n * d / 2 dwords (pairs of bf16 or fp16)
     int *err;                 // sticky out-of-range flag
     int num_cus;              // compute units of the device
     hipStream_t stream;
 };
+
+// Byte offsets of the regions of a dedup workspace (see cp_dedup.hip).
+struct DedupLayout {
+    uint64_t slots;       // hash slots (power of two)
+    uint64_t slot_bytes;  // bytes per staging slot (16-byte aligned record window)
+    uint64_t keys, sidx, slot_of, uniq, staged_ids, count, staging, total;
+};
+
+struct DedupArgs {
+    const uint8_t *records;  // device-accessible table records
+    uint64_t rows, record_bytes;
+    const int64_t *ids;
+    uint64_t n;
+    uint8_t *workspace;
+    DedupLayout layout;
+    int num_cus;
+    hipStream_t stream;
+};
+
+DedupLayout dedup_layout(uint64_t n, uint64_t record_bytes, uint64_t tail_pad);
+
+// Dedups ids into the workspace and stages each distinct record once; after
+// it, staged_ids[j] is the byte offset of lookup j's record in the staging
+// area (or -1 for a bad id).
+hipError_t dedup_prepare(const DedupArgs &a);
 
 // True when a kernel for (d, kv) is compiled in.
 bool supported(uint32_t d, uint32_t kv);
