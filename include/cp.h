@@ -153,6 +153,43 @@ uint64_t cp_dedup_workspace_bytes(const cp_table *table, uint64_t n);
 cp_status cp_lookup_decode_dedup(const cp_table *table, const int64_t *ids, uint64_t n, uint16_t *out,
                                  void *workspace, uint64_t workspace_bytes, void *stream);
 
+/* Copies records [first_row, first_row + nrows) of the table to host memory
+ * `dst` (nrows * R bytes, packed records). Waits for all work on the table's
+ * device first, so records written by cp_table_encode on any stream are
+ * included. nrows == 0 is a no-op.
+ * Errors: INVALID_ARGUMENT (NULL table/dst, range beyond rows), HIP. */
+cp_status cp_table_download(const cp_table *table, uint64_t first_row, uint64_t nrows, void *dst);
+
+/* Device workspace bytes that cp_table_encode needs for nrows rows on this
+ * table (0 for a NULL table or nrows == 0): one byte per trellis memory and
+ * step, (d / 2) * 2^(16 - kv) bytes, for each row encoded concurrently (at
+ * most one per resident 1024-thread workgroup). 1 MB per concurrent row at
+ * d = 512, kv = 4. */
+uint64_t cp_encode_workspace_bytes(const cp_table *table, uint64_t nrows);
+
+/* Encodes rows e_j (fp32, device, row-major nrows x d) into records
+ * [first_row, first_row + nrows) of the table: z = sqrt(d) e / ||e||, a
+ * tail-biting trellis-coded quantisation of z on the table's trellis, and
+ * alpha = ||e|| / ||f(c)|| rounded once to bf16 ("How it works", "How it
+ * differs": magnitude split from content, TCQ on a tail-biting trellis, the
+ * norm-restoring scale). The search is the two-pass tail-biting Viterbi
+ * heuristic: a pass from every start over the steps rotated by half a row
+ * picks the start memory, a pass from that memory alone picks the code. All
+ * arithmetic is fp64 in a fixed order with fixed tie rules, so the records
+ * are fully determined by the input. A row with zero norm is stored as the
+ * all-zero code with alpha = 0. Rows must be finite (otherwise the record is
+ * unspecified).
+ *   rows      - device fp32[nrows][d], 4-byte aligned; read only.
+ *   workspace - device memory, 256-byte aligned, at least
+ *               cp_encode_workspace_bytes(table, nrows) bytes, caller-owned
+ *               scratch; calls sharing a workspace must not overlap.
+ *   stream    - as in cp_lookup_decode. Asynchronous; no allocation.
+ * Lookups of the rows being encoded must not overlap the call.
+ * Errors: INVALID_ARGUMENT (NULL table/rows/workspace, range beyond rows,
+ * misaligned pointers, workspace too small), UNSUPPORTED, HIP. */
+cp_status cp_table_encode(cp_table *table, uint64_t first_row, uint64_t nrows, const float *rows, void *workspace,
+                          uint64_t workspace_bytes, void *stream);
+
 /* Synchronises `stream`, then returns CP_ERR_ID_OUT_OF_RANGE and clears the
  * table's flag if any lookup since the last check saw an id outside
  * [0, rows); otherwise CP_OK. Errors: INVALID_ARGUMENT, HIP. */

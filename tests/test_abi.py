@@ -108,3 +108,9 @@ def test_product_code_does_not_reach_the_oracle():
 def test_dedup_workspace_query_without_a_table():
     assert cp.cp_dedup_workspace_bytes(0, 1000) == 0
     assert cp.cp_lookup_decode_dedup(0, 8, 1, 16, 256, 1 << 20, None) == cp.CP_ERR_INVALID_ARGUMENT
+
+
+def test_encode_and_download_without_a_table():
+    assert cp.cp_encode_workspace_bytes(0, 1000) == 0
+    assert cp.cp_table_encode(0, 0, 1, 16, 256, 1 << 20, None) == cp.CP_ERR_INVALID_ARGUMENT
+    assert cp.cp_table_download(0, 0, 1, 16) == cp.CP_ERR_INVALID_ARGUMENT

@@ -1,0 +1,128 @@
+"""GPU trellis-coded quantisation (cp_table_encode) against the oracle's
+heuristic encoder: every record bit-exact (code bytes and the bf16 alpha).
+
+Both sides run the same two-pass tail-biting search in fp64 with one rounding
+per operation in the same order and the same tie rules, so the records must
+agree bit for bit; alpha is rounded once from fp64 to bf16 on both sides."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import trellis_coded_row_amd as cp
+import workload
+from parity import assert_bit_exact, check_lookup, say
+
+pytestmark = pytest.mark.gpu
+
+LUT = workload.lut_fp16()
+
+
+def gpu_encode(e32: np.ndarray, d: int, kv: int, table_rows: int | None = None, first_row: int = 0):
+    n = e32.shape[0]
+    rows = table_rows if table_rows is not None else max(n, 1)
+    t = cp.Table(rows, d, kv, LUT)
+    if first_row or rows != n:
+        t.upload(np.zeros((rows, t.record_bytes), dtype=np.uint8))
+    dev = torch.from_numpy(np.ascontiguousarray(e32, dtype=np.float32)).cuda()
+    t.encode(dev, first_row=first_row)
+    torch.cuda.synchronize()
+    return t, t.download()
+
+
+def oracle_encode(e32: np.ndarray, d: int, kv: int) -> np.ndarray:
+    recs, _ = oracle.encode_rows(e32.astype(np.float64), d, kv, LUT, mode=oracle.ENC_HEURISTIC)
+    return recs
+
+
+def check_records(got: np.ndarray, exp: np.ndarray, label: str) -> None:
+    assert got.shape == exp.shape, (label, got.shape, exp.shape)
+    bad = np.nonzero((got != exp).any(axis=1))[0]
+    if bad.size:
+        r = int(bad[0])
+        raise AssertionError(f"{label}: {bad.size} of {got.shape[0]} records differ, first row {r}: "
+                             f"got {got[r].tobytes().hex()} want {exp[r].tobytes().hex()}")
+
+
+@pytest.mark.parametrize("d,kv,n", [
+    (64, 4, 600),   # more rows than resident workgroups: the grid-stride loop
+    (64, 3, 300),
+    (64, 5, 257),
+    (64, 6, 129),
+    (128, 4, 97),
+    (256, 5, 33),
+    (256, 6, 31),
+    (512, 3, 19),
+    (512, 4, 24),
+    (512, 5, 17),
+    (512, 6, 13),
+])
+def test_encode_matches_oracle(d, kv, n):
+    e = workload.gaussian_rows(n, d, seed=7000 + d + kv).astype(np.float32)
+    say(f"encode d={d} kv={kv} n={n}")
+    exp = oracle_encode(e, d, kv)
+    t, got = gpu_encode(e, d, kv)
+    check_records(got, exp, f"encode d{d} kv{kv}")
+    # the encoded table decodes like the oracle's records
+    ids = np.arange(n, dtype=np.int64)[::-1].copy()
+    check_lookup(t, LUT, got, d, kv, ids, f"decode of encoded d{d} kv{kv}")
+    t.close()
+    say(f"encode d={d} kv={kv} n={n}: ok")
+
+
+def test_encode_special_rows():
+    d, kv = 64, 4
+    rng = np.random.default_rng(77)
+    rows = [
+        np.zeros(d),                                   # zero row: zero code, alpha 0
+        np.eye(d)[5] * 3.0,                            # one non-zero coordinate
+        np.full(d, 0.25),                              # constant row
+        rng.standard_normal(d) * 1e-40,                # float subnormals: alpha a bf16 subnormal
+        rng.standard_normal(d) * 3e37,                 # large values, alpha near the bf16 top
+        np.full(d, 3.3e38),                            # alpha rounds past the largest bf16
+        -np.full(d, 1.0),
+        rng.standard_normal(d),
+    ]
+    e = np.stack(rows).astype(np.float32)
+    e = np.concatenate([e, e[::-1]])                   # duplicates in another order
+    say(f"encode special rows d={d} kv={kv} n={e.shape[0]}")
+    exp = oracle_encode(e, d, kv)
+    assert (exp[0] == 0).all()
+    t, got = gpu_encode(e, d, kv)
+    check_records(got, exp, "special rows")
+    t.close()
+
+
+def test_encode_into_a_range_of_a_larger_table():
+    d, kv = 128, 5
+    e = workload.gaussian_rows(40, d, seed=4242).astype(np.float32)
+    exp = oracle_encode(e, d, kv)
+    say("encode rows 100..139 of a 300-row table")
+    t, got = gpu_encode(e, d, kv, table_rows=300, first_row=100)
+    check_records(got[100:140], exp, "range")
+    assert (got[:100] == 0).all() and (got[140:] == 0).all()
+    t.close()
+
+
+def test_encode_rejects_bad_arguments():
+    d, kv = 64, 4
+    t = cp.Table(16, d, kv, LUT)
+    rows = torch.zeros((8, d), dtype=torch.float32, device="cuda")
+    need = t.encode_workspace_bytes(8)
+    assert need > 0
+    small = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    st = cp.cp_table_encode(t.handle, 0, 8, rows.data_ptr(), small.data_ptr(), need - 1, None)
+    assert st == cp.CP_ERR_INVALID_ARGUMENT
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    assert cp.cp_table_encode(t.handle, 10, 8, rows.data_ptr(), ws.data_ptr(), need, None) == \
+        cp.CP_ERR_INVALID_ARGUMENT                   # rows 10..17 of 16
+    assert cp.cp_table_encode(t.handle, 0, 0, 0, 0, 0, None) == cp.CP_OK
+    assert cp.cp_table_encode(t.handle, 0, 8, rows.data_ptr(), ws.data_ptr() + 8, need, None) == \
+        cp.CP_ERR_INVALID_ARGUMENT                   # workspace not 256-byte aligned
+    assert cp.cp_table_encode(t.handle, 0, 8, rows.data_ptr(), ws.data_ptr(), need, None) == cp.CP_OK
+    torch.cuda.synchronize()
+    got = t.download(0, 8)
+    assert (got == 0).all()                          # zero rows
+    t.close()

@@ -22,6 +22,7 @@ __all__ = [
     "CPError", "Table", "load_library",
     "cp_record_bytes", "cp_supported", "cp_table_create", "cp_table_upload", "cp_lookup_decode",
     "cp_lookup_decode_raw", "cp_dedup_workspace_bytes", "cp_lookup_decode_dedup",
+    "cp_table_download", "cp_encode_workspace_bytes", "cp_table_encode",
     "cp_table_check", "cp_table_describe", "cp_table_destroy",
     "cp_status_string", "cp_last_hip_error",
     "CP_OK", "CP_ERR_INVALID_ARGUMENT", "CP_ERR_UNSUPPORTED", "CP_ERR_OUT_OF_MEMORY", "CP_ERR_HIP",
@@ -81,6 +82,9 @@ def load_library() -> ctypes.CDLL:
         "cp_lookup_decode_raw": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
         "cp_dedup_workspace_bytes": (ctypes.c_uint64, [vp, ctypes.c_uint64]),
         "cp_lookup_decode_dedup": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp]),
+        "cp_table_download": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp]),
+        "cp_encode_workspace_bytes": (ctypes.c_uint64, [vp, ctypes.c_uint64]),
+        "cp_table_encode": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp]),
         "cp_table_check": (ctypes.c_int, [vp, vp]),
         "cp_table_describe": (ctypes.c_int, [vp, ctypes.POINTER(cp_table_desc)]),
         "cp_table_destroy": (ctypes.c_int, [vp]),
@@ -88,6 +92,9 @@ def load_library() -> ctypes.CDLL:
         "cp_last_hip_error": (ctypes.c_int, []),
     }
     for name, (res, args) in sig.items():
+        if not hasattr(L, name):
+            raise ImportError(f"{path} does not export {name}: it is older than its sources; "
+                              "rebuild it (python trellis_coded_row_amd/build.py)")
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
@@ -145,6 +152,19 @@ def cp_dedup_workspace_bytes(table: int, n: int) -> int:
 def cp_lookup_decode_dedup(table: int, ids_ptr: int, n: int, out_ptr: int, workspace_ptr: int,
                            workspace_bytes: int, stream: int | None) -> int:
     return _L.cp_lookup_decode_dedup(table, ids_ptr, n, out_ptr, workspace_ptr, workspace_bytes, stream)
+
+
+def cp_table_download(table: int, first_row: int, nrows: int, dst_ptr: int) -> int:
+    return _L.cp_table_download(table, first_row, nrows, dst_ptr)
+
+
+def cp_encode_workspace_bytes(table: int, nrows: int) -> int:
+    return int(_L.cp_encode_workspace_bytes(table, nrows))
+
+
+def cp_table_encode(table: int, first_row: int, nrows: int, rows_ptr: int, workspace_ptr: int,
+                    workspace_bytes: int, stream: int | None) -> int:
+    return _L.cp_table_encode(table, first_row, nrows, rows_ptr, workspace_ptr, workspace_bytes, stream)
 
 
 def cp_table_check(table: int, stream: int | None) -> int:
@@ -261,6 +281,37 @@ class Table:
         if st != CP_OK:
             raise CPError(st, "cp_lookup_decode_dedup")
         return out
+
+    def download(self, first_row: int = 0, nrows: int | None = None) -> np.ndarray:
+        """uint8[nrows, record_bytes]: the stored records (waits for the device)."""
+        if nrows is None:
+            nrows = self.rows - first_row
+        out = np.empty((nrows, self.record_bytes), dtype=np.uint8)
+        st = cp_table_download(self.handle, first_row, nrows, out.ctypes.data)
+        if st != CP_OK:
+            raise CPError(st, "cp_table_download")
+        return out
+
+    def encode_workspace_bytes(self, nrows: int) -> int:
+        return cp_encode_workspace_bytes(self.handle, nrows)
+
+    def encode(self, rows, first_row: int = 0, workspace=None, stream=None) -> None:
+        """Encodes fp32 device rows [nrows, d] into records first_row.. of the
+        table (asynchronous on `stream`). workspace: a uint8 device tensor of
+        at least encode_workspace_bytes(nrows) bytes (allocated when None)."""
+        import torch
+
+        if not (rows.is_cuda and rows.dtype == torch.float32 and rows.dim() == 2 and rows.shape[1] == self.d
+                and rows.is_contiguous()):
+            raise ValueError(f"rows must be a contiguous float32 device tensor of shape (n, {self.d})")
+        n = rows.shape[0]
+        need = self.encode_workspace_bytes(n)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=rows.device)
+        st = cp_table_encode(self.handle, first_row, n, rows.data_ptr(), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), _stream_handle(stream))
+        if st != CP_OK:
+            raise CPError(st, "cp_table_encode")
 
     def check(self, stream=None) -> bool:
         """Synchronises; False (and the flag cleared) if an id was out of range."""

@@ -215,6 +215,59 @@ cp_status cp_lookup_decode_dedup(const cp_table *t, const int64_t *ids, uint64_t
     return e == hipSuccess ? CP_OK : hip_fail(e);
 }
 
+cp_status cp_table_download(const cp_table *t, uint64_t first_row, uint64_t nrows, void *dst)
+{
+    if (!t) return CP_ERR_INVALID_ARGUMENT;
+    if (nrows == 0) return CP_OK;
+    if (!dst || first_row > t->desc.rows || nrows > t->desc.rows - first_row) return CP_ERR_INVALID_ARGUMENT;
+    const uint64_t off = first_row * t->record_bytes, bytes = nrows * t->record_bytes;
+    hipError_t e = hipSetDevice(t->device);
+    if (e == hipSuccess) e = hipDeviceSynchronize();  // encodes in flight on any stream land first
+    if (e != hipSuccess) return hip_fail(e);
+    if (t->desc.residency == CP_RESIDENCY_HOST_MAPPED) {
+        memcpy(dst, t->records + off, bytes);
+        return CP_OK;
+    }
+    e = hipMemcpy(dst, t->records + off, bytes, hipMemcpyDeviceToHost);
+    return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
+uint64_t cp_encode_workspace_bytes(const cp_table *t, uint64_t nrows)
+{
+    if (!t || nrows == 0) return 0;
+    uint32_t blocks = 0;
+    if (cpk::encode_grid(t->desc.bits_per_step, t->num_cus, nrows, &blocks) != hipSuccess) return 0;
+    return (uint64_t)blocks * cpk::encode_workspace_per_block(t->desc.d, t->desc.bits_per_step);
+}
+
+cp_status cp_table_encode(cp_table *t, uint64_t first_row, uint64_t nrows, const float *rows, void *workspace,
+                          uint64_t workspace_bytes, void *stream)
+{
+    if (!t) return CP_ERR_INVALID_ARGUMENT;
+    if (nrows == 0) return CP_OK;
+    if (!rows || ((uintptr_t)rows & 3u) || first_row > t->desc.rows || nrows > t->desc.rows - first_row)
+        return CP_ERR_INVALID_ARGUMENT;
+    if (!cpk::encode_supported(t->desc.d, t->desc.bits_per_step)) return CP_ERR_UNSUPPORTED;
+    uint32_t blocks = 0;
+    hipError_t e = cpk::encode_grid(t->desc.bits_per_step, t->num_cus, nrows, &blocks);
+    if (e != hipSuccess) return hip_fail(e);
+    const uint64_t need = (uint64_t)blocks * cpk::encode_workspace_per_block(t->desc.d, t->desc.bits_per_step);
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return CP_ERR_INVALID_ARGUMENT;
+    cpk::EncodeArgs a;
+    a.rows = rows;
+    a.nrows = nrows;
+    a.d = t->desc.d;
+    a.kv = t->desc.bits_per_step;
+    a.lut = t->lut_dev;
+    a.out = t->records_dev + first_row * t->record_bytes;
+    a.record_bytes = t->record_bytes;
+    a.workspace = static_cast<uint8_t *>(workspace);
+    a.blocks = blocks;
+    a.stream = (hipStream_t)stream;
+    e = cpk::encode(a);
+    return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
 cp_status cp_table_check(cp_table *t, void *stream)
 {
     if (!t) return CP_ERR_INVALID_ARGUMENT;

@@ -1,0 +1,401 @@
+// cp_encode.hip - trellis-coded quantisation (TCQ) of table rows on the GPU.
+//
+// Produces the records the lookup path decodes: row e_i -> {c_i, alpha_i}
+// (Conditional Program digest on onedev.kr, sections "How it works" and "How
+// it differs"):
+//   - z = sqrt(d) e / ||e||, the magnitude split off the content;
+//   - c = the tail-biting path through the Gaussian HYB bitshift trellis that
+//     the search below picks for all d coordinates jointly, no rotation;
+//   - alpha = ||e|| / ||f(c)||, the norm-restoring scale, stored as bf16.
+// Trellis reading as in the decoder: the window of step t is bits
+// [kv(t+1)-16, kv(t+1)) of the circular code; its output pair is
+// +-LUT[((s*s + s) >> 7) & 511], negated when bit 15 of the window is set.
+//
+// Search (two-pass tail-biting heuristic). A memory is the M = 16 - kv oldest
+// bits of the next window. From memory m the kv new bits u form the window
+// s = m | u << M and lead to memory s >> kv; a next memory m2 therefore has
+// the 2^kv predecessors (m2 << kv | r) mod 2^M. Pass A runs the Viterbi
+// recursion from every memory at cost 0 over the steps rotated by T/2 and
+// reads, on the best path, the memory W held at the original start; pass B
+// runs it from W alone, and the path of pass B that ends in W is the code.
+//
+// Arithmetic: fp64, one rounding per operation, in a fixed order (no fused
+// multiply-add; sums in index order; an add-compare-select keeps the smallest
+// r among equal metrics; the end memory is the smallest among equal metrics).
+// The result is therefore one specific code, reproducible bit for bit.
+//
+// Layout on the GPU: one workgroup of 1024 threads per row; path metrics of
+// both time steps, the per-step branch costs, z and the codebook in LDS; the
+// back-pointers (one byte per memory per step) in a caller workspace.
+#pragma clang fp contract(off)
+
+#include "cp_internal.h"
+
+namespace cpk {
+
+namespace {
+
+constexpr int kThreads = 1024;
+
+__device__ __forceinline__ double half_to_double(uint32_t h16)
+{
+    return (double)(float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+// Nearest bf16 (ties to even) of a double with a single rounding: truncate to
+// float and set the lowest bit when inexact (round to odd keeps what the
+// second rounding needs, float having 16 more significant bits than bf16),
+// then round to nearest even at 8 significant bits.
+__device__ __forceinline__ uint16_t bf16_rne(double x)
+{
+    if (x != x) return 0x7FC0;
+    const float f = __double2float_rz(x);
+    uint32_t b = __builtin_bit_cast(uint32_t, f);
+    if ((double)f != x) b |= 1u;
+    if ((b & 0x7F800000u) == 0x7F800000u) return (uint16_t)(b >> 16);
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// Path-metric storage: 16 bytes of padding after every 256 bytes, so that the
+// predecessor blocks read by the lanes of a wave fall on distinct LDS banks.
+__device__ __forceinline__ uint32_t pad(uint32_t m) { return m + ((m >> 5) << 1); }
+
+template <int KV>
+struct Tcq {
+    static constexpr uint32_t M = 16 - KV;             // memory bits
+    static constexpr uint32_t S = 1u << M;             // memories
+    static constexpr uint32_t BR = 1u << KV;           // predecessors (and successors) per group
+    static constexpr uint32_t G = S / BR;              // groups sharing one predecessor set
+    static constexpr uint32_t IPT = S / kThreads;      // next memories per thread
+    static constexpr uint32_t TPG = BR / IPT;          // threads per group
+    static constexpr uint32_t CH = BR < 16 ? BR : 16;  // predecessors held in registers at once
+    static constexpr uint32_t SP = S + (S >> 4);       // padded metric array length
+    static_assert(IPT >= 1 && TPG * G == (uint32_t)kThreads, "thread mapping");
+};
+
+template <int KV>
+struct Shared {
+    double D[2][Tcq<KV>::SP];
+    double cost[2][1024];  // branch costs of one step, entry 2 * idx + negated
+    double z[512];
+    uint32_t lut[512];
+    uint8_t code[6 * 512 / 16 + 2];
+    double red_v[kThreads / 64];
+    uint32_t red_i[kThreads / 64];
+    uint32_t W;
+    double norm;
+};
+
+// cost[2 idx + neg] = (z0 - g0)^2 + (z1 - g1)^2 for the pair g = +-LUT[idx].
+__device__ __forceinline__ void fill_costs(double *cost, const uint32_t *lut, double z0, double z1)
+{
+    const uint32_t i = threadIdx.x;
+    const uint32_t e = lut[i >> 1];
+    double g0 = half_to_double(e & 0xFFFFu), g1 = half_to_double(e >> 16);
+    if (i & 1u) {
+        g0 = -g0;
+        g1 = -g1;
+    }
+    const double e0 = z0 - g0, e1 = z1 - g1;
+    cost[i] = e0 * e0 + e1 * e1;
+}
+
+// One store of a thread's IPT back-pointers (consecutive bytes).
+template <uint32_t IPT>
+__device__ __forceinline__ void store_bp(uint8_t *p, const uint32_t *br)
+{
+    if constexpr (IPT == 8) {
+        uint64_t v = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i) v |= (uint64_t)br[i] << (8 * i);
+        *reinterpret_cast<uint64_t *>(p) = v;
+    } else if constexpr (IPT == 4) {
+        *reinterpret_cast<uint32_t *>(p) = br[0] | br[1] << 8 | br[2] << 16 | br[3] << 24;
+    } else if constexpr (IPT == 2) {
+        *reinterpret_cast<uint16_t *>(p) = (uint16_t)(br[0] | br[1] << 8);
+    } else {
+        *p = (uint8_t)br[0];
+    }
+}
+
+// Position of next memory m2's back-pointer within one step's S bytes: the
+// thread owning m2 = L | u << (M - kv) stores it at L * 2^kv + u.
+template <int KV>
+__device__ __forceinline__ uint32_t bp_pos(uint32_t m2)
+{
+    using P = Tcq<KV>;
+    return ((m2 & (P::G - 1)) << KV) | (m2 >> (P::M - KV));
+}
+
+// One Viterbi pass over the T steps t = (k + rot) mod T; start < 0: every
+// memory starts at cost 0, else only `start`. bp receives T * S bytes.
+// Returns which metric buffer holds the end metrics.
+template <int KV>
+__device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t start, uint32_t rot, uint8_t *__restrict__ bp)
+{
+    using P = Tcq<KV>;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t L = tid / P::TPG, tq = tid % P::TPG;
+    for (uint32_t m = tid; m < P::S; m += kThreads)
+        sh.D[0][pad(m)] = (start < 0 || (int32_t)m == start) ? 0.0 : __builtin_inf();
+    fill_costs(sh.cost[0], sh.lut, sh.z[2 * (rot % T)], sh.z[2 * (rot % T) + 1]);
+    __syncthreads();
+    int cur = 0;
+    for (uint32_t k = 0; k < T; ++k) {
+        const double *Dc = sh.D[cur];
+        double *Dn = sh.D[cur ^ 1];
+        const double *cst = sh.cost[k & 1];
+        double best[P::IPT];
+        uint32_t br[P::IPT];
+#pragma unroll
+        for (uint32_t i = 0; i < P::IPT; ++i) {
+            best[i] = __builtin_inf();
+            br[i] = 0;
+        }
+#pragma unroll
+        for (uint32_t c = 0; c < P::BR / P::CH; ++c) {
+            double Dv[P::CH];
+            const double *src = Dc + pad((L << KV) | (c * P::CH));
+#pragma unroll
+            for (uint32_t j = 0; j < P::CH; ++j) Dv[j] = src[j];
+#pragma unroll
+            for (uint32_t i = 0; i < P::IPT; ++i) {
+                const uint32_t u = tq * P::IPT + i;
+                const uint32_t base = (L << KV) | (u << P::M) | (c * P::CH);
+                const uint32_t sg = u >> (KV - 1);
+#pragma unroll
+                for (uint32_t j = 0; j < P::CH; ++j) {
+                    const uint32_t s = base | j;
+                    const uint32_t h = s * s + s;
+                    const double v = Dv[j] + cst[((h >> 6) & 0x3FEu) | sg];
+                    if (v < best[i]) {
+                        best[i] = v;
+                        br[i] = c * P::CH + j;
+                    }
+                }
+                // keep the scheduler from hoisting every later gather above
+                // this group (it would exceed the register budget)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < P::IPT; ++i) {
+            const uint32_t u = tq * P::IPT + i;
+            Dn[pad(L | (u << (P::M - KV)))] = best[i];
+        }
+        store_bp<P::IPT>(bp + (uint64_t)k * P::S + tid * P::IPT, br);
+        if (k + 1 < T) {
+            const uint32_t t1 = (k + 1 + rot) % T;
+            fill_costs(sh.cost[(k + 1) & 1], sh.lut, sh.z[2 * t1], sh.z[2 * t1 + 1]);
+        }
+        __syncthreads();
+        cur ^= 1;
+    }
+    return cur;
+}
+
+// Smallest metric over all memories, the smallest memory on ties.
+template <int KV>
+__device__ __forceinline__ uint32_t argmin_memory(Shared<KV> &sh, const double *D)
+{
+    using P = Tcq<KV>;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
+    double bv = __builtin_inf();
+    uint32_t bi = 0xFFFFFFFFu;
+    for (uint32_t m = tid; m < P::S; m += kThreads) {
+        const double v = D[pad(m)];
+        if (v < bv || (v == bv && m < bi)) {
+            bv = v;
+            bi = m;
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        const double ov = __shfl_down(bv, off, 64);
+        const uint32_t oi = __shfl_down(bi, off, 64);
+        if (lane + off < 64 && (ov < bv || (ov == bv && oi < bi))) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    if (lane == 0) {
+        sh.red_v[w] = bv;
+        sh.red_i[w] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double v = sh.red_v[0];
+        uint32_t i = sh.red_i[0];
+        for (uint32_t q = 1; q < kThreads / 64; ++q)
+            if (sh.red_v[q] < v || (sh.red_v[q] == v && sh.red_i[q] < i)) {
+                v = sh.red_v[q];
+                i = sh.red_i[q];
+            }
+        // every metric infinite (not reachable from a finite row): memory 0
+        sh.W = i == 0xFFFFFFFFu ? 0u : i;
+    }
+    __syncthreads();
+    const uint32_t r = sh.W;
+    __syncthreads();
+    return r;
+}
+
+template <int KV>
+__global__ __launch_bounds__(kThreads) void tcq_encode_rows(const float *__restrict__ e, uint64_t nrows,
+                                                            uint32_t d, const uint32_t *__restrict__ lut,
+                                                            uint8_t *__restrict__ out, uint64_t record_bytes,
+                                                            uint8_t *__restrict__ workspace)
+{
+    using P = Tcq<KV>;
+    __shared__ Shared<KV> sh;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t T = d / 2, N = KV * T, NB = N / 8;
+    uint8_t *bp = workspace + (uint64_t)blockIdx.x * T * P::S;
+    if (tid < 512) sh.lut[tid] = lut[tid];
+
+    for (uint64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
+        const float *er = e + row * d;
+        uint8_t *rec = out + row * record_bytes;
+        for (uint32_t b = tid; b < NB + 2; b += kThreads) sh.code[b] = 0;
+        if (tid == 0) {
+            double n2 = 0.0;
+            for (uint32_t i = 0; i < d; ++i) {
+                const double v = (double)er[i];
+                n2 = n2 + v * v;
+            }
+            sh.norm = __builtin_sqrt(n2);
+        }
+        __syncthreads();
+        const double norm = sh.norm;
+        if (norm > 0.0) {
+            const double sd = __builtin_sqrt((double)d);
+            for (uint32_t i = tid; i < d; i += kThreads) sh.z[i] = sd * (double)er[i] / norm;
+            __syncthreads();
+
+            // pass A (p = 0): every start, steps rotated by T/2; W = the best
+            // path's memory before step 0, i.e. after step T-1, which pass A
+            // visits as k = T-rot-1. Pass B (p = 1): from W alone; the path
+            // ending in W is the code.
+            const uint32_t rot = T / 2;
+            uint32_t W = 0;
+            for (int p = 0; p < 2; ++p) {
+                const int cend = viterbi_pass<KV>(sh, T, p == 0 ? -1 : (int32_t)W, p == 0 ? rot : 0, bp);
+                const uint32_t end = p == 0 ? argmin_memory<KV>(sh, sh.D[cend]) : W;
+                if (tid == 0) {
+                    uint32_t m2 = end, w = 0;
+                    for (int32_t k = (int32_t)T - 1; k >= 0; --k) {
+                        if ((uint32_t)k == T - rot - 1) w = m2;
+                        const uint32_t r = bp[(uint64_t)k * P::S + bp_pos<KV>(m2)];
+                        const uint32_t s = ((m2 << KV) | r) & 0xFFFFu;
+                        if (p == 1) {
+                            const uint32_t u = s >> P::M;
+                            for (uint32_t i = 0; i < (uint32_t)KV; ++i)
+                                if ((u >> i) & 1u) {
+                                    const uint32_t j = KV * (uint32_t)k + i;
+                                    sh.code[j >> 3] |= (uint8_t)(1u << (j & 7));
+                                }
+                        }
+                        m2 = s & (P::S - 1);
+                    }
+                    sh.W = w;
+                }
+                __syncthreads();
+                if (p == 0) W = sh.W;
+                __syncthreads();
+            }
+
+            // f(c) of the emitted code (in the cost buffer, free now), then alpha
+            uint32_t *f = reinterpret_cast<uint32_t *>(sh.cost[0]);
+            for (uint32_t t = tid; t < T; t += kThreads) {
+                uint32_t s = 0;
+                for (uint32_t q = 0; q < 16; ++q) {
+                    const uint32_t j = (KV * (t + 1) + N - 16 + q) % N;
+                    s |= (uint32_t)((sh.code[j >> 3] >> (j & 7)) & 1u) << q;
+                }
+                const uint32_t h = s * s + s;
+                uint32_t pr = sh.lut[(h >> 7) & 511u];
+                if (s & 0x8000u) pr ^= 0x80008000u;
+                f[t] = pr;
+            }
+            __syncthreads();
+            if (tid == 0) {
+                double fn2 = 0.0;
+                for (uint32_t t = 0; t < T; ++t) {
+                    const double a = half_to_double(f[t] & 0xFFFFu), b = half_to_double(f[t] >> 16);
+                    fn2 = fn2 + a * a;
+                    fn2 = fn2 + b * b;
+                }
+                const double alpha = fn2 > 0.0 ? norm / __builtin_sqrt(fn2) : 0.0;
+                const uint16_t ab = bf16_rne(alpha);
+                sh.code[NB] = (uint8_t)(ab & 0xFFu);
+                sh.code[NB + 1] = (uint8_t)(ab >> 8);
+            }
+        }
+        // a zero row (or one whose norm is not finite and positive) keeps the
+        // all-zero code and alpha 0
+        __syncthreads();
+        for (uint32_t b = tid; b < NB + 2; b += kThreads) rec[b] = sh.code[b];
+        __syncthreads();
+    }
+}
+
+const void *encode_kernel(uint32_t kv)
+{
+    switch (kv) {
+    case 3: return reinterpret_cast<const void *>(&tcq_encode_rows<3>);
+    case 4: return reinterpret_cast<const void *>(&tcq_encode_rows<4>);
+    case 5: return reinterpret_cast<const void *>(&tcq_encode_rows<5>);
+    case 6: return reinterpret_cast<const void *>(&tcq_encode_rows<6>);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+bool encode_supported(uint32_t d, uint32_t kv)
+{
+    return (d == 64 || d == 128 || d == 256 || d == 512) && kv >= 3 && kv <= 6;
+}
+
+hipError_t encode_grid(uint32_t kv, int num_cus, uint64_t nrows, uint32_t *blocks)
+{
+    *blocks = 0;
+    const void *k = encode_kernel(kv);
+    if (!k) return hipErrorInvalidValue;
+    int per_cu = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0);
+    if (e != hipSuccess) return e;
+    if (per_cu < 1) return hipErrorInvalidConfiguration;
+    const uint64_t most = (uint64_t)per_cu * (uint64_t)(num_cus > 0 ? num_cus : 1);
+    *blocks = (uint32_t)(nrows < most ? nrows : most);
+    return hipSuccess;
+}
+
+uint64_t encode_workspace_per_block(uint32_t d, uint32_t kv) { return (uint64_t)(d / 2) << (16 - kv); }
+
+hipError_t encode(const EncodeArgs &a)
+{
+    if (a.nrows == 0 || a.blocks == 0) return hipSuccess;
+    switch (a.kv) {
+    case 3:
+        hipLaunchKernelGGL(tcq_encode_rows<3>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
+                           a.lut, a.out, a.record_bytes, a.workspace);
+        break;
+    case 4:
+        hipLaunchKernelGGL(tcq_encode_rows<4>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
+                           a.lut, a.out, a.record_bytes, a.workspace);
+        break;
+    case 5:
+        hipLaunchKernelGGL(tcq_encode_rows<5>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
+                           a.lut, a.out, a.record_bytes, a.workspace);
+        break;
+    case 6:
+        hipLaunchKernelGGL(tcq_encode_rows<6>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
+                           a.lut, a.out, a.record_bytes, a.workspace);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cpk

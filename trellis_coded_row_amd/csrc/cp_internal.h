@@ -46,6 +46,26 @@ DedupLayout dedup_layout(uint64_t n, uint64_t record_bytes, uint64_t tail_pad);
 // area (or -1 for a bad id).
 hipError_t dedup_prepare(const DedupArgs &a);
 
+// Launch parameters of one encode call (see cp_encode.hip).
+struct EncodeArgs {
+    const float *rows;         // nrows * d fp32 values, row-major, device
+    uint64_t nrows;
+    uint32_t d, kv;
+    const uint32_t *lut;       // device codebook (fp16 pairs)
+    uint8_t *out;              // nrows packed records (device-accessible)
+    uint64_t record_bytes;
+    uint8_t *workspace;        // blocks * encode_workspace_per_block(d, kv) bytes
+    uint32_t blocks;           // from encode_grid
+    hipStream_t stream;
+};
+
+bool encode_supported(uint32_t d, uint32_t kv);
+// Workgroups one encode launch uses for nrows rows (all resident at once).
+hipError_t encode_grid(uint32_t kv, int num_cus, uint64_t nrows, uint32_t *blocks);
+// Back-pointer bytes per workgroup: (d / 2) steps * 2^(16 - kv) memories.
+uint64_t encode_workspace_per_block(uint32_t d, uint32_t kv);
+hipError_t encode(const EncodeArgs &a);
+
 // True when a kernel for (d, kv) is compiled in.
 bool supported(uint32_t d, uint32_t kv);
 
