@@ -127,6 +127,91 @@ def pcie_probe(torch, mib: int = 1024) -> dict:
     return {"h2d_GBps": n * 4 / ms / 1e6, "MiB": mib}
 
 
+VALU_PEAK_TOPS = 39.3  # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: one 64-bit VALU op per lane-slot
+
+
+def bench_encode(args, np, torch, cp, workload) -> int:
+    """Trellis-coded quantisation of a batch of rows (cp_table_encode): one
+    step = encode the whole batch. The add-compare-select of the Viterbi
+    recursion dominates: 2 passes x T steps x 2^16 branches per row, each an
+    fp64 add and an fp64 compare, i.e. 2 * 2 * (d/2) * 2^16 algorithmic fp64
+    operations per row, bounded by the VALU issue rate."""
+    d, kv, n = args.encode_d, args.encode_kv, args.encode_rows
+    lut = workload.lut_fp16(0)
+    e = workload.gaussian_rows(n, d, seed=9100).astype(np.float32)
+    table = cp.Table(n, d, kv, lut)
+    rows = torch.from_numpy(e).cuda()
+    ws = torch.empty(table.encode_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    step = lambda: table.encode(rows, workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    total_ms = time_region(step, args.steps, torch)
+    wall_s = time.perf_counter() - wall0
+    ms = total_ms / args.steps
+    branches = 2 * (d // 2) * (1 << 16) * n
+    ops = 2 * branches
+    achieved = ops / (ms / 1e3) / 1e12
+    res = {
+        "metric": "encoded rows/s (trellis-coded quantisation, two-pass tail-biting Viterbi)",
+        "value": n / (ms / 1e3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": f"encode_d{d}_kv{kv}: {n:,} Gaussian rows (d={d}) quantised to {kv / 2:g} bits/element "
+                        f"+ bf16 scale ({table.record_bytes}-byte records)",
+            "rows": n, "d": d, "bits_per_step": kv, "entry_point": "cp_table_encode",
+            "workspace_bytes": table.encode_workspace_bytes(n),
+        },
+        "wall_s_timed_region": wall_s,
+        "roofline": {
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": VALU_PEAK_TOPS,
+            "unit": "TOP/s",
+            "frac": achieved / VALU_PEAK_TOPS,
+            "traffic": None,
+            "algorithmic_ops_per_launch": ops,
+            "kernel": f"tcq_encode_rows<{kv}>",
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle  # CPU baseline leg only
+
+        threads = max(1, min(16, os.cpu_count() or 1))
+        cal = min(n, threads)
+        t = time.perf_counter()
+        oracle.encode_rows(e[:cal].astype(np.float64), d, kv, lut, mode=oracle.ENC_HEURISTIC, nthreads=threads)
+        per_row = (time.perf_counter() - t) / cal
+        sample = int(min(n, max(cal, args.cpu_seconds / max(per_row, 1e-9))))
+        t = time.perf_counter()
+        exp, _ = oracle.encode_rows(e[:sample].astype(np.float64), d, kv, lut, mode=oracle.ENC_HEURISTIC,
+                                    nthreads=threads)
+        cpu_s = time.perf_counter() - t
+        got = table.download(0, sample)
+        res["cpu_baseline"] = {
+            "value": sample / cpu_s,
+            "unit": "rows/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {sample:,} of the {n:,} rows ({cpu_s:.1f} s, {threads} threads, plain C oracle, "
+                      "same two-pass search)",
+            "gpu_records_matching_oracle": int((got == exp).all(axis=1).sum()),
+        }
+    table.close()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +228,11 @@ def main() -> int:
                     help="also time launches with L2/MALL flushed (512 MiB written) before each")
     ap.add_argument("--probes", action="store_true", help="also run 1 GiB copy and fill probes")
     ap.add_argument("--extra", action="store_true", help="--flushed and --probes")
+    ap.add_argument("--encode", action="store_true",
+                    help="time cp_table_encode instead (trellis-coded quantisation of --encode-rows rows)")
+    ap.add_argument("--encode-rows", type=int, default=4096)
+    ap.add_argument("--encode-d", type=int, default=512)
+    ap.add_argument("--encode-kv", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     args = ap.parse_args()
@@ -163,6 +253,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.encode:
+        return bench_encode(args, np, torch, cp, workload)
     cfg = workload.CONFIGS[args.config]
     ids_kind = args.ids or cfg.ids_kind
     lut = workload.lut_fp16(0)

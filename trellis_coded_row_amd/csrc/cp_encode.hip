@@ -57,7 +57,8 @@ __device__ __forceinline__ uint16_t bf16_rne(double x)
 }
 
 // Path-metric storage: 16 bytes of padding after every 256 bytes, so that the
-// predecessor blocks read by the lanes of a wave fall on distinct LDS banks.
+// predecessor metrics read by consecutive lanes (consecutive groups) fall on
+// different LDS banks.
 __device__ __forceinline__ uint32_t pad(uint32_t m) { return m + ((m >> 5) << 1); }
 
 template <int KV>
@@ -68,7 +69,6 @@ struct Tcq {
     static constexpr uint32_t G = S / BR;              // groups sharing one predecessor set
     static constexpr uint32_t IPT = S / kThreads;      // next memories per thread
     static constexpr uint32_t TPG = BR / IPT;          // threads per group
-    static constexpr uint32_t CH = BR < 16 ? BR : 16;  // predecessors held in registers at once
     static constexpr uint32_t SP = S + (S >> 4);       // padded metric array length
     static_assert(IPT >= 1 && TPG * G == (uint32_t)kThreads, "thread mapping");
 };
@@ -118,13 +118,20 @@ __device__ __forceinline__ void store_bp(uint8_t *p, const uint32_t *br)
     }
 }
 
-// Position of next memory m2's back-pointer within one step's S bytes: the
-// thread owning m2 = L | u << (M - kv) stores it at L * 2^kv + u.
+// Thread mapping: thread tid serves group L = tid mod G (the next memories
+// m2 = L | u << (M - kv) share the predecessors L << kv | r) and its IPT
+// successors u = (tid / G) * IPT + i. Consecutive lanes thus take consecutive
+// groups, whose windows differ in their low bits, which spreads the branch
+// cost gathers over the LDS banks (lanes sharing a group would read costs at
+// indices that agree in their low bits). A thread stores the back-pointers of
+// its IPT next memories as IPT consecutive bytes at tid * IPT; this is the
+// position of next memory m2 within one step's S bytes.
 template <int KV>
 __device__ __forceinline__ uint32_t bp_pos(uint32_t m2)
 {
     using P = Tcq<KV>;
-    return ((m2 & (P::G - 1)) << KV) | (m2 >> (P::M - KV));
+    const uint32_t L = m2 & (P::G - 1), u = m2 >> (P::M - KV);
+    return ((u / P::IPT) * P::G + L) * P::IPT + u % P::IPT;
 }
 
 // One Viterbi pass over the T steps t = (k + rot) mod T; start < 0: every
@@ -135,7 +142,7 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
 {
     using P = Tcq<KV>;
     const uint32_t tid = threadIdx.x;
-    const uint32_t L = tid / P::TPG, tq = tid % P::TPG;
+    const uint32_t L = tid % P::G, tq = tid / P::G;
     for (uint32_t m = tid; m < P::S; m += kThreads)
         sh.D[0][pad(m)] = (start < 0 || (int32_t)m == start) ? 0.0 : __builtin_inf();
     fill_costs(sh.cost[0], sh.lut, sh.z[2 * (rot % T)], sh.z[2 * (rot % T) + 1]);
@@ -152,31 +159,38 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
             best[i] = __builtin_inf();
             br[i] = 0;
         }
+        // software-pipelined: the branch costs of predecessor r + 1 are
+        // requested before the add-compare-selects of predecessor r
+        double cv[2][P::IPT];
 #pragma unroll
-        for (uint32_t c = 0; c < P::BR / P::CH; ++c) {
-            double Dv[P::CH];
-            const double *src = Dc + pad((L << KV) | (c * P::CH));
+        for (uint32_t i = 0; i < P::IPT; ++i) {
+            const uint32_t u = tq * P::IPT + i;
+            const uint32_t s = (L << KV) | (u << P::M);
+            const uint32_t h = s * s + s;
+            cv[0][i] = cst[((h >> 6) & 0x3FEu) | (u >> (KV - 1))];
+        }
 #pragma unroll
-            for (uint32_t j = 0; j < P::CH; ++j) Dv[j] = src[j];
+        for (uint32_t r = 0; r < P::BR; ++r) {
+            if (r + 1 < P::BR) {
+#pragma unroll
+                for (uint32_t i = 0; i < P::IPT; ++i) {
+                    const uint32_t u = tq * P::IPT + i;
+                    const uint32_t s = (L << KV) | (u << P::M) | (r + 1);
+                    const uint32_t h = s * s + s;
+                    cv[(r + 1) & 1][i] = cst[((h >> 6) & 0x3FEu) | (u >> (KV - 1))];
+                }
+            }
+            const double dv = Dc[pad((L << KV) | r)];
 #pragma unroll
             for (uint32_t i = 0; i < P::IPT; ++i) {
-                const uint32_t u = tq * P::IPT + i;
-                const uint32_t base = (L << KV) | (u << P::M) | (c * P::CH);
-                const uint32_t sg = u >> (KV - 1);
-#pragma unroll
-                for (uint32_t j = 0; j < P::CH; ++j) {
-                    const uint32_t s = base | j;
-                    const uint32_t h = s * s + s;
-                    const double v = Dv[j] + cst[((h >> 6) & 0x3FEu) | sg];
-                    if (v < best[i]) {
-                        best[i] = v;
-                        br[i] = c * P::CH + j;
-                    }
+                const double v = dv + cv[r & 1][i];
+                if (v < best[i]) {
+                    best[i] = v;
+                    br[i] = r;
                 }
-                // keep the scheduler from hoisting every later gather above
-                // this group (it would exceed the register budget)
-                __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, P::IPT + 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6 * P::IPT, 0);
         }
 #pragma unroll
         for (uint32_t i = 0; i < P::IPT; ++i) {
