@@ -84,6 +84,25 @@ typedef struct {
     uint32_t reserved;      /* 0 */
 } cp_table_desc;
 
+/* Shape of a mixed-rate table: every row has a rate class, and class c is
+ * coded at bits_per_step[c]. The pages study giving rows bits by how often
+ * they are looked up, over their code rates of 1.5 / 2 / 2.5 / 3 bits per
+ * element ("How it is used"; "Assumptions and limits", which also warns that
+ * the access counts behind such an allocation may not carry over between text
+ * domains); they give no format. Here the records of all rows are packed in
+ * row order, each at its own class's rate (cp_record_bytes(d, kv_c)), so a
+ * row's record starts at the sum of the sizes of the records before it. */
+typedef struct {
+    uint32_t struct_size;      /* sizeof(cp_mixed_desc) */
+    uint32_t d;                /* 64, 128, 256 or 512 */
+    uint32_t nclass;           /* 1..4 rate classes */
+    uint32_t bits_per_step[4]; /* kv of class c, 3..6; 0 for c >= nclass */
+    uint32_t residency;        /* cp_residency */
+    uint64_t rows;             /* >= 1 */
+    uint32_t flags;            /* CP_FLAG_* */
+    uint32_t reserved;         /* 0 */
+} cp_mixed_desc;
+
 /* Bytes of one record: kv*d/16 code bytes + 2 scale bytes, i.e. b + 16/d bits
  * per parameter at b = kv/2 ("How it works"). Returns 0 when (d, kv) cannot
  * form a whole-byte code of at least 16 bits. */
@@ -104,8 +123,34 @@ int cp_supported(uint32_t d, uint32_t bits_per_step);
  * residency or flags), UNSUPPORTED, OUT_OF_MEMORY, HIP. */
 cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, cp_table **out);
 
+/* Creates a mixed-rate table on the current HIP device.
+ *   desc      - shape, rate classes and residency; copied.
+ *   lut_fp16  - as in cp_table_create.
+ *   row_class - host uint8[rows], the class (< nclass) of each row; read
+ *               during the call only.
+ * Besides the records (their total size follows from the classes) the table
+ * keeps an index of 16 bytes per 32 rows in device memory (a byte offset and
+ * two class bit planes per block of rows), from which a lookup finds any
+ * record with a few popcounts. cp_table_upload / cp_table_download /
+ * cp_lookup_decode / cp_lookup_decode_raw / cp_table_check /
+ * cp_table_destroy work as for single-rate tables (record ranges given by the
+ * rows' own sizes); cp_table_describe reports bits_per_step = 0;
+ * cp_lookup_decode_dedup and cp_table_encode return UNSUPPORTED.
+ * Errors: INVALID_ARGUMENT (NULL pointers, struct_size, rows == 0, nclass,
+ * a class's rate without whole-byte records, a nonzero unused rate, a row
+ * class >= nclass, residency or flags), UNSUPPORTED (no kernel for d or a
+ * rate), OUT_OF_MEMORY, HIP. */
+cp_status cp_table_create_mixed(const cp_mixed_desc *desc, const uint16_t *lut_fp16, const uint8_t *row_class,
+                                cp_table **out);
+
+/* Byte offset and size of row `row`'s record within the table's packed
+ * records (row * R and R for a single-rate table).
+ * Errors: INVALID_ARGUMENT (NULL pointers, row >= rows). */
+cp_status cp_table_record_range(const cp_table *table, uint64_t row, uint64_t *offset, uint64_t *bytes);
+
 /* Copies records [first_row, first_row + nrows) from host memory `src`
- * (nrows * R bytes, packed records) into the table. Synchronous: the data
+ * (the rows' packed records: nrows * R bytes, or the sum of the rows' own
+ * sizes for a mixed-rate table) into the table. Synchronous: the data
  * has landed when it returns. nrows == 0 is a no-op.
  * Errors: INVALID_ARGUMENT (NULL table/src, range beyond rows), HIP. */
 cp_status cp_table_upload(cp_table *table, uint64_t first_row, uint64_t nrows, const void *src);
@@ -197,6 +242,10 @@ cp_status cp_table_check(cp_table *table, void *stream);
 
 /* Reads back the table's shape. Errors: INVALID_ARGUMENT. */
 cp_status cp_table_describe(const cp_table *table, cp_table_desc *desc_out);
+
+/* Reads back the shape with its rate classes (a single-rate table reports one
+ * class). Errors: INVALID_ARGUMENT. */
+cp_status cp_table_describe_mixed(const cp_table *table, cp_mixed_desc *desc_out);
 
 /* Frees the table (no pending lookups may use it). NULL is a no-op (CP_OK). */
 cp_status cp_table_destroy(cp_table *table);

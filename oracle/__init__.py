@@ -80,6 +80,15 @@ def lib() -> ctypes.CDLL:
                 [u16p, u8p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, i64p,
                  ctypes.c_uint64, u16p, ctypes.c_int, ctypes.c_int],
             ),
+            "cpo_mixed_offsets": (
+                ctypes.c_int,
+                [ctypes.c_uint64, ctypes.c_uint32, u32p, ctypes.c_uint32, u8p, ctypes.POINTER(ctypes.c_uint64)],
+            ),
+            "cpo_lookup_decode_mixed": (
+                ctypes.c_int64,
+                [u16p, u8p, ctypes.c_uint64, ctypes.c_uint32, u32p, ctypes.c_uint32, u8p,
+                 ctypes.POINTER(ctypes.c_uint64), i64p, ctypes.c_uint64, u16p, ctypes.c_int, ctypes.c_int],
+            ),
             "cpo_tcq_encode": (
                 ctypes.c_double,
                 [f64p, ctypes.c_uint32, ctypes.c_uint32, u16p, ctypes.c_int, ctypes.c_uint32,
@@ -202,6 +211,46 @@ def lookup_decode(lut, records, rows: int, d: int, kv: int, ids, raw: bool = Fal
     bad = lib().cpo_lookup_decode(
         _p(lut, ctypes.c_uint16), _p(records, ctypes.c_uint8), rows, d, kv,
         _p(ids, ctypes.c_int64), n, _p(out, ctypes.c_uint16), int(raw), nthreads)
+    if bad < 0:
+        raise ValueError("unsupported (d, kv)")
+    return out, int(bad)
+
+
+def mixed_offsets(d: int, kv_of_class, row_class) -> np.ndarray:
+    """uint64[rows + 1]: where each row's record starts in a mixed-rate table
+    (records packed in row order, each at its class's rate); the last entry
+    is the total size."""
+    kvs = _c(kv_of_class, np.uint32).reshape(-1)
+    cls = _c(row_class, np.uint8).reshape(-1)
+    rows = cls.shape[0]
+    off = np.empty(rows + 1, dtype=np.uint64)
+    st = lib().cpo_mixed_offsets(rows, d, _p(kvs, ctypes.c_uint32), kvs.shape[0], _p(cls, ctypes.c_uint8),
+                                 _p(off, ctypes.c_uint64))
+    if st:
+        raise ValueError("bad class or rate")
+    return off
+
+
+def lookup_decode_mixed(lut, records, d: int, kv_of_class, row_class, ids, raw: bool = False,
+                        offsets=None, nthreads: int | None = None) -> tuple[np.ndarray, int]:
+    """Rows ids[j] of a mixed-rate table, in lookup order; as lookup_decode.
+    offsets: from mixed_offsets (computed here when None)."""
+    lut = _c(lut, np.uint16).reshape(-1)
+    records = np.ascontiguousarray(records, dtype=np.uint8).reshape(-1)
+    kvs = _c(kv_of_class, np.uint32).reshape(-1)
+    cls = _c(row_class, np.uint8).reshape(-1)
+    if offsets is None:
+        offsets = mixed_offsets(d, kvs, cls)
+    offsets = _c(offsets, np.uint64)
+    ids = _c(ids, np.int64).reshape(-1)
+    n = ids.shape[0]
+    out = np.empty((n, d), dtype=np.uint16)
+    if nthreads is None:
+        nthreads = default_threads()
+    bad = lib().cpo_lookup_decode_mixed(
+        _p(lut, ctypes.c_uint16), _p(records, ctypes.c_uint8), cls.shape[0], d, _p(kvs, ctypes.c_uint32),
+        kvs.shape[0], _p(cls, ctypes.c_uint8), _p(offsets, ctypes.c_uint64), _p(ids, ctypes.c_int64), n,
+        _p(out, ctypes.c_uint16), int(raw), nthreads)
     if bad < 0:
         raise ValueError("unsupported (d, kv)")
     return out, int(bad)

@@ -51,6 +51,11 @@
  *   R7 encoder objective: minimise ||z - f(c)||^2 over tail-biting codes with
  *      unit scale; alpha is set afterwards from the norms. Ties keep the
  *      smallest predecessor and then the smallest start memory.
+ *   R10 mixed-rate table (the pages study allocating bits by access frequency
+ *      over their code rates but give no format): each row has a rate class,
+ *      class c codes at kv_c bits per step, and the records of all rows are
+ *      packed in row order, so row i's record starts at the sum of the record
+ *      sizes of rows 0..i-1.
  */
 #include "cp_oracle.h"
 
@@ -228,6 +233,10 @@ typedef struct {
     const uint8_t *records;
     uint64_t rows;
     uint32_t d, kv;
+    /* mixed-rate tables (R10): NULL for a single-rate table */
+    const uint32_t *kv_of_class;
+    const uint8_t *row_class;
+    const uint64_t *offsets;
     const int64_t *ids;
     uint64_t begin, end;
     uint16_t *out;
@@ -249,13 +258,39 @@ static void *lookup_worker(void *arg)
             job->bad++;
             continue;
         }
+        uint32_t kv = job->kv;
         const uint8_t *rec = job->records + (uint64_t)id * rbytes;
+        if (job->row_class) {
+            kv = job->kv_of_class[job->row_class[id]];
+            rec = job->records + job->offsets[id];
+        }
         if (job->raw)
-            cpo_decode_code(job->lut, rec, job->d, job->kv, dst);
+            cpo_decode_code(job->lut, rec, job->d, kv, dst);
         else
-            cpo_decode_record(job->lut, rec, job->d, job->kv, dst);
+            cpo_decode_record(job->lut, rec, job->d, kv, dst);
     }
     return NULL;
+}
+
+/* Runs the lookup jobs on nthreads threads; returns the bad-id count. */
+static int64_t run_lookup(lookup_job proto, uint64_t n, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    lookup_job jobs[256];
+    pthread_t th[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = proto;
+        jobs[i].begin = n * (uint64_t)i / (uint64_t)nthreads;
+        jobs[i].end = n * (uint64_t)(i + 1) / (uint64_t)nthreads;
+        jobs[i].bad = 0;
+    }
+    for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, lookup_worker, &jobs[i]);
+    lookup_worker(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i) pthread_join(th[i], NULL);
+    int64_t bad = 0;
+    for (int i = 0; i < nthreads; ++i) bad += (int64_t)jobs[i].bad;
+    return bad;
 }
 
 /* Decodes rows ids[0..n) of a packed record table into out[n][d] (bf16 bits,
@@ -268,22 +303,49 @@ int64_t cpo_lookup_decode(const uint16_t *lut, const uint8_t *records, uint64_t 
                           uint16_t *out, int raw, int nthreads)
 {
     if (!cpo_record_bytes(d, kv)) return -1;
-    if (nthreads < 1) nthreads = 1;
-    if (nthreads > 256) nthreads = 256;
-    lookup_job jobs[256];
-    pthread_t th[256];
-    for (int i = 0; i < nthreads; ++i) {
-        lookup_job j = {lut, records, rows, d, kv, ids,
-                        n * (uint64_t)i / (uint64_t)nthreads,
-                        n * (uint64_t)(i + 1) / (uint64_t)nthreads, out, raw, 0};
-        jobs[i] = j;
+    lookup_job proto = {lut, records, rows, d, kv, NULL, NULL, NULL, ids, 0, 0, out, raw, 0};
+    return run_lookup(proto, n, nthreads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* mixed-rate tables (R10)                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Record offsets of a mixed-rate table: row i is coded at
+ * kv_of_class[row_class[i]] bits per step, and the records are packed in row
+ * order with nothing between them, so row i starts at the sum of the record
+ * sizes of rows 0..i-1. offsets[0..rows] (offsets[rows] = total bytes).
+ * Returns 0, or -1 for a class >= nclass or a rate without whole-byte
+ * records. The pages study bit allocation by access frequency over their code
+ * rates [KO "How it is used" (1.5 / 2 / 2.5 / 3 bits), "Assumptions and
+ * limits"; EN Perspective]; how rates are chosen is the caller's. */
+int cpo_mixed_offsets(uint64_t rows, uint32_t d, const uint32_t *kv_of_class, uint32_t nclass,
+                      const uint8_t *row_class, uint64_t *offsets)
+{
+    uint64_t acc = 0;
+    for (uint64_t i = 0; i < rows; ++i) {
+        if (row_class[i] >= nclass) return -1;
+        uint64_t r = cpo_record_bytes(d, kv_of_class[row_class[i]]);
+        if (!r) return -1;
+        offsets[i] = acc;
+        acc += r;
     }
-    for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, lookup_worker, &jobs[i]);
-    lookup_worker(&jobs[0]);
-    for (int i = 1; i < nthreads; ++i) pthread_join(th[i], NULL);
-    int64_t bad = 0;
-    for (int i = 0; i < nthreads; ++i) bad += (int64_t)jobs[i].bad;
-    return bad;
+    offsets[rows] = acc;
+    return 0;
+}
+
+/* Lookup into a mixed-rate table: as cpo_lookup_decode, row id's record
+ * being the one at offsets[id], decoded at its class's rate. */
+int64_t cpo_lookup_decode_mixed(const uint16_t *lut, const uint8_t *records, uint64_t rows, uint32_t d,
+                                const uint32_t *kv_of_class, uint32_t nclass, const uint8_t *row_class,
+                                const uint64_t *offsets, const int64_t *ids, uint64_t n, uint16_t *out,
+                                int raw, int nthreads)
+{
+    for (uint32_t c = 0; c < nclass; ++c)
+        if (!cpo_record_bytes(d, kv_of_class[c])) return -1;
+    lookup_job proto = {lut, records, rows, d, kv_of_class[0], kv_of_class, row_class, offsets, ids, 0, 0,
+                        out, raw, 0};
+    return run_lookup(proto, n, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -41,6 +41,13 @@ int64_t cpo_lookup_decode(const uint16_t *lut, const uint8_t *records, uint64_t 
                           uint32_t d, uint32_t kv, const int64_t *ids, uint64_t n,
                           uint16_t *out, int raw, int nthreads);
 
+int cpo_mixed_offsets(uint64_t rows, uint32_t d, const uint32_t *kv_of_class, uint32_t nclass,
+                      const uint8_t *row_class, uint64_t *offsets);
+int64_t cpo_lookup_decode_mixed(const uint16_t *lut, const uint8_t *records, uint64_t rows, uint32_t d,
+                                const uint32_t *kv_of_class, uint32_t nclass, const uint8_t *row_class,
+                                const uint64_t *offsets, const int64_t *ids, uint64_t n, uint16_t *out,
+                                int raw, int nthreads);
+
 double cpo_tcq_encode(const double *z, uint32_t d, uint32_t kv, const uint16_t *lut, int mode,
                       uint32_t max_starts, uint8_t *code_out, cpo_encode_info *info);
 double cpo_distortion(const double *z, const uint16_t *lut, const uint8_t *code, uint32_t d,

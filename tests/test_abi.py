@@ -114,3 +114,72 @@ def test_encode_and_download_without_a_table():
     assert cp.cp_encode_workspace_bytes(0, 1000) == 0
     assert cp.cp_table_encode(0, 0, 1, 16, 256, 1 << 20, None) == cp.CP_ERR_INVALID_ARGUMENT
     assert cp.cp_table_download(0, 0, 1, 16) == cp.CP_ERR_INVALID_ARGUMENT
+
+
+def _mdesc(**kw):
+    base = dict(struct_size=ctypes.sizeof(cp.cp_mixed_desc), d=64, nclass=2,
+                bits_per_step=(ctypes.c_uint32 * 4)(4, 3, 0, 0), residency=0, rows=8, flags=0, reserved=0)
+    base.update(kw)
+    return cp.cp_mixed_desc(**base)
+
+
+def test_mixed_create_rejects_bad_descriptors_before_touching_the_device():
+    lut = (ctypes.c_uint16 * 1024)()
+    cls = (ctypes.c_uint8 * 8)(0, 1, 0, 1, 1, 1, 0, 0)
+    bad_cls = (ctypes.c_uint8 * 8)(0, 1, 2, 1, 1, 1, 0, 0)
+    lp, cp_ = ctypes.addressof(lut), ctypes.addressof(cls)
+    u4 = lambda *v: (ctypes.c_uint32 * 4)(*v)
+    cases = [
+        (_mdesc(struct_size=40), cp_, cp.CP_ERR_INVALID_ARGUMENT),
+        (_mdesc(nclass=0), cp_, cp.CP_ERR_INVALID_ARGUMENT),
+        (_mdesc(nclass=5), cp_, cp.CP_ERR_INVALID_ARGUMENT),
+        (_mdesc(bits_per_step=u4(4, 3, 5, 0)), cp_, cp.CP_ERR_INVALID_ARGUMENT),  # unused class set
+        (_mdesc(bits_per_step=u4(4, 7, 0, 0)), cp_, cp.CP_ERR_UNSUPPORTED),
+        (_mdesc(d=96), cp_, cp.CP_ERR_UNSUPPORTED),
+        (_mdesc(d=10), cp_, cp.CP_ERR_INVALID_ARGUMENT),
+        (_mdesc(rows=0), cp_, cp.CP_ERR_INVALID_ARGUMENT),
+        (_mdesc(residency=3), cp_, cp.CP_ERR_INVALID_ARGUMENT),
+        (_mdesc(), ctypes.addressof(bad_cls), cp.CP_ERR_INVALID_ARGUMENT),  # class 2 of 2
+        (_mdesc(), 0, cp.CP_ERR_INVALID_ARGUMENT),
+    ]
+    for desc, cls_p, want in cases:
+        st, h = cp.cp_table_create_mixed(desc, lp, cls_p)
+        assert (st, h) == (want, 0), (desc.d, desc.nclass, list(desc.bits_per_step))
+
+
+def test_descriptor_layouts_match_the_header(tmp_path):
+    # the ctypes mirrors must have the C layout (compiled with the host compiler)
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "cp.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu\\n", sizeof(cp_table_desc), '
+                   'offsetof(cp_table_desc, rows), sizeof(cp_mixed_desc), offsetof(cp_mixed_desc, rows), '
+                   'offsetof(cp_mixed_desc, residency)); return 0; }\n')
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(cpbuild.ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    want = [ctypes.sizeof(cp.cp_table_desc), cp.cp_table_desc.rows.offset, ctypes.sizeof(cp.cp_mixed_desc),
+            cp.cp_mixed_desc.rows.offset, cp.cp_mixed_desc.residency.offset]
+    assert [int(x) for x in got] == want
+
+
+def test_record_range_without_a_table():
+    st, _, _ = cp.cp_table_record_range(0, 0)
+    assert st == cp.CP_ERR_INVALID_ARGUMENT
+    st, _ = cp.cp_table_describe_mixed(0)
+    assert st == cp.CP_ERR_INVALID_ARGUMENT
+
+
+def test_one_hip_runtime_in_the_process():
+    # the binding loads torch's HIP runtime before the library, so importing
+    # the package alone (torch not yet imported) maps a single libamdhip64
+    import subprocess
+    import sys
+
+    code = ("import trellis_coded_row_amd\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
+                         cwd=cpbuild.ROOT).stdout.split()
+    assert out[-1] == "1"

@@ -85,3 +85,23 @@ def test_host_d512_replay(big_records):
         check_lookup(t, LUT, recs, cfg.d, cfg.kv, ids[:96], "host_d512 one-token slice", dedup=True)
     finally:
         t.close()
+
+
+def test_mixed_d512_replay():
+    """The 97.69 M-row mixed-rate table (rates by Zipf access rank), the whole
+    replay compared with the oracle's mixed-rate lookup."""
+    from test_gpu_mixed import check_mixed, make_mixed
+
+    cfg = workload.CONFIGS["mixed_d512"]
+    kvs = cfg.extra["kv_of_class"]
+    say("building the 97,690,000-row mixed-rate table")
+    cls = workload.rank_classes(cfg.rows, cfg.ids_seed, cfg.extra["shares"])
+    packed = workload.random_mixed_records(cfg.d, kvs, cls, cfg.table_seed)
+    off = oracle.mixed_offsets(cfg.d, kvs, cls)
+    t = make_mixed(cfg.d, kvs, cls, packed, chunk=1 << 24)
+    try:
+        for r in (0, 12_345_678, cfg.rows - 1):
+            assert t.record_range(r) == (int(off[r]), int(off[r + 1] - off[r]))
+        check_mixed(t, cfg.d, kvs, cls, packed, cfg.ids(), "mixed_d512 zipf replay", offsets=off)
+    finally:
+        t.close()

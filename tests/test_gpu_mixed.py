@@ -1,0 +1,105 @@
+"""Mixed-rate tables on the GPU (cp_table_create_mixed + cp_lookup_decode)
+against the oracle's mixed-rate lookup: f(c) bit-exact, scaled rows within
+1 bf16 ulp, record ranges equal to the oracle's offsets."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import trellis_coded_row_amd as cp
+import workload
+from parity import assert_bf16_within_ulp, assert_bit_exact, device_lookup, say
+
+pytestmark = pytest.mark.gpu
+
+LUT = workload.lut_fp16()
+
+
+def make_mixed(d, kvs, cls, packed, residency=cp.CP_RESIDENCY_DEVICE, chunk=1 << 20):
+    t = cp.MixedTable(d, kvs, cls, LUT, residency=residency)
+    off = workload.mixed_layout(d, kvs, cls)
+    for r0 in range(0, cls.size, chunk):
+        r1 = min(cls.size, r0 + chunk)
+        t.upload_bytes(packed[int(off[r0]):int(off[r1])], r0, r1 - r0)
+    return t
+
+
+def check_mixed(t, d, kvs, cls, packed, ids, label, offsets=None, expect_bad=0):
+    say(f"{label}: n={ids.shape[0]} d={d} rates={kvs} rows={cls.size}")
+    exp_raw, bad = oracle.lookup_decode_mixed(LUT, packed, d, kvs, cls, ids, raw=True, offsets=offsets)
+    exp, _ = oracle.lookup_decode_mixed(LUT, packed, d, kvs, cls, ids, offsets=offsets)
+    assert bad == expect_bad
+    got_raw = device_lookup(t, ids, raw=True)
+    assert t.check() == (expect_bad == 0)
+    assert_bit_exact(got_raw, exp_raw, label + " f(c)")
+    got = device_lookup(t, ids)
+    assert t.check() == (expect_bad == 0)
+    ndiff = assert_bf16_within_ulp(got, exp, label + " rows")
+    say(f"{label}: ok (scaled rows differing from the oracle: {ndiff})")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("kvs", [(6, 5, 4, 3), (3, 6), (5,)])
+def test_mixed_lookup_matches_oracle(d, kvs):
+    rows = 3001
+    rng = np.random.default_rng(d * 7 + len(kvs))
+    cls = rng.integers(0, len(kvs), size=rows).astype(np.uint8)
+    packed = workload.random_mixed_records(d, kvs, cls, seed=d + 11)
+    t = make_mixed(d, kvs, cls, packed)
+    # record ranges: the library's index against the oracle's running sum
+    off = oracle.mixed_offsets(d, kvs, cls)
+    for r in (0, 1, 31, 32, 33, 1000, rows - 1):
+        assert t.record_range(r) == (int(off[r]), int(off[r + 1] - off[r])), r
+    ids = np.concatenate([rng.integers(0, rows, size=2000), np.arange(rows - 40, rows), [0, 0, rows - 1]])
+    check_mixed(t, d, kvs, cls, packed, ids.astype(np.int64), f"mixed d{d} {kvs}")
+    # ragged batch with ids outside the table
+    bad = ids[:517].copy()
+    bad[::50] = rows + 5
+    bad[7] = -1
+    check_mixed(t, d, kvs, cls, packed, bad.astype(np.int64), f"mixed bad ids d{d} {kvs}",
+                expect_bad=int(((bad < 0) | (bad >= rows)).sum()))
+    st, desc = cp.cp_table_describe_mixed(t.handle)
+    assert st == cp.CP_OK and desc.nclass == len(kvs) and list(desc.bits_per_step)[:len(kvs)] == list(kvs)
+    t.close()
+
+
+def test_mixed_one_row_table_and_empty_batch():
+    d, kvs = 512, (3, 6)
+    cls = np.array([1], dtype=np.uint8)
+    packed = workload.random_mixed_records(d, kvs, cls, seed=5)
+    t = make_mixed(d, kvs, cls, packed)
+    check_mixed(t, d, kvs, cls, packed, np.array([0, 0, 1, 0], dtype=np.int64), "one row", expect_bad=1)
+    out = t.lookup_decode(torch.empty(0, dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    assert out.shape == (0, d)
+    t.close()
+
+
+def test_mixed_host_resident():
+    d, kvs = 256, (6, 4, 3)
+    rows = 5000
+    cls = np.random.default_rng(3).integers(0, 3, size=rows).astype(np.uint8)
+    packed = workload.random_mixed_records(d, kvs, cls, seed=12)
+    t = make_mixed(d, kvs, cls, packed, residency=cp.CP_RESIDENCY_HOST_MAPPED)
+    ids = workload.zipf_ids(rows, 3000, seed=4)
+    check_mixed(t, d, kvs, cls, packed, ids, "mixed host-resident")
+    assert (t.download(100, 50) == packed[int(t.record_range(100)[0]):int(sum(t.record_range(149)))]).all()
+    t.close()
+
+
+def test_mixed_unsupported_paths():
+    d, kvs = 64, (4, 3)
+    cls = np.zeros(64, dtype=np.uint8)
+    t = cp.MixedTable(d, kvs, cls, LUT)
+    assert t.dedup_workspace_bytes(10) == 0 and t.encode_workspace_bytes(10) == 0
+    ids = torch.zeros(4, dtype=torch.int64, device="cuda")
+    out = torch.empty((4, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    assert cp.cp_lookup_decode_dedup(t.handle, ids.data_ptr(), 4, out.data_ptr(), ws.data_ptr(), 1 << 20,
+                                     None) == cp.CP_ERR_UNSUPPORTED
+    rows = torch.zeros((4, d), dtype=torch.float32, device="cuda")
+    assert cp.cp_table_encode(t.handle, 0, 4, rows.data_ptr(), ws.data_ptr(), 1 << 20, None) == \
+        cp.CP_ERR_UNSUPPORTED
+    t.close()

@@ -368,3 +368,65 @@ def test_distortion_between_rate_distortion_bound_and_scalar_quantiser():
     costs = [oracle.tcq_encode(zi, d, kv, LUT, oracle.ENC_HEURISTIC).cost for zi in z]
     mse = float(np.mean(costs)) / d
     assert 0.0625 < mse < 0.1175, mse
+
+
+# ---------------------------------------------------------------------------
+# mixed-rate tables (reading R10)
+# ---------------------------------------------------------------------------
+
+def test_mixed_offsets_are_the_running_sum_of_record_sizes():
+    # d = 64: records of kv 6 / 5 / 4 / 3 are 26 / 22 / 18 / 14 bytes
+    cls = np.array([0, 3, 3, 1, 2, 0], dtype=np.uint8)
+    off = oracle.mixed_offsets(64, (6, 5, 4, 3), cls)
+    assert off.tolist() == [0, 26, 40, 54, 76, 94, 120]
+    with pytest.raises(ValueError):
+        oracle.mixed_offsets(64, (6, 5), cls)  # class 3 of only 2
+
+
+def test_mixed_lookup_with_one_class_is_the_single_rate_lookup():
+    d, kv, rows = 128, 5, 300
+    recs = workload.random_records(rows, d, kv, seed=61)
+    ids = np.random.default_rng(5).integers(-3, rows + 3, size=700)
+    cls = np.zeros(rows, dtype=np.uint8)
+    for raw in (False, True):
+        exp, bad = oracle.lookup_decode(LUT, recs, rows, d, kv, ids, raw=raw)
+        got, bad2 = oracle.lookup_decode_mixed(LUT, recs.reshape(-1), d, (kv,), cls, ids, raw=raw)
+        assert bad == bad2 > 0
+        assert (got == exp).all()
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_mixed_lookup_reads_each_row_at_its_own_rate(d):
+    # four single-rate tables; the mixed table takes row i from the table of
+    # row i's class, so its lookups must equal those single-rate lookups
+    rows = 400
+    kvs = (6, 5, 4, 3)
+    tables = [workload.random_records(rows, d, k, seed=70 + k) for k in kvs]
+    cls = np.random.default_rng(9).integers(0, 4, size=rows).astype(np.uint8)
+    packed = np.concatenate([tables[c][i] for i, c in enumerate(cls)])
+    ids = np.random.default_rng(10).integers(0, rows, size=1000)
+    got, bad = oracle.lookup_decode_mixed(LUT, packed, d, kvs, cls, ids)
+    assert bad == 0
+    for c, k in enumerate(kvs):
+        sel = cls[ids] == c
+        exp, _ = oracle.lookup_decode(LUT, tables[c], rows, d, k, ids[sel])
+        assert (got[sel] == exp).all(), c
+    # and the workload's packer lays the records out where the oracle reads them
+    off = oracle.mixed_offsets(d, kvs, cls)
+    assert (workload.mixed_layout(d, kvs, cls) == off).all()
+    rec = workload.random_mixed_records(d, kvs, cls, seed=3)
+    assert rec.size == int(off[-1])
+    for i in (0, 1, rows - 1):
+        R = workload.record_bytes(d, kvs[cls[i]])
+        nb = R - 2
+        a = int(rec[off[i] + nb]) | int(rec[off[i] + nb + 1]) << 8
+        assert 0x3D00 <= a <= 0x4180, hex(a)  # a lognormal(0, 0.5) scale (e^-3.5 .. e^3.5)
+
+
+def test_rank_classes_follow_access_rank():
+    rows = 100_000
+    cls = workload.rank_classes(rows, seed=202)
+    assert np.bincount(cls, minlength=4).tolist() == [5_000, 15_000, 30_000, 50_000]
+    ids = workload.zipf_ids(rows, 50_000, seed=202)
+    share = np.bincount(cls[ids], minlength=4) / ids.size
+    assert share[0] > 0.8 and share[3] < 0.05  # hot rows are the high-rate ones

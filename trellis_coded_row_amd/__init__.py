@@ -16,6 +16,12 @@ import os
 
 import numpy as np
 
+# torch first: its HIP runtime must be the one libcp.so binds to. Loaded the
+# other way round, the library pulls in the system's libamdhip64 and torch
+# then brings its own, so the process holds two HIP runtimes and the streams
+# and device pointers torch hands over belong to the other one.
+import torch  # noqa: F401
+
 from . import build as _build
 
 __all__ = [
@@ -23,6 +29,7 @@ __all__ = [
     "cp_record_bytes", "cp_supported", "cp_table_create", "cp_table_upload", "cp_lookup_decode",
     "cp_lookup_decode_raw", "cp_dedup_workspace_bytes", "cp_lookup_decode_dedup",
     "cp_table_download", "cp_encode_workspace_bytes", "cp_table_encode",
+    "cp_table_create_mixed", "cp_table_record_range", "cp_table_describe_mixed", "cp_mixed_desc", "MixedTable",
     "cp_table_check", "cp_table_describe", "cp_table_destroy",
     "cp_status_string", "cp_last_hip_error",
     "CP_OK", "CP_ERR_INVALID_ARGUMENT", "CP_ERR_UNSUPPORTED", "CP_ERR_OUT_OF_MEMORY", "CP_ERR_HIP",
@@ -46,6 +53,19 @@ class cp_table_desc(ctypes.Structure):
         ("struct_size", ctypes.c_uint32),
         ("d", ctypes.c_uint32),
         ("bits_per_step", ctypes.c_uint32),
+        ("residency", ctypes.c_uint32),
+        ("rows", ctypes.c_uint64),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+class cp_mixed_desc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("d", ctypes.c_uint32),
+        ("nclass", ctypes.c_uint32),
+        ("bits_per_step", ctypes.c_uint32 * 4),
         ("residency", ctypes.c_uint32),
         ("rows", ctypes.c_uint64),
         ("flags", ctypes.c_uint32),
@@ -77,6 +97,10 @@ def load_library() -> ctypes.CDLL:
         "cp_record_bytes": (ctypes.c_uint64, [ctypes.c_uint32, ctypes.c_uint32]),
         "cp_supported": (ctypes.c_int, [ctypes.c_uint32, ctypes.c_uint32]),
         "cp_table_create": (ctypes.c_int, [ctypes.POINTER(cp_table_desc), vp, ctypes.POINTER(vp)]),
+        "cp_table_create_mixed": (ctypes.c_int, [ctypes.POINTER(cp_mixed_desc), vp, vp, ctypes.POINTER(vp)]),
+        "cp_table_record_range": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64),
+                                                 ctypes.POINTER(ctypes.c_uint64)]),
+        "cp_table_describe_mixed": (ctypes.c_int, [vp, ctypes.POINTER(cp_mixed_desc)]),
         "cp_table_upload": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp]),
         "cp_lookup_decode": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
         "cp_lookup_decode_raw": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
@@ -106,6 +130,7 @@ _L = load_library()
 
 
 class CPError(RuntimeError):
+
     def __init__(self, status: int, what: str):
         self.status = status
         msg = f"{what}: {cp_status_string(status)}"
@@ -131,6 +156,26 @@ def cp_table_create(desc: cp_table_desc, lut_ptr: int) -> tuple[int, int]:
     h = ctypes.c_void_p()
     st = _L.cp_table_create(ctypes.byref(desc), lut_ptr, ctypes.byref(h))
     return st, (h.value or 0)
+
+
+def cp_table_create_mixed(desc: cp_mixed_desc, lut_ptr: int, row_class_ptr: int) -> tuple[int, int]:
+    """Returns (status, table handle or 0)."""
+    h = ctypes.c_void_p()
+    st = _L.cp_table_create_mixed(ctypes.byref(desc), lut_ptr, row_class_ptr, ctypes.byref(h))
+    return st, (h.value or 0)
+
+
+def cp_table_record_range(table: int, row: int) -> tuple[int, int, int]:
+    """Returns (status, byte offset, bytes) of a row's record."""
+    off, nb = ctypes.c_uint64(), ctypes.c_uint64()
+    st = _L.cp_table_record_range(table, row, ctypes.byref(off), ctypes.byref(nb))
+    return st, int(off.value), int(nb.value)
+
+
+def cp_table_describe_mixed(table: int) -> tuple[int, cp_mixed_desc]:
+    desc = cp_mixed_desc()
+    st = _L.cp_table_describe_mixed(table, ctypes.byref(desc))
+    return st, desc
 
 
 def cp_table_upload(table: int, first_row: int, nrows: int, src_ptr: int) -> int:
@@ -194,8 +239,6 @@ def cp_last_hip_error() -> int:
 # --------------------------------------------------------------------------
 
 def _stream_handle(stream) -> int | None:
-    import torch
-
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -229,9 +272,14 @@ class Table:
         if st != CP_OK:
             raise CPError(st, "cp_table_upload")
 
-    def _check_io(self, ids, out, dtype):
-        import torch
+    def record_range(self, row: int) -> tuple[int, int]:
+        """(byte offset, bytes) of a row's record in the packed records."""
+        st, off, nb = cp_table_record_range(self.handle, row)
+        if st != CP_OK:
+            raise CPError(st, "cp_table_record_range")
+        return off, nb
 
+    def _check_io(self, ids, out, dtype):
         if not (ids.is_cuda and ids.dtype == torch.int64 and ids.dim() == 1 and ids.is_contiguous()):
             raise ValueError("ids must be a contiguous 1-D int64 device tensor")
         n = ids.shape[0]
@@ -244,8 +292,6 @@ class Table:
 
     def lookup_decode(self, ids, out=None, stream=None):
         """bf16[n, d]: alpha * f(c) of rows ids[j], in lookup order."""
-        import torch
-
         n, out = self._check_io(ids, out, torch.bfloat16)
         st = cp_lookup_decode(self.handle, ids.data_ptr(), n, out.data_ptr(), _stream_handle(stream))
         if st != CP_OK:
@@ -254,8 +300,6 @@ class Table:
 
     def lookup_decode_raw(self, ids, out=None, stream=None):
         """fp16[n, d]: the unscaled f(c) of rows ids[j], in lookup order."""
-        import torch
-
         n, out = self._check_io(ids, out, torch.float16)
         st = cp_lookup_decode_raw(self.handle, ids.data_ptr(), n, out.data_ptr(), _stream_handle(stream))
         if st != CP_OK:
@@ -270,8 +314,6 @@ class Table:
         workspace: a uint8 device tensor of at least dedup_workspace_bytes(n)
         bytes (allocated here when None); scratch, reusable across calls that
         do not overlap."""
-        import torch
-
         n, out = self._check_io(ids, out, torch.bfloat16)
         need = self.dedup_workspace_bytes(n)
         if workspace is None:
@@ -299,8 +341,6 @@ class Table:
         """Encodes fp32 device rows [nrows, d] into records first_row.. of the
         table (asynchronous on `stream`). workspace: a uint8 device tensor of
         at least encode_workspace_bytes(nrows) bytes (allocated when None)."""
-        import torch
-
         if not (rows.is_cuda and rows.dtype == torch.float32 and rows.dim() == 2 and rows.shape[1] == self.d
                 and rows.is_contiguous()):
             raise ValueError(f"rows must be a contiguous float32 device tensor of shape (n, {self.d})")
@@ -340,3 +380,55 @@ class Table:
             self.close()
         except Exception:
             pass
+
+
+class MixedTable(Table):
+    """A mixed-rate CP table: row i is coded at bits_per_step[row_class[i]].
+    Records are uploaded as the rows' packed bytes (``upload_bytes``); lookups
+    are those of ``Table``."""
+
+    def __init__(self, d: int, bits_per_step, row_class: np.ndarray, lut_fp16: np.ndarray,
+                 residency: int = CP_RESIDENCY_DEVICE, flags: int = 0):
+        lut = np.ascontiguousarray(lut_fp16, dtype=np.uint16).reshape(-1)
+        if lut.size != 1024:
+            raise ValueError("the codebook has 512 entries of 2 fp16 values")
+        cls = np.ascontiguousarray(row_class, dtype=np.uint8).reshape(-1)
+        kvs = list(bits_per_step)
+        if not 1 <= len(kvs) <= 4:
+            raise ValueError("1 to 4 rate classes")
+        arr = (ctypes.c_uint32 * 4)(*(kvs + [0] * (4 - len(kvs))))
+        desc = cp_mixed_desc(ctypes.sizeof(cp_mixed_desc), d, len(kvs), arr, residency, cls.size, flags, 0)
+        st, h = cp_table_create_mixed(desc, lut.ctypes.data, cls.ctypes.data)
+        if st != CP_OK:
+            raise CPError(st, "cp_table_create_mixed")
+        self.handle = h
+        self.rows, self.d, self.bits_per_step = cls.size, d, 0
+        self.rates = tuple(kvs)
+        self.residency = residency
+        self.record_bytes = 0
+
+    def upload(self, records: np.ndarray, first_row: int = 0) -> None:
+        raise TypeError("use upload_bytes(packed, first_row, nrows) on a mixed-rate table")
+
+    def upload_bytes(self, packed: np.ndarray, first_row: int, nrows: int) -> None:
+        """packed: the uint8 records of rows [first_row, first_row + nrows), back to back."""
+        buf = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1)
+        off0, _ = self.record_range(first_row)
+        off1, nb1 = self.record_range(first_row + nrows - 1)
+        if buf.size != off1 + nb1 - off0:
+            raise ValueError(f"expected {off1 + nb1 - off0} bytes, got {buf.size}")
+        st = cp_table_upload(self.handle, first_row, nrows, buf.ctypes.data)
+        if st != CP_OK:
+            raise CPError(st, "cp_table_upload")
+
+    def download(self, first_row: int = 0, nrows: int | None = None) -> np.ndarray:
+        """uint8[bytes]: the packed records of rows [first_row, first_row + nrows)."""
+        if nrows is None:
+            nrows = self.rows - first_row
+        off0, _ = self.record_range(first_row)
+        off1, nb1 = self.record_range(first_row + nrows - 1)
+        out = np.empty(off1 + nb1 - off0, dtype=np.uint8)
+        st = cp_table_download(self.handle, first_row, nrows, out.ctypes.data)
+        if st != CP_OK:
+            raise CPError(st, "cp_table_download")
+        return out

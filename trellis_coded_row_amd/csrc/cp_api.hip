@@ -8,9 +8,16 @@
 #include "cp_internal.h"
 
 struct cp_table {
-    cp_table_desc desc;
-    uint64_t record_bytes;
+    cp_table_desc desc;     // bits_per_step = 0 for a mixed-rate table
+    uint64_t record_bytes;  // single-rate tables; 0 for a mixed-rate table
     uint64_t alloc_bytes;
+    uint64_t records_bytes;  // bytes of all records (without the tail pad)
+    // mixed-rate tables
+    uint32_t mixed, nclass;
+    uint32_t kv_of_class[4];
+    cpk::MixedRates rates;
+    cpk::MixedEntry *index_dev;
+    cpk::MixedEntry *index_host;
     uint8_t *records;      // hipMalloc'd (device) or hipHostMalloc'd (host)
     uint8_t *records_dev;  // device-accessible address of the same memory
     uint32_t *lut_dev;
@@ -72,8 +79,42 @@ static void release(cp_table *t)
             (void)hipFree(t->records);
     }
     if (t->lut_dev) (void)hipFree(t->lut_dev);
+    if (t->index_dev) (void)hipFree(t->index_dev);
+    free(t->index_host);
     if (t->err_dev) (void)hipFree(t->err_dev);
     free(t);
+}
+
+// Allocates the record storage (rows' records + the zeroed tail pad), the
+// codebook and the error flag of a table whose descriptor fields are set.
+static cp_status allocate(cp_table *t, const uint16_t *lut_fp16)
+{
+    t->alloc_bytes = t->records_bytes + kTailPad;
+    hipError_t e = hipGetDevice(&t->device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&t->num_cus, hipDeviceAttributeMultiprocessorCount, t->device);
+    if (e != hipSuccess) return hip_fail(e);
+    if (t->desc.residency == CP_RESIDENCY_HOST_MAPPED) {
+        unsigned flags = hipHostMallocMapped;
+        if (t->desc.flags & CP_FLAG_HOST_NONCOHERENT) flags |= hipHostMallocNonCoherent;
+        e = hipHostMalloc((void **)&t->records, t->alloc_bytes, flags);
+        if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&t->records_dev, t->records, 0);
+        if (e == hipSuccess) memset(t->records + t->records_bytes, 0, kTailPad);
+    } else {
+        e = hipMalloc((void **)&t->records, t->alloc_bytes);
+        t->records_dev = t->records;
+        if (e == hipSuccess) e = hipMemset(t->records + t->records_bytes, 0, kTailPad);
+    }
+    if (e == hipSuccess) e = hipMalloc((void **)&t->lut_dev, 512 * sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemcpy(t->lut_dev, lut_fp16, 512 * sizeof(uint32_t), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMalloc((void **)&t->err_dev, sizeof(int));
+    if (e == hipSuccess) e = hipMemset(t->err_dev, 0, sizeof(int));
+    return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
+static bool valid_residency(uint32_t residency, uint32_t flags)
+{
+    if (residency != CP_RESIDENCY_DEVICE && residency != CP_RESIDENCY_HOST_MAPPED) return false;
+    return (flags & ~(uint32_t)CP_FLAG_HOST_NONCOHERENT) == 0;
 }
 
 cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, cp_table **out)
@@ -82,9 +123,7 @@ cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, c
     if (!desc || !lut_fp16 || !out) return CP_ERR_INVALID_ARGUMENT;
     if (desc->struct_size != sizeof(cp_table_desc) || desc->rows == 0 || desc->reserved != 0)
         return CP_ERR_INVALID_ARGUMENT;
-    if (desc->residency != CP_RESIDENCY_DEVICE && desc->residency != CP_RESIDENCY_HOST_MAPPED)
-        return CP_ERR_INVALID_ARGUMENT;
-    if (desc->flags & ~(uint32_t)CP_FLAG_HOST_NONCOHERENT) return CP_ERR_INVALID_ARGUMENT;
+    if (!valid_residency(desc->residency, desc->flags)) return CP_ERR_INVALID_ARGUMENT;
     const uint64_t R = cp_record_bytes(desc->d, desc->bits_per_step);
     if (R == 0) return CP_ERR_INVALID_ARGUMENT;
     if (!cpk::supported(desc->d, desc->bits_per_step)) return CP_ERR_UNSUPPORTED;
@@ -94,34 +133,97 @@ cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, c
     if (!t) return CP_ERR_OUT_OF_MEMORY;
     t->desc = *desc;
     t->record_bytes = R;
-    t->alloc_bytes = desc->rows * R + kTailPad;
-
-    hipError_t e = hipGetDevice(&t->device);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&t->num_cus, hipDeviceAttributeMultiprocessorCount, t->device);
-    if (e != hipSuccess) {
+    t->records_bytes = desc->rows * R;
+    const cp_status st = allocate(t, lut_fp16);
+    if (st != CP_OK) {
         release(t);
-        return hip_fail(e);
-    }
-    if (desc->residency == CP_RESIDENCY_HOST_MAPPED) {
-        unsigned flags = hipHostMallocMapped;
-        if (desc->flags & CP_FLAG_HOST_NONCOHERENT) flags |= hipHostMallocNonCoherent;
-        e = hipHostMalloc((void **)&t->records, t->alloc_bytes, flags);
-        if (e == hipSuccess) e = hipHostGetDevicePointer((void **)&t->records_dev, t->records, 0);
-        if (e == hipSuccess) memset(t->records + desc->rows * R, 0, kTailPad);
-    } else {
-        e = hipMalloc((void **)&t->records, t->alloc_bytes);
-        t->records_dev = t->records;
-        if (e == hipSuccess) e = hipMemset(t->records + desc->rows * R, 0, kTailPad);
-    }
-    if (e == hipSuccess) e = hipMalloc((void **)&t->lut_dev, 512 * sizeof(uint32_t));
-    if (e == hipSuccess) e = hipMemcpy(t->lut_dev, lut_fp16, 512 * sizeof(uint32_t), hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipMalloc((void **)&t->err_dev, sizeof(int));
-    if (e == hipSuccess) e = hipMemset(t->err_dev, 0, sizeof(int));
-    if (e != hipSuccess) {
-        release(t);
-        return hip_fail(e);
+        return st;
     }
     *out = t;
+    return CP_OK;
+}
+
+cp_status cp_table_create_mixed(const cp_mixed_desc *desc, const uint16_t *lut_fp16, const uint8_t *row_class,
+                                cp_table **out)
+{
+    if (out) *out = nullptr;
+    if (!desc || !lut_fp16 || !row_class || !out) return CP_ERR_INVALID_ARGUMENT;
+    if (desc->struct_size != sizeof(cp_mixed_desc) || desc->rows == 0 || desc->reserved != 0)
+        return CP_ERR_INVALID_ARGUMENT;
+    if (desc->nclass < 1 || desc->nclass > 4) return CP_ERR_INVALID_ARGUMENT;
+    if (!valid_residency(desc->residency, desc->flags)) return CP_ERR_INVALID_ARGUMENT;
+    uint32_t R[4] = {0, 0, 0, 0};
+    for (uint32_t c = 0; c < desc->nclass; ++c) {
+        R[c] = (uint32_t)cp_record_bytes(desc->d, desc->bits_per_step[c]);
+        if (R[c] == 0) return CP_ERR_INVALID_ARGUMENT;
+        if (!cpk::supported(desc->d, desc->bits_per_step[c])) return CP_ERR_UNSUPPORTED;
+    }
+    for (uint32_t c = desc->nclass; c < 4; ++c)
+        if (desc->bits_per_step[c] != 0) return CP_ERR_INVALID_ARGUMENT;
+    if (!cpk::mixed_supported(desc->d)) return CP_ERR_UNSUPPORTED;
+    if (desc->rows > (UINT64_MAX - kTailPad) / 256) return CP_ERR_INVALID_ARGUMENT;
+
+    cp_table *t = (cp_table *)calloc(1, sizeof(cp_table));
+    if (!t) return CP_ERR_OUT_OF_MEMORY;
+    t->desc.struct_size = sizeof(cp_table_desc);
+    t->desc.d = desc->d;
+    t->desc.bits_per_step = 0;
+    t->desc.residency = desc->residency;
+    t->desc.rows = desc->rows;
+    t->desc.flags = desc->flags;
+    t->mixed = 1;
+    t->nclass = desc->nclass;
+    t->rates.kv_packed = 0;
+    for (uint32_t c = 0; c < 4; ++c) {
+        t->kv_of_class[c] = desc->bits_per_step[c];
+        t->rates.R[c] = R[c];
+        t->rates.kv_packed |= (desc->bits_per_step[c] & 0xFFu) << (8 * c);
+    }
+    const uint64_t nidx = cpk::mixed_index_entries(desc->rows);
+    t->index_host = (cpk::MixedEntry *)aligned_alloc(16, nidx * sizeof(cpk::MixedEntry));
+    if (!t->index_host) {
+        release(t);
+        return CP_ERR_OUT_OF_MEMORY;
+    }
+    if (cpk::mixed_index_build(row_class, desc->rows, desc->nclass, R, t->index_host, &t->records_bytes) != 0) {
+        release(t);
+        return CP_ERR_INVALID_ARGUMENT;  // a class >= nclass
+    }
+    cp_status st = allocate(t, lut_fp16);
+    if (st == CP_OK) {
+        hipError_t e = hipMalloc((void **)&t->index_dev, nidx * sizeof(cpk::MixedEntry));
+        if (e == hipSuccess)
+            e = hipMemcpy(t->index_dev, t->index_host, nidx * sizeof(cpk::MixedEntry), hipMemcpyHostToDevice);
+        if (e != hipSuccess) st = hip_fail(e);
+    }
+    if (st != CP_OK) {
+        release(t);
+        return st;
+    }
+    *out = t;
+    return CP_OK;
+}
+
+// Byte range of records [first_row, first_row + nrows) (nrows >= 1, in range).
+static void record_span(const cp_table *t, uint64_t first_row, uint64_t nrows, uint64_t *off, uint64_t *bytes)
+{
+    if (!t->mixed) {
+        *off = first_row * t->record_bytes;
+        *bytes = nrows * t->record_bytes;
+        return;
+    }
+    const uint64_t last = first_row + nrows - 1;
+    uint32_t cls = 0;
+    const uint64_t a = cpk::mixed_record_offset(t->index_host, t->rates.R, first_row, nullptr);
+    const uint64_t b = cpk::mixed_record_offset(t->index_host, t->rates.R, last, &cls);
+    *off = a;
+    *bytes = b + t->rates.R[cls] - a;
+}
+
+cp_status cp_table_record_range(const cp_table *t, uint64_t row, uint64_t *offset, uint64_t *bytes)
+{
+    if (!t || !offset || !bytes || row >= t->desc.rows) return CP_ERR_INVALID_ARGUMENT;
+    record_span(t, row, 1, offset, bytes);
     return CP_OK;
 }
 
@@ -131,7 +233,8 @@ cp_status cp_table_upload(cp_table *t, uint64_t first_row, uint64_t nrows, const
     if (nrows == 0) return CP_OK;
     if (!src || first_row > t->desc.rows || nrows > t->desc.rows - first_row)
         return CP_ERR_INVALID_ARGUMENT;
-    const uint64_t off = first_row * t->record_bytes, bytes = nrows * t->record_bytes;
+    uint64_t off, bytes;
+    record_span(t, first_row, nrows, &off, &bytes);
     if (t->desc.residency == CP_RESIDENCY_HOST_MAPPED) {
         memcpy(t->records + off, src, bytes);
         return CP_OK;
@@ -146,6 +249,21 @@ static cp_status lookup(const cp_table *t, const int64_t *ids, uint64_t n, uint1
     if (!t) return CP_ERR_INVALID_ARGUMENT;
     if (n == 0) return CP_OK;
     if (!ids || !out || ((uintptr_t)out & 15u) || ((uintptr_t)ids & 7u)) return CP_ERR_INVALID_ARGUMENT;
+    if (t->mixed) {
+        cpk::MixedLaunchArgs m;
+        m.records = t->records_dev;
+        m.rows = t->desc.rows;
+        m.lut = t->lut_dev;
+        m.ids = ids;
+        m.n = n;
+        m.out = reinterpret_cast<uint32_t *>(out);
+        m.err = t->err_dev;
+        m.index = t->index_dev;
+        m.rates = t->rates;
+        m.stream = (hipStream_t)stream;
+        hipError_t e = cpk::launch_mixed(t->desc.d, raw, m);
+        return e == hipSuccess ? CP_OK : hip_fail(e);
+    }
     cpk::LaunchArgs a;
     a.records = t->records_dev;
     a.rows = t->desc.rows;
@@ -174,7 +292,7 @@ cp_status cp_lookup_decode_raw(const cp_table *t, const int64_t *ids, uint64_t n
 
 uint64_t cp_dedup_workspace_bytes(const cp_table *t, uint64_t n)
 {
-    if (!t) return 0;
+    if (!t || t->mixed) return 0;
     return cpk::dedup_layout(n, t->record_bytes, kTailPad).total;
 }
 
@@ -185,6 +303,7 @@ cp_status cp_lookup_decode_dedup(const cp_table *t, const int64_t *ids, uint64_t
     if (n == 0) return CP_OK;
     if (!ids || !out || ((uintptr_t)out & 15u) || ((uintptr_t)ids & 7u)) return CP_ERR_INVALID_ARGUMENT;
     if (n > 0x7FFFFFFFull) return CP_ERR_INVALID_ARGUMENT;  // staging indices are 32-bit
+    if (t->mixed) return CP_ERR_UNSUPPORTED;
     const cpk::DedupLayout L = cpk::dedup_layout(n, t->record_bytes, kTailPad);
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total) return CP_ERR_INVALID_ARGUMENT;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -220,7 +339,8 @@ cp_status cp_table_download(const cp_table *t, uint64_t first_row, uint64_t nrow
     if (!t) return CP_ERR_INVALID_ARGUMENT;
     if (nrows == 0) return CP_OK;
     if (!dst || first_row > t->desc.rows || nrows > t->desc.rows - first_row) return CP_ERR_INVALID_ARGUMENT;
-    const uint64_t off = first_row * t->record_bytes, bytes = nrows * t->record_bytes;
+    uint64_t off, bytes;
+    record_span(t, first_row, nrows, &off, &bytes);
     hipError_t e = hipSetDevice(t->device);
     if (e == hipSuccess) e = hipDeviceSynchronize();  // encodes in flight on any stream land first
     if (e != hipSuccess) return hip_fail(e);
@@ -234,7 +354,7 @@ cp_status cp_table_download(const cp_table *t, uint64_t first_row, uint64_t nrow
 
 uint64_t cp_encode_workspace_bytes(const cp_table *t, uint64_t nrows)
 {
-    if (!t || nrows == 0) return 0;
+    if (!t || nrows == 0 || t->mixed) return 0;
     uint32_t blocks = 0;
     if (cpk::encode_grid(t->desc.bits_per_step, t->num_cus, nrows, &blocks) != hipSuccess) return 0;
     return (uint64_t)blocks * cpk::encode_workspace_per_block(t->desc.d, t->desc.bits_per_step);
@@ -247,7 +367,7 @@ cp_status cp_table_encode(cp_table *t, uint64_t first_row, uint64_t nrows, const
     if (nrows == 0) return CP_OK;
     if (!rows || ((uintptr_t)rows & 3u) || first_row > t->desc.rows || nrows > t->desc.rows - first_row)
         return CP_ERR_INVALID_ARGUMENT;
-    if (!cpk::encode_supported(t->desc.d, t->desc.bits_per_step)) return CP_ERR_UNSUPPORTED;
+    if (t->mixed || !cpk::encode_supported(t->desc.d, t->desc.bits_per_step)) return CP_ERR_UNSUPPORTED;
     uint32_t blocks = 0;
     hipError_t e = cpk::encode_grid(t->desc.bits_per_step, t->num_cus, nrows, &blocks);
     if (e != hipSuccess) return hip_fail(e);
@@ -283,6 +403,25 @@ cp_status cp_table_describe(const cp_table *t, cp_table_desc *desc_out)
 {
     if (!t || !desc_out) return CP_ERR_INVALID_ARGUMENT;
     *desc_out = t->desc;
+    return CP_OK;
+}
+
+cp_status cp_table_describe_mixed(const cp_table *t, cp_mixed_desc *desc_out)
+{
+    if (!t || !desc_out) return CP_ERR_INVALID_ARGUMENT;
+    memset(desc_out, 0, sizeof(*desc_out));
+    desc_out->struct_size = sizeof(cp_mixed_desc);
+    desc_out->d = t->desc.d;
+    desc_out->residency = t->desc.residency;
+    desc_out->rows = t->desc.rows;
+    desc_out->flags = t->desc.flags;
+    if (t->mixed) {
+        desc_out->nclass = t->nclass;
+        for (uint32_t c = 0; c < 4; ++c) desc_out->bits_per_step[c] = t->kv_of_class[c];
+    } else {
+        desc_out->nclass = 1;
+        desc_out->bits_per_step[0] = t->desc.bits_per_step;
+    }
     return CP_OK;
 }
 

@@ -66,6 +66,40 @@ hipError_t encode_grid(uint32_t kv, int num_cus, uint64_t nrows, uint32_t *block
 uint64_t encode_workspace_per_block(uint32_t d, uint32_t kv);
 hipError_t encode(const EncodeArgs &a);
 
+// Mixed-rate tables (see cp_mixed.hip): one index entry per 32 rows.
+struct alignas(16) MixedEntry {
+    uint64_t base;  // byte offset of the block's first record
+    uint32_t p0;    // bit j: bit 0 of row (32b + j)'s rate class
+    uint32_t p1;    // bit j: bit 1 of that class
+};
+
+struct MixedRates {
+    uint32_t kv_packed;  // kv of class c in bits [8c, 8c + 8)
+    uint32_t R[4];       // record bytes of class c (0 for unused classes)
+};
+
+struct MixedLaunchArgs {
+    const uint8_t *records;  // device-accessible packed records
+    uint64_t rows;
+    const uint32_t *lut;
+    const int64_t *ids;
+    uint64_t n;
+    uint32_t *out;
+    int *err;
+    const MixedEntry *index;  // device
+    MixedRates rates;
+    hipStream_t stream;
+};
+
+bool mixed_supported(uint32_t d);
+hipError_t launch_mixed(uint32_t d, bool raw, const MixedLaunchArgs &a);
+uint64_t mixed_index_entries(uint64_t rows);
+// Builds the index on the host; -1 when a class is >= nclass.
+int mixed_index_build(const uint8_t *row_class, uint64_t rows, uint32_t nclass, const uint32_t R[4],
+                      MixedEntry *index, uint64_t *total_bytes);
+// Byte offset (and class) of a row's record, from a host copy of the index.
+uint64_t mixed_record_offset(const MixedEntry *index, const uint32_t R[4], uint64_t row, uint32_t *cls);
+
 // True when a kernel for (d, kv) is compiled in.
 bool supported(uint32_t d, uint32_t kv);
 

@@ -1,0 +1,223 @@
+// cp_lane.h - per-lane decode helpers shared by the gather-decode kernels
+// (cp_decode.hip: one rate per table; cp_mixed.hip: a rate per row).
+// Device code for gfx950 only; included by .hip sources.
+#pragma once
+
+#include <type_traits>
+
+#include "cp_internal.h"
+
+// Launch-shape knobs (overridable at build time for tuning).
+#ifndef CPK_COPIES
+#define CPK_COPIES 16
+#endif
+#ifndef CPK_BLOCK
+#define CPK_BLOCK 1024
+#endif
+#ifndef CPK_NT_STORE
+#define CPK_NT_STORE 1
+#endif
+#ifndef CPK_FMA_MIX
+#define CPK_FMA_MIX 1
+#endif
+#ifndef CPK_BLOCKS_PER_CU
+#define CPK_BLOCKS_PER_CU 0
+#endif
+#ifndef CPK_CHUNK
+#define CPK_CHUNK 16
+#endif
+
+
+namespace cpk {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 64-bit value of lane `lane` (wave-uniform result). The builtin works on
+// int; both halves go through uint32_t so the low half is not sign-extended.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, uint32_t lane)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, (int)lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), (int)lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t ld32(const uint8_t *p)
+{
+    return *reinterpret_cast<const uint32_t *>(p);
+}
+
+// alpha * (fp16 half of e) in one v_fma_mix_f32: the half is widened exactly,
+// the product of a bf16 and an fp16 is exact in fp32, and adding -0 leaves
+// every product (signed zeros included) unchanged.
+__device__ __forceinline__ float mix_lo(uint32_t e, float a, float negz)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(e), "v"(a), "v"(negz));
+    return r;
+}
+
+__device__ __forceinline__ float mix_hi(uint32_t e, float a, float negz)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(e), "v"(a), "v"(negz));
+    return r;
+}
+
+// The same with the scale in an SGPR (uniform per row when a row fills the
+// wave), which saves moving it into a VGPR for every row.
+__device__ __forceinline__ float mix_lo_s(uint32_t e, float a, float negz)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(e), "s"(a), "v"(negz));
+    return r;
+}
+
+__device__ __forceinline__ float mix_hi_s(uint32_t e, float a, float negz)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(e), "s"(a), "v"(negz));
+    return r;
+}
+
+// One output pair: e = LUT entry (fp16 lo = element 2t, hi = element 2t+1),
+// negmask = 0x80008000 when the window's bit 15 is set. Scaled: bf16 pair of
+// alpha * value, rounded to nearest even; that rounding is symmetric in sign,
+// so the sign flip can be applied to the packed result.
+template <bool RAW, bool SALPHA = false>
+__device__ __forceinline__ uint32_t emit_pair(uint32_t e, uint32_t negmask, float alpha)
+{
+    if constexpr (RAW) {
+        return e ^ negmask;
+    } else {
+        f32x2 v;
+#if CPK_FMA_MIX
+        const float negz = __builtin_bit_cast(float, 0x80000000u);
+        if constexpr (SALPHA) {
+            v.x = mix_lo_s(e, alpha, negz);
+            v.y = mix_hi_s(e, alpha, negz);
+        } else {
+            v.x = mix_lo(e, alpha, negz);
+            v.y = mix_hi(e, alpha, negz);
+        }
+#else
+        v.x = alpha * (float)__builtin_bit_cast(_Float16, (uint16_t)(e & 0xFFFFu));
+        v.y = alpha * (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
+#endif
+        bf16x2 b = __builtin_convertvector(v, bf16x2);
+        return __builtin_bit_cast(uint32_t, b) ^ negmask;
+    }
+}
+
+// h = x*x + x (mod 2^32) on the low 24 bits of x. Bits 7..15 of h, the only
+// bits the output rule reads, depend on bits 0..15 of x alone (the higher
+// bits only add multiples of 2^16), so x may carry the following code bits.
+__device__ __forceinline__ uint32_t hash_mad(uint32_t x)
+{
+    uint32_t h;
+    asm("v_mad_u32_u24 %0, %1, %1, %1" : "=v"(h) : "v"(x));
+    return h;
+}
+
+// (a & mask) | b in one v_and_or_b32 (kept as written: the compiler otherwise
+// reassociates the LDS address into more instructions).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(b));
+    return r;
+}
+
+// Code bits a lane needs for its 4 windows: 16 + 3kv; they fit in 32 bits up
+// to kv = 5.
+template <int KV>
+using field_t = typename std::conditional<(16 + 3 * KV <= 32), uint32_t, uint64_t>::type;
+
+// Decodes one row's 8 outputs of this lane from `newbits` (the lane's 4kv
+// new code bits) and the row's scale, and returns them packed (4 dwords).
+template <int D, int KV, bool RAW, int COPIES, bool SALPHA>
+__device__ __forceinline__ u32x4 decode_lane(uint32_t newbits, uint32_t alpha_bits, uint32_t l, uint32_t g,
+                                             const uint32_t *s_lut, uint32_t lds_off)
+{
+    constexpr int LANES = D / 8;
+    constexpr int M = 16 - KV;
+    constexpr int NEWB = 4 * KV;
+    using F = field_t<KV>;
+    // older bits from the previous lane(s) of the same row; lane 0 takes them
+    // from the last lane: the circular (tail-biting) wrap
+    uint32_t prev;
+    if constexpr (LANES == 64)
+        prev = __builtin_amdgcn_update_dpp(newbits, newbits, 0x13C /* wave_ror:1 */, 0xF, 0xF, false);
+    else
+        prev = __shfl(newbits, (int)(g * LANES + (l + LANES - 1) % LANES), 64);
+    F hist;
+    if constexpr (NEWB < M) {
+        // kv = 3: 13 history bits span the two previous lanes
+        const uint32_t prev2 = __shfl(newbits, (int)(g * LANES + (l + LANES - 2) % LANES), 64);
+        hist = (F)((((uint64_t)prev << NEWB) | prev2) >> (2 * NEWB - M));
+    } else {
+        hist = (F)(prev >> (NEWB - M));
+    }
+    const F field = ((F)newbits << M) | hist;  // bit 0 = code bit NEWB*l - M
+    const float alpha = __builtin_bit_cast(float, alpha_bits);
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t x = (uint32_t)(field >> (KV * k));  // low 16 bits: window s_t
+        const uint32_t h = hash_mad(x);
+        // LDS block of entry idx = (h >> 7) & 511 starts at byte idx * 128,
+        // i.e. h & 0xFF80; bit 15 of the window (the sign) picks the negated
+        // half (+64 bytes); the lane picks one of the 16 copies
+        const uint32_t e = *reinterpret_cast<const uint32_t *>(
+            reinterpret_cast<const char *>(s_lut) + and_or(h, 0xFF80u, and_or(x >> 9, 0x40u, lds_off)));
+        v[k] = emit_pair<RAW, SALPHA>(e, 0u, alpha);
+    }
+    return v;
+}
+
+// Codebook in LDS: per entry a 128-byte block of 16 copies of the fp16 pair
+// followed by 16 copies of its negation (both sign bits flipped), 64 KB.
+constexpr int kLdsLutWords = 512 * 32;
+
+template <int BLOCK>
+__device__ __forceinline__ void stage_lut(uint32_t *s_lut, const uint32_t *__restrict__ lut)
+{
+    for (int u = threadIdx.x; u < 4096; u += BLOCK) {
+        // 16-byte unit u holds 4 copies of entry u >> 3, negated when bit 2 of
+        // u is set; consecutive lanes write consecutive units (no bank conflicts)
+        const uint32_t v = lut[u >> 3] ^ ((u & 4) ? 0x80008000u : 0u);
+        reinterpret_cast<u32x4 *>(s_lut)[u] = (u32x4){v, v, v, v};
+    }
+    __syncthreads();
+}
+
+// The 4kv new code bits of lane l of the record at byte offset o, for any kv
+// (two aligned dword loads; records are 2-byte aligned).
+__device__ __forceinline__ uint32_t lane_bits(const uint8_t *__restrict__ tab, uint64_t o, uint32_t newb,
+                                              uint32_t l)
+{
+    const uint64_t bit = o * 8 + (uint64_t)newb * l;
+    const uint8_t *p = tab + ((bit >> 5) << 2);
+    const uint64_t both = ((uint64_t)ld32(p + 4) << 32) | ld32(p);
+    return (uint32_t)(both >> (bit & 31)) & ((1u << newb) - 1u);
+}
+
+// The scale of the record at byte offset o with nb code bytes, as fp32 bits.
+__device__ __forceinline__ uint32_t scale_bits(const uint8_t *__restrict__ tab, uint64_t o, uint32_t nb)
+{
+    const uint64_t ao = o + nb;  // bf16 at bytes [nb, nb + 2)
+    const uint32_t adw = ld32(tab + (ao & ~(uint64_t)3));
+    return ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16;
+}
+
+__device__ __forceinline__ void store16(uint32_t *dst, u32x4 v)
+{
+#if CPK_NT_STORE
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
+#else
+    *reinterpret_cast<u32x4 *>(dst) = v;
+#endif
+}
+
+}  // namespace cpk

@@ -1,0 +1,237 @@
+// cp_mixed.hip - gather-and-decode for mixed-rate CP tables: every row has a
+// rate class, class c coded at kv_c bits per step.
+//
+// The pages study allocating bits by how often a row is looked up, over the
+// code rates they evaluate (1.5 / 2 / 2.5 / 3 bits per element), and find
+// that the access counts behind it may not carry over between text domains
+// ("2비트 코드와 공유 트렐리스로 n-gram 룩업 테이블을 4~8배 압축한다",
+// onedev.kr, sections "How it is used" and "Assumptions and limits"). They
+// give no format; this library stores the records of all rows packed in row
+// order, each at its own class's rate, so a row's record starts at the sum of
+// the record sizes before it. To find it in O(1) the library keeps an index
+// of one 16-byte entry per 32 rows:
+//   base - byte offset of the block's first record;
+//   p0   - bit j = bit 0 of the class of row 32b + j;
+//   p1   - bit j = bit 1 of that class;
+// so row 32b + j starts at base + sum over c of n_c * R_c, n_c being the
+// number of rows of class c among the block's first j rows (popcounts of the
+// two bit planes under a mask), and has class bit j of (p0, p1).
+//
+// The kernel is the single-rate gather-decode with the record located through
+// the index and the trellis walk chosen per row: at d = 512 a row fills the
+// wave, so the rate is uniform per row and selects one of four decoders with
+// a scalar branch; at smaller d the rows decoded side by side may differ in
+// rate, and each rate present among them runs over the whole wave with its
+// result kept where it applies (the control flow stays uniform, which the
+// lane shuffles of the walk require).
+#include "cp_lane.h"
+
+namespace cpk {
+
+namespace {
+
+template <int D, int KV, bool RAW, bool SALPHA>
+__device__ __forceinline__ u32x4 decode_rate(uint32_t nb, uint32_t ab, uint32_t l, uint32_t g,
+                                             const uint32_t *s_lut, uint32_t lds_off)
+{
+    return decode_lane<D, KV, RAW, CPK_COPIES, SALPHA>(nb, ab, l, g, s_lut, lds_off);
+}
+
+// One row's lane outputs when the whole wave decodes that row (kv uniform).
+template <int D, bool RAW>
+__device__ __forceinline__ u32x4 decode_uniform(uint32_t kv, uint32_t nb, uint32_t ab, uint32_t l, uint32_t g,
+                                                const uint32_t *s_lut, uint32_t lds_off)
+{
+    switch (kv) {
+    case 3: return decode_rate<D, 3, RAW, true>(nb, ab, l, g, s_lut, lds_off);
+    case 4: return decode_rate<D, 4, RAW, true>(nb, ab, l, g, s_lut, lds_off);
+    case 5: return decode_rate<D, 5, RAW, true>(nb, ab, l, g, s_lut, lds_off);
+    default: return decode_rate<D, 6, RAW, true>(nb, ab, l, g, s_lut, lds_off);
+    }
+}
+
+// Each rate present among the rows decoded side by side runs over the whole
+// wave; a lane keeps the result of its own row's rate.
+template <int D, int KV, bool RAW>
+__device__ __forceinline__ void decode_if_present(u32x4 &v, uint32_t kv, uint32_t nb, uint32_t ab, uint32_t l,
+                                                  uint32_t g, const uint32_t *s_lut, uint32_t lds_off)
+{
+    if (__ballot(kv == (uint32_t)KV)) {
+        const u32x4 t = decode_rate<D, KV, RAW, false>(nb, ab, l, g, s_lut, lds_off);
+        if (kv == (uint32_t)KV) v = t;
+    }
+}
+
+template <int D, bool RAW, int BLOCK, int CHUNK>
+__global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__restrict__ tab, const uint64_t rows,
+                                                             const uint32_t *__restrict__ lut,
+                                                             const int64_t *__restrict__ ids, const uint64_t n,
+                                                             uint32_t *__restrict__ out, int *__restrict__ err,
+                                                             const MixedEntry *__restrict__ index,
+                                                             const MixedRates rates)
+{
+    constexpr int LANES = D / 8;
+    constexpr int GROUPS = 64 / LANES;
+    constexpr int WAVES = BLOCK / 64;
+    constexpr int CI = CHUNK / GROUPS;
+    static_assert(CHUNK <= 64 && CI >= 1 && CI * GROUPS == CHUNK, "one id per lane per chunk");
+
+    __shared__ __attribute__((aligned(16))) uint32_t s_lut[kLdsLutWords];
+    stage_lut<BLOCK>(s_lut, lut);
+
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t l = lane % LANES;
+    const uint32_t g = lane / LANES;
+    const uint32_t lds_off = (lane & 15u) * 4u;
+    const uint64_t wave =
+        (uint64_t)blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t waves = (uint64_t)gridDim.x * WAVES;
+    const uint64_t nchunks = (n + CHUNK - 1) / CHUNK;
+    bool bad = false;
+
+    auto row_of = [&](uint64_t c, uint32_t i) -> uint64_t { return c * CHUNK + i; };
+    auto load_id = [&](uint64_t c) -> int64_t {
+        const uint64_t j = row_of(c, lane);
+        return (c < nchunks && lane < CHUNK && j < n) ? ids[j] : 0;
+    };
+    int64_t my_id = load_id(wave);
+    for (uint64_t c = wave; c < nchunks; c += waves) {
+        uint32_t cn = __builtin_amdgcn_readfirstlane((uint32_t)((n - c * CHUNK) < CHUNK ? (n - c * CHUNK) : CHUNK));
+        asm volatile("" : "+s"(cn));
+        const bool in = lane < cn;
+        const bool ok = in && (uint64_t)my_id < rows;
+        bad |= in && !ok;
+        // lane k locates chunk row k's record (an invalid id reads row 0's,
+        // whose rate and extent are consistent with each other)
+        const uint64_t rid = ok ? (uint64_t)my_id : 0;
+        const MixedEntry e = index[rid >> 5];
+        const uint32_t j = (uint32_t)rid & 31u, below = (1u << j) - 1u;
+        const uint32_t n1 = __builtin_popcount(e.p0 & ~e.p1 & below);
+        const uint32_t n2 = __builtin_popcount(~e.p0 & e.p1 & below);
+        const uint32_t n3 = __builtin_popcount(e.p0 & e.p1 & below);
+        const uint32_t n0 = j - n1 - n2 - n3;
+        const uint64_t my_off = e.base + (uint64_t)n0 * rates.R[0] + (uint64_t)n1 * rates.R[1] +
+                                (uint64_t)n2 * rates.R[2] + (uint64_t)n3 * rates.R[3];
+        const uint32_t cls = ((e.p0 >> j) & 1u) | (((e.p1 >> j) & 1u) << 1);
+        const uint32_t my_kv = (rates.kv_packed >> (8u * cls)) & 0xFFu;
+        const uint64_t okmask = __ballot(ok);
+        my_id = load_id(c + waves);
+
+        if constexpr (GROUPS == 1) {
+            uint32_t nb[CI], ab[CI], kv[CI];
+#pragma unroll
+            for (int i = 0; i < CI; ++i) {
+                const uint64_t o = readlane_u64(my_off, (uint32_t)i);
+                kv[i] = (uint32_t)__builtin_amdgcn_readlane((int)my_kv, i);
+                nb[i] = lane_bits(tab, o, 4u * kv[i], l);
+                ab[i] = scale_bits(tab, o, kv[i] * (uint32_t)(D / 16));
+            }
+#pragma unroll
+            for (int i = 0; i < CI; ++i) {
+                const u32x4 v = decode_uniform<D, RAW>(kv[i], nb[i], ab[i], l, g, s_lut, lds_off);
+                if ((uint32_t)i < cn) store16(out + row_of(c, i) * (D / 2) + 4u * l, v);
+            }
+        } else {
+            uint32_t nb[CI], ab[CI], kv[CI];
+#pragma unroll
+            for (int i = 0; i < CI; ++i) {
+                const int r = (int)(g * CI + i);
+                const uint64_t o = __shfl(my_off, r, 64);
+                kv[i] = (uint32_t)__shfl((int)my_kv, r, 64);
+                nb[i] = lane_bits(tab, o, 4u * kv[i], l);
+                ab[i] = scale_bits(tab, o, kv[i] * (uint32_t)(D / 16));
+            }
+#pragma unroll
+            for (int i = 0; i < CI; ++i) {
+                const uint32_t r = g * CI + i;
+                u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+                decode_if_present<D, 3, RAW>(v, kv[i], nb[i], ab[i], l, g, s_lut, lds_off);
+                decode_if_present<D, 4, RAW>(v, kv[i], nb[i], ab[i], l, g, s_lut, lds_off);
+                decode_if_present<D, 5, RAW>(v, kv[i], nb[i], ab[i], l, g, s_lut, lds_off);
+                decode_if_present<D, 6, RAW>(v, kv[i], nb[i], ab[i], l, g, s_lut, lds_off);
+                if (r < cn) store16(out + row_of(c, r) * (D / 2) + 4u * l, v);
+            }
+        }
+        const uint64_t badmask = __ballot(in) & ~okmask;
+        if (badmask) {
+            __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+            for (int i = 0; i < CI; ++i) {
+                const uint32_t r = g * CI + i;
+                if ((badmask >> r) & 1u)
+                    store16(out + row_of(c, r) * (D / 2) + 4u * l, (u32x4){0u, 0u, 0u, 0u});
+            }
+        }
+    }
+    if (bad) atomicOr(err, 1);
+}
+
+template <int D, bool RAW>
+hipError_t launch_mixed_one(const MixedLaunchArgs &a)
+{
+    constexpr int BLOCK = CPK_BLOCK;
+    constexpr int GROUPS = 64 / (D / 8);
+    constexpr int CHUNK = (CPK_CHUNK / GROUPS > 0 ? CPK_CHUNK / GROUPS : 1) * GROUPS;
+    const uint64_t nchunks = (a.n + CHUNK - 1) / CHUNK;
+    const uint64_t blocks = (nchunks + BLOCK / 64 - 1) / (BLOCK / 64);
+    hipLaunchKernelGGL((gather_decode_mixed<D, RAW, BLOCK, CHUNK>), dim3((unsigned)blocks), dim3(BLOCK), 0,
+                       a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err, a.index, a.rates);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool mixed_supported(uint32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+hipError_t launch_mixed(uint32_t d, bool raw, const MixedLaunchArgs &a)
+{
+    if (a.n == 0) return hipSuccess;
+    switch (d) {
+    case 64: return raw ? launch_mixed_one<64, true>(a) : launch_mixed_one<64, false>(a);
+    case 128: return raw ? launch_mixed_one<128, true>(a) : launch_mixed_one<128, false>(a);
+    case 256: return raw ? launch_mixed_one<256, true>(a) : launch_mixed_one<256, false>(a);
+    case 512: return raw ? launch_mixed_one<512, true>(a) : launch_mixed_one<512, false>(a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+uint64_t mixed_index_entries(uint64_t rows) { return (rows + 31) / 32; }
+
+int mixed_index_build(const uint8_t *row_class, uint64_t rows, uint32_t nclass, const uint32_t R[4],
+                      MixedEntry *index, uint64_t *total_bytes)
+{
+    uint64_t acc = 0;
+    const uint64_t nblk = mixed_index_entries(rows);
+    for (uint64_t b = 0; b < nblk; ++b) {
+        MixedEntry e;
+        e.base = acc;
+        e.p0 = 0;
+        e.p1 = 0;
+        const uint64_t r0 = b * 32;
+        const uint32_t cnt = (uint32_t)(rows - r0 < 32 ? rows - r0 : 32);
+        for (uint32_t j = 0; j < cnt; ++j) {
+            const uint32_t c = row_class[r0 + j];
+            if (c >= nclass) return -1;
+            e.p0 |= (c & 1u) << j;
+            e.p1 |= ((c >> 1) & 1u) << j;
+            acc += R[c];
+        }
+        index[b] = e;
+    }
+    *total_bytes = acc;
+    return 0;
+}
+
+uint64_t mixed_record_offset(const MixedEntry *index, const uint32_t R[4], uint64_t row, uint32_t *cls)
+{
+    const MixedEntry &e = index[row >> 5];
+    const uint32_t j = (uint32_t)row & 31u, below = (1u << j) - 1u;
+    const uint32_t n1 = __builtin_popcount(e.p0 & ~e.p1 & below);
+    const uint32_t n2 = __builtin_popcount(~e.p0 & e.p1 & below);
+    const uint32_t n3 = __builtin_popcount(e.p0 & e.p1 & below);
+    const uint32_t n0 = j - n1 - n2 - n3;
+    if (cls) *cls = ((e.p0 >> j) & 1u) | (((e.p1 >> j) & 1u) << 1);
+    return e.base + (uint64_t)n0 * R[0] + (uint64_t)n1 * R[1] + (uint64_t)n2 * R[2] + (uint64_t)n3 * R[3];
+}
+
+}  // namespace cpk

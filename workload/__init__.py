@@ -157,6 +157,72 @@ def uniform_ids(rows: int, n: int, seed: int) -> np.ndarray:
     return rng.integers(0, rows, size=n, dtype=np.int64)
 
 
+# Mixed-rate tables: rate classes by access rank (class 0 = most looked-up
+# rows). With these shares the mean rate is 3.75 bits per step (1.875 bits
+# per element), inside the 2-bit budget of the single-rate table.
+MIXED_KV = (6, 5, 4, 3)
+MIXED_SHARES = (0.05, 0.15, 0.30, 0.50)
+
+
+def rank_classes(rows: int, seed: int, shares=MIXED_SHARES, threads: int | None = None) -> np.ndarray:
+    """uint8[rows]: each row's rate class from its access rank under the Zipf
+    id stream of `seed` (zipf_ids sends rank r to row keyed_permutation(r)):
+    the first shares[0] of the ranks get class 0, the next shares[1] class 1,
+    and so on. A stand-in for access counts taken from a text corpus."""
+    bounds = np.floor(np.cumsum(np.asarray(shares, dtype=np.float64)) * rows).astype(np.int64)
+    bounds[-1] = rows
+    cls = np.empty(rows, dtype=np.uint8)
+    step = 1 << 22
+
+    def fill(a: int) -> None:
+        r = np.arange(a, min(a + step, rows), dtype=np.int64)
+        cls[keyed_permutation(r, rows, seed)] = np.searchsorted(bounds, r, side="right").astype(np.uint8)
+
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, range(0, rows, step)))
+    return cls
+
+
+def mixed_layout(d: int, kv_of_class, row_class: np.ndarray) -> np.ndarray:
+    """uint64[rows + 1]: byte offset of each row's record when the records
+    are packed in row order at their classes' sizes (last entry: total)."""
+    sizes = np.array([record_bytes(d, k) for k in kv_of_class], dtype=np.uint64)
+    off = np.zeros(row_class.shape[0] + 1, dtype=np.uint64)
+    np.cumsum(sizes[row_class], out=off[1:])
+    return off
+
+
+def random_mixed_records(d: int, kv_of_class, row_class: np.ndarray, seed: int,
+                         offsets: np.ndarray | None = None, threads: int | None = None) -> np.ndarray:
+    """uint8[total]: the packed records of a random-code mixed-rate table.
+    Every row gets uniform code bytes and a LogNormal(0, 0.5) bf16 scale;
+    chunk c (CHUNK_ROWS rows) draws from its own stream."""
+    if offsets is None:
+        offsets = mixed_layout(d, kv_of_class, row_class)
+    rows = row_class.shape[0]
+    nb = np.array([k * d // 16 for k in kv_of_class], dtype=np.int64)
+    out = np.empty(int(offsets[-1]), dtype=np.uint8)
+
+    def fill(c: int) -> None:
+        r0, r1 = c * CHUNK_ROWS, min(rows, (c + 1) * CHUNK_ROWS)
+        a, b = int(offsets[r0]), int(offsets[r1])
+        rng = np.random.default_rng([seed, 0x3A7E, c])
+        words = rng.integers(0, 2**64 - 1, size=(b - a + 7) // 8, dtype=np.uint64, endpoint=True)
+        out[a:b] = words.view(np.uint8)[: b - a]
+        alpha = _bf16_bits(rng.lognormal(0.0, 0.5, size=r1 - r0))
+        pos = offsets[r0:r1].astype(np.int64) + nb[row_class[r0:r1]]
+        out[pos] = (alpha & 0xFF).astype(np.uint8)
+        out[pos + 1] = (alpha >> 8).astype(np.uint8)
+
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, range((rows + CHUNK_ROWS - 1) // CHUNK_ROWS)))
+    return out
+
+
 def ids_digest(ids: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(ids, dtype=np.int64).tobytes()).hexdigest()[:16]
 
@@ -213,6 +279,11 @@ CONFIGS = {
         host_resident=True,
         description="the 12.70 GB d512 table in pinned host memory, read over PCIe"),
 }
+CONFIGS["mixed_d512"] = TableConfig(
+    "mixed_d512", 97_690_000, 512, 0, 104, "zipf", REPLAY_IDS, 202, encoded_rows=0,
+    description="97,690,000 x d512 mixed-rate table: rows coded at 3 / 2.5 / 2 / 1.5 bits per element "
+                "by Zipf access rank (5% / 15% / 30% / 50% of rows), ~11.5 GB in HBM; the Zipf(1.1) replay",
+    extra={"kv_of_class": MIXED_KV, "shares": MIXED_SHARES})
 for _kv in (3, 4, 5, 6):
     CONFIGS[f"rate_d512_kv{_kv}"] = TableConfig(
         f"rate_d512_kv{_kv}", 1 << 22, 512, _kv, 103, "zipf", REPLAY_IDS, 203,
