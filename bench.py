@@ -29,18 +29,26 @@ if ROOT not in sys.path:
 
 METRIC = "decoded rows/s + effective GB/s (% of HBM peak), 393,216-lookup replay"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "trellis_coded_row_amd", "csrc", "cp_decode.hip")
+CSRC = os.path.join(ROOT, "trellis_coded_row_amd", "csrc")
+# the sources of each lookup kernel (a counter summary is valid for these bytes)
+KERNEL_SOURCES = {
+    "single": ("cp_decode.hip", "cp_lane.h"),
+    "mixed": ("cp_mixed.hip", "cp_lane.h"),
+}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def kernel_source_hash(kind: str = "single") -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-def read_counter_summary(config: str, ids_kind: str) -> dict | None:
+def read_counter_summary(config: str, ids_kind: str, kind: str = "single") -> dict | None:
     """HBM traffic per launch from a committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel source."""
+    was taken on the current kernel sources."""
     path = os.path.join(PROFILES, f"counters_gather_decode_{config}_{ids_kind}.txt")
     if not os.path.exists(path):
         return None
@@ -51,7 +59,7 @@ def read_counter_summary(config: str, ids_kind: str) -> dict | None:
             if line and not line.startswith("#") and ":" in line:
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256") != kernel_source_hash():
+    if vals.get("kernel_source_sha256") != kernel_source_hash(kind):
         return None
     try:
         fetch = float(vals["FETCH_SIZE_KiB_per_dispatch"]) * 1024 * float(vals["fetch_scale"])
@@ -218,7 +226,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="gpu_d512",
-                    help="workload: gpu_d512 (default), host_d512, small_d256, rate_d512_kv{3,4,5,6}, tiny_d64")
+                    help="workload: gpu_d512 (default), host_d512, mixed_d512, small_d256, rate_d512_kv{3,4,5,6}, "
+                         "tiny_d64")
     ap.add_argument("--ids", default=None, choices=["zipf", "uniform", "slice96"],
                     help="id stream (default: the config's own)")
     ap.add_argument("--noncoherent", action="store_true", help="host_d512: non-coherent pinned memory")
@@ -259,10 +268,18 @@ def main() -> int:
     ids_kind = args.ids or cfg.ids_kind
     lut = workload.lut_fp16(0)
 
+    mixed = cfg.kv == 0
     t_gen = time.time()
     # every row a random code: the decode cost does not depend on how codes
     # were chosen (any bit string is a valid tail-biting code)
-    records = workload.random_records(cfg.rows, cfg.d, cfg.kv, cfg.table_seed)
+    if mixed:
+        kvs = cfg.extra["kv_of_class"]
+        classes = workload.rank_classes(cfg.rows, cfg.ids_seed, cfg.extra["shares"])
+        offsets = workload.mixed_layout(cfg.d, kvs, classes)
+        records = workload.random_mixed_records(cfg.d, kvs, classes, cfg.table_seed, offsets)
+        class_bytes = np.array([workload.record_bytes(cfg.d, k) for k in kvs], dtype=np.int64)
+    else:
+        records = workload.random_records(cfg.rows, cfg.d, cfg.kv, cfg.table_seed)
     if ids_kind == "zipf":
         ids_np = workload.zipf_ids(cfg.rows, cfg.n_ids, cfg.ids_seed)
     elif ids_kind == "uniform":
@@ -274,10 +291,16 @@ def main() -> int:
     residency = cp.CP_RESIDENCY_HOST_MAPPED if cfg.host_resident else cp.CP_RESIDENCY_DEVICE
     flags = cp.CP_FLAG_HOST_NONCOHERENT if args.noncoherent else 0
     t_up = time.time()
-    table = cp.Table(cfg.rows, cfg.d, cfg.kv, lut, residency=residency, flags=flags)
     chunk = 1 << 22
-    for r0 in range(0, cfg.rows, chunk):
-        table.upload(records[r0:r0 + chunk], first_row=r0)
+    if mixed:
+        table = cp.MixedTable(cfg.d, kvs, classes, lut, residency=residency, flags=flags)
+        for r0 in range(0, cfg.rows, chunk):
+            r1 = min(cfg.rows, r0 + chunk)
+            table.upload_bytes(records[int(offsets[r0]):int(offsets[r1])], r0, r1 - r0)
+    else:
+        table = cp.Table(cfg.rows, cfg.d, cfg.kv, lut, residency=residency, flags=flags)
+        for r0 in range(0, cfg.rows, chunk):
+            table.upload(records[r0:r0 + chunk], first_row=r0)
     upload_s = time.time() - t_up
 
     n = ids_np.shape[0]
@@ -305,8 +328,17 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
     launch_ms = ms_per_step  # one kernel launch per step
 
-    R = cfg.R
-    algo_bytes = n * (R + 2 * cfg.d)
+    if mixed:
+        # each lookup reads its row's own record and the 16-byte index entry
+        # of its block of 32 rows
+        rec_bytes = int(class_bytes[classes[ids_np]].sum())
+        algo_bytes = rec_bytes + n * (16 + 2 * cfg.d)
+        R = rec_bytes / n
+        table_bytes = int(offsets[-1])
+    else:
+        R = cfg.R
+        algo_bytes = n * (R + 2 * cfg.d)
+        table_bytes = cfg.table_bytes
     rows_per_s = n * args.steps / (total_ms / 1e3)
     achieved = algo_bytes / (launch_ms / 1e3) / 1e9
     res = {
@@ -323,16 +355,19 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: {n:,} lookups ({ids_kind} ids) into a {cfg.rows:,} x d{cfg.d} CP table, "
-                        f"{cfg.kv / 2:g} bits/element + bf16 scale ({R}-byte records, "
-                        f"{cfg.table_bytes / 1e9:.2f} GB, {'pinned host memory' if cfg.host_resident else 'HBM'})",
-            "rows": cfg.rows, "d": cfg.d, "bits_per_step": cfg.kv, "record_bytes": R, "lookups": n,
+            "workload": (f"{cfg.name}: {n:,} lookups ({ids_kind} ids) into a {cfg.rows:,} x d{cfg.d} CP table, "
+                         + (f"rates {'/'.join(f'{k / 2:g}' for k in kvs)} bits/element by access rank "
+                            f"({R:.1f} record bytes per lookup on average" if mixed else
+                            f"{cfg.kv / 2:g} bits/element + bf16 scale ({R}-byte records")
+                         + f", {table_bytes / 1e9:.2f} GB, {'pinned host memory' if cfg.host_resident else 'HBM'})"),
+            "rows": cfg.rows, "d": cfg.d, "bits_per_step": list(kvs) if mixed else cfg.kv, "record_bytes": R,
+            "lookups": n,
             "ids": ids_kind, "ids_sha256_16": workload.ids_digest(ids_np),
             "residency": "host" + ("-noncoherent" if args.noncoherent else "") if cfg.host_resident else "hbm",
             "entry_point": "cp_lookup_decode_dedup" if args.dedup else "cp_lookup_decode",
         },
-        "effective_GBps": n * (R + 2 * cfg.d) * args.steps / (total_ms / 1e3) / 1e9,
-        "pct_hbm_peak": 100.0 * n * (R + 2 * cfg.d) * args.steps / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+        "effective_GBps": algo_bytes * args.steps / (total_ms / 1e3) / 1e9,
+        "pct_hbm_peak": 100.0 * algo_bytes * args.steps / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
         "launch_ms_mean": launch_ms,
         "wall_s_timed_region": wall_s,
         "setup_s": {"generate": round(gen_s, 2), "upload": round(upload_s, 2)},
@@ -340,11 +375,11 @@ def main() -> int:
     if cfg.host_resident:
         # the records cross PCIe: report that rate against a measured
         # pinned host-to-device copy (the HBM roofline does not bound it)
-        res["pcie_record_GBps"] = n * R / (launch_ms / 1e3) / 1e9
+        res["pcie_record_GBps"] = n * R / (launch_ms / 1e3) / 1e9  # R: mean record bytes per lookup
         probe = pcie_probe(torch)
         res["pcie_probe"] = probe
         res["pcie_frac"] = res["pcie_record_GBps"] / probe["h2d_GBps"]
-    counters = read_counter_summary(cfg.name, ids_kind)
+    counters = read_counter_summary(cfg.name, ids_kind, "mixed" if mixed else "single")
     res["roofline"] = {
         "bound": "hbm",
         "achieved": achieved,
@@ -353,7 +388,7 @@ def main() -> int:
         "frac": achieved / HBM_PEAK_GBPS,
         "traffic": counters["bytes"] if counters else None,
         "algorithmic_bytes_per_launch": algo_bytes,
-        "kernel": f"gather_decode<{cfg.d},{cfg.kv}>",
+        "kernel": f"gather_decode_mixed<{cfg.d}>" if mixed else f"gather_decode<{cfg.d},{cfg.kv}>",
     }
 
     if args.extra or args.flushed:
@@ -372,13 +407,20 @@ def main() -> int:
         import oracle  # CPU baseline leg only
 
         threads = max(1, min(16, os.cpu_count() or 1))
+        if mixed:
+            o_off = oracle.mixed_offsets(cfg.d, kvs, classes)
+            decode = lambda sel: oracle.lookup_decode_mixed(lut, records, cfg.d, kvs, classes, sel,
+                                                            offsets=o_off, nthreads=threads)
+        else:
+            decode = lambda sel: oracle.lookup_decode(lut, records, cfg.rows, cfg.d, cfg.kv, sel,
+                                                      nthreads=threads)
         cal = min(n, 2048)
         t = time.perf_counter()
-        oracle.lookup_decode(lut, records, cfg.rows, cfg.d, cfg.kv, ids_np[:cal], nthreads=threads)
+        decode(ids_np[:cal])
         per_row = (time.perf_counter() - t) / cal
         sample = int(min(n, max(cal, args.cpu_seconds / max(per_row, 1e-9))))
         t = time.perf_counter()
-        exp, _ = oracle.lookup_decode(lut, records, cfg.rows, cfg.d, cfg.kv, ids_np[:sample], nthreads=threads)
+        exp, _ = decode(ids_np[:sample])
         cpu_s = time.perf_counter() - t
         got = out[:sample].view(torch.int16).cpu().numpy().view(np.uint16)
         res["cpu_baseline"] = {

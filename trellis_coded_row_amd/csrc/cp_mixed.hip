@@ -18,48 +18,50 @@
 // two bit planes under a mask), and has class bit j of (p0, p1).
 //
 // The kernel is the single-rate gather-decode with the record located through
-// the index and the trellis walk chosen per row: at d = 512 a row fills the
-// wave, so the rate is uniform per row and selects one of four decoders with
-// a scalar branch; at smaller d the rows decoded side by side may differ in
-// rate, and each rate present among them runs over the whole wave with its
-// result kept where it applies (the control flow stays uniform, which the
-// lane shuffles of the walk require).
+// the index and one trellis walk that takes the rate as an operand: shift
+// amounts come from kv, the history bits from the two previous lanes of the
+// row. Rows of different rates can therefore share a wave (d < 512) with
+// uniform control flow, and at d = 512 the code stays one walk per row rather
+// than four (a version with a compile-time walk per rate and a branch per row
+// was 3x the code and 8% slower on the d512 replay).
 #include "cp_lane.h"
 
 namespace cpk {
 
 namespace {
 
-template <int D, int KV, bool RAW, bool SALPHA>
-__device__ __forceinline__ u32x4 decode_rate(uint32_t nb, uint32_t ab, uint32_t l, uint32_t g,
-                                             const uint32_t *s_lut, uint32_t lds_off)
+// One row's 8 outputs of this lane for a rate known only at run time (kv per
+// lane): the history bits come from the two previous lanes of the row (kv = 3
+// needs both; for kv >= 4 the second contributes nothing), the window field
+// is 64 bits wide and the shifts take the rate as an operand.
+template <int D, bool RAW, bool SALPHA>
+__device__ __forceinline__ u32x4 decode_any_rate(uint32_t newbits, uint32_t kv, uint32_t alpha_bits, uint32_t l,
+                                                 uint32_t g, const uint32_t *s_lut, uint32_t lds_off)
 {
-    return decode_lane<D, KV, RAW, CPK_COPIES, SALPHA>(nb, ab, l, g, s_lut, lds_off);
-}
-
-// One row's lane outputs when the whole wave decodes that row (kv uniform).
-template <int D, bool RAW>
-__device__ __forceinline__ u32x4 decode_uniform(uint32_t kv, uint32_t nb, uint32_t ab, uint32_t l, uint32_t g,
-                                                const uint32_t *s_lut, uint32_t lds_off)
-{
-    switch (kv) {
-    case 3: return decode_rate<D, 3, RAW, true>(nb, ab, l, g, s_lut, lds_off);
-    case 4: return decode_rate<D, 4, RAW, true>(nb, ab, l, g, s_lut, lds_off);
-    case 5: return decode_rate<D, 5, RAW, true>(nb, ab, l, g, s_lut, lds_off);
-    default: return decode_rate<D, 6, RAW, true>(nb, ab, l, g, s_lut, lds_off);
+    constexpr int LANES = D / 8;
+    const uint32_t newb = 4u * kv, m = 16u - kv;
+    uint32_t prev, prev2;
+    if constexpr (LANES == 64) {
+        prev = __builtin_amdgcn_update_dpp(newbits, newbits, 0x13C /* wave_ror:1 */, 0xF, 0xF, false);
+        prev2 = __builtin_amdgcn_update_dpp(prev, prev, 0x13C, 0xF, 0xF, false);
+    } else {
+        prev = __shfl(newbits, (int)(g * LANES + (l + LANES - 1) % LANES), 64);
+        prev2 = __shfl(newbits, (int)(g * LANES + (l + LANES - 2) % LANES), 64);
     }
-}
-
-// Each rate present among the rows decoded side by side runs over the whole
-// wave; a lane keeps the result of its own row's rate.
-template <int D, int KV, bool RAW>
-__device__ __forceinline__ void decode_if_present(u32x4 &v, uint32_t kv, uint32_t nb, uint32_t ab, uint32_t l,
-                                                  uint32_t g, const uint32_t *s_lut, uint32_t lds_off)
-{
-    if (__ballot(kv == (uint32_t)KV)) {
-        const u32x4 t = decode_rate<D, KV, RAW, false>(nb, ab, l, g, s_lut, lds_off);
-        if (kv == (uint32_t)KV) v = t;
+    // the m bits of the code just below this lane's new bits
+    const uint32_t hist = (uint32_t)((((uint64_t)prev << newb) | prev2) >> (2u * newb - m));
+    const uint64_t field = ((uint64_t)newbits << m) | hist;
+    const float alpha = __builtin_bit_cast(float, alpha_bits);
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t x = (uint32_t)(field >> (kv * (uint32_t)k));
+        const uint32_t h = hash_mad(x);
+        const uint32_t e = *reinterpret_cast<const uint32_t *>(
+            reinterpret_cast<const char *>(s_lut) + and_or(h, 0xFF80u, and_or(x >> 9, 0x40u, lds_off)));
+        v[k] = emit_pair<RAW, SALPHA>(e, 0u, alpha);
     }
+    return v;
 }
 
 template <int D, bool RAW, int BLOCK, int CHUNK>
@@ -94,17 +96,22 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
         const uint64_t j = row_of(c, lane);
         return (c < nchunks && lane < CHUNK && j < n) ? ids[j] : 0;
     };
+    // index entry of the row a lane looks up (row 0 for an id outside the
+    // table or a lane past the chunk, whose rate and extent agree)
+    auto entry_of = [&](int64_t id) -> MixedEntry {
+        return index[((uint64_t)id < rows ? (uint64_t)id : 0) >> 5];
+    };
     int64_t my_id = load_id(wave);
+    MixedEntry e = entry_of(my_id);
     for (uint64_t c = wave; c < nchunks; c += waves) {
         uint32_t cn = __builtin_amdgcn_readfirstlane((uint32_t)((n - c * CHUNK) < CHUNK ? (n - c * CHUNK) : CHUNK));
         asm volatile("" : "+s"(cn));
         const bool in = lane < cn;
         const bool ok = in && (uint64_t)my_id < rows;
         bad |= in && !ok;
-        // lane k locates chunk row k's record (an invalid id reads row 0's,
-        // whose rate and extent are consistent with each other)
+        // lane k locates chunk row k's record (a lane past the chunk gets
+        // id 0 from load_id, so its entry is row 0's as well)
         const uint64_t rid = ok ? (uint64_t)my_id : 0;
-        const MixedEntry e = index[rid >> 5];
         const uint32_t j = (uint32_t)rid & 31u, below = (1u << j) - 1u;
         const uint32_t n1 = __builtin_popcount(e.p0 & ~e.p1 & below);
         const uint32_t n2 = __builtin_popcount(~e.p0 & e.p1 & below);
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
             }
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const u32x4 v = decode_uniform<D, RAW>(kv[i], nb[i], ab[i], l, g, s_lut, lds_off);
+                const u32x4 v = decode_any_rate<D, RAW, true>(nb[i], kv[i], ab[i], l, g, s_lut, lds_off);
                 if ((uint32_t)i < cn) store16(out + row_of(c, i) * (D / 2) + 4u * l, v);
             }
         } else {
@@ -144,14 +151,12 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
                 const uint32_t r = g * CI + i;
-                u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-                decode_if_present<D, 3, RAW>(v, kv[i], nb[i], ab[i], l, g, s_lut, lds_off);
-                decode_if_present<D, 4, RAW>(v, kv[i], nb[i], ab[i], l, g, s_lut, lds_off);
-                decode_if_present<D, 5, RAW>(v, kv[i], nb[i], ab[i], l, g, s_lut, lds_off);
-                decode_if_present<D, 6, RAW>(v, kv[i], nb[i], ab[i], l, g, s_lut, lds_off);
+                const u32x4 v = decode_any_rate<D, RAW, false>(nb[i], kv[i], ab[i], l, g, s_lut, lds_off);
                 if (r < cn) store16(out + row_of(c, r) * (D / 2) + 4u * l, v);
             }
         }
+        // the next chunk's index entries load while this chunk's stores drain
+        e = entry_of(my_id);
         const uint64_t badmask = __ballot(in) & ~okmask;
         if (badmask) {
             __builtin_amdgcn_s_waitcnt(0);
