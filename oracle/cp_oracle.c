@@ -51,7 +51,7 @@
  *   R7 encoder objective: minimise ||z - f(c)||^2 over tail-biting codes with
  *      unit scale; alpha is set afterwards from the norms. Ties keep the
  *      smallest predecessor and then the smallest start memory.
- *   R10 mixed-rate table (the pages study allocating bits by access frequency
+ *   R11 mixed-rate table (the pages study allocating bits by access frequency
  *      over their code rates but give no format): each row has a rate class,
  *      class c codes at kv_c bits per step, and the records of all rows are
  *      packed in row order, so row i's record starts at the sum of the record
@@ -233,7 +233,7 @@ typedef struct {
     const uint8_t *records;
     uint64_t rows;
     uint32_t d, kv;
-    /* mixed-rate tables (R10): NULL for a single-rate table */
+    /* mixed-rate tables (R11): NULL for a single-rate table */
     const uint32_t *kv_of_class;
     const uint8_t *row_class;
     const uint64_t *offsets;
@@ -308,7 +308,7 @@ int64_t cpo_lookup_decode(const uint16_t *lut, const uint8_t *records, uint64_t 
 }
 
 /* ------------------------------------------------------------------------ */
-/* mixed-rate tables (R10)                                                   */
+/* mixed-rate tables (R11)                                                   */
 /* ------------------------------------------------------------------------ */
 
 /* Record offsets of a mixed-rate table: row i is coded at

@@ -371,7 +371,7 @@ def test_distortion_between_rate_distortion_bound_and_scalar_quantiser():
 
 
 # ---------------------------------------------------------------------------
-# mixed-rate tables (reading R10)
+# mixed-rate tables (reading R11)
 # ---------------------------------------------------------------------------
 
 def test_mixed_offsets_are_the_running_sum_of_record_sizes():
