@@ -233,6 +233,8 @@ def main() -> int:
     ap.add_argument("--noncoherent", action="store_true", help="host_d512: non-coherent pinned memory")
     ap.add_argument("--dedup", action="store_true",
                     help="use cp_lookup_decode_dedup (each distinct record fetched once)")
+    ap.add_argument("--hot-share", type=float, default=0.0,
+                    help="host_d512: keep device copies of this share of the rows, the most looked-up first")
     ap.add_argument("--flushed", action="store_true",
                     help="also time launches with L2/MALL flushed (512 MiB written) before each")
     ap.add_argument("--probes", action="store_true", help="also run 1 GiB copy and fill probes")
@@ -302,6 +304,12 @@ def main() -> int:
         for r0 in range(0, cfg.rows, chunk):
             table.upload(records[r0:r0 + chunk], first_row=r0)
     upload_s = time.time() - t_up
+    hot_rows = 0
+    if args.hot_share > 0:
+        # the rows of the smallest Zipf ranks of the id stream (its most frequent rows)
+        k = int(args.hot_share * cfg.rows)
+        hot_rows = table.set_hot_rows(workload.keyed_permutation(np.arange(k, dtype=np.int64), cfg.rows,
+                                                                  cfg.ids_seed))
 
     n = ids_np.shape[0]
     ids = torch.from_numpy(ids_np).cuda()
@@ -364,6 +372,7 @@ def main() -> int:
             "lookups": n,
             "ids": ids_kind, "ids_sha256_16": workload.ids_digest(ids_np),
             "residency": "host" + ("-noncoherent" if args.noncoherent else "") if cfg.host_resident else "hbm",
+            "hot_rows_in_hbm": hot_rows,
             "entry_point": "cp_lookup_decode_dedup" if args.dedup else "cp_lookup_decode",
         },
         "effective_GBps": algo_bytes * args.steps / (total_ms / 1e3) / 1e9,

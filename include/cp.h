@@ -231,9 +231,30 @@ uint64_t cp_encode_workspace_bytes(const cp_table *table, uint64_t nrows);
  *   stream    - as in cp_lookup_decode. Asynchronous; no allocation.
  * Lookups of the rows being encoded must not overlap the call.
  * Errors: INVALID_ARGUMENT (NULL table/rows/workspace, range beyond rows,
- * misaligned pointers, workspace too small), UNSUPPORTED, HIP. */
+ * misaligned pointers, workspace too small), UNSUPPORTED (no encoder for the
+ * shape, a mixed-rate table, or a table with hot-row copies: set those after
+ * encoding), HIP. */
 cp_status cp_table_encode(cp_table *table, uint64_t first_row, uint64_t nrows, const float *rows, void *workspace,
                           uint64_t workspace_bytes, void *stream);
+
+/* Keeps device-memory copies of the records of `rows` (host int64[count], any
+ * order, repeats allowed) for a table in pinned host memory, so that lookups
+ * of those rows read HBM instead of crossing PCIe. Meant for the rows looked
+ * up most often: the pages name caching of hot rows, and note that the access
+ * counts it rests on may change with the text a model serves ("Assumptions
+ * and limits"; ai4snews digest, Perspective).
+ *   - Replaces any previous set; count == 0 drops the copies.
+ *   - Waits for the device first (no lookup may still read the old copies).
+ *   - cp_lookup_decode / cp_lookup_decode_raw use the copies; results are the
+ *     same as without them. cp_table_upload keeps the copies current.
+ *   - Device memory: count * R bytes plus an index of 8 bytes per 32 rows.
+ * Errors: INVALID_ARGUMENT (NULL table, NULL rows with count > 0, a row
+ * outside [0, rows)), UNSUPPORTED (a table in device memory or a mixed-rate
+ * table), OUT_OF_MEMORY, HIP. */
+cp_status cp_table_set_hot_rows(cp_table *table, const int64_t *rows, uint64_t count);
+
+/* Number of distinct rows with a device copy (0 for NULL or none). */
+uint64_t cp_table_hot_rows(const cp_table *table);
 
 /* Synchronises `stream`, then returns CP_ERR_ID_OUT_OF_RANGE and clears the
  * table's flag if any lookup since the last check saw an id outside

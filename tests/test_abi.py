@@ -183,3 +183,8 @@ def test_one_hip_runtime_in_the_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True,
                          cwd=cpbuild.ROOT).stdout.split()
     assert out[-1] == "1"
+
+
+def test_hot_rows_without_a_table():
+    assert cp.cp_table_set_hot_rows(0, 0, 0) == cp.CP_ERR_INVALID_ARGUMENT
+    assert cp.cp_table_hot_rows(0) == 0

@@ -105,3 +105,18 @@ def test_mixed_d512_replay():
         check_mixed(t, cfg.d, kvs, cls, packed, cfg.ids(), "mixed_d512 zipf replay", offsets=off)
     finally:
         t.close()
+
+
+def test_host_d512_replay_with_hot_rows(big_records):
+    """The pinned-host table with device copies of the 5% most looked-up rows
+    (by Zipf rank): the whole replay against the oracle."""
+    _, recs = big_records
+    cfg = workload.CONFIGS["host_d512"]
+    hot = workload.keyed_permutation(np.arange(cfg.rows // 20, dtype=np.int64), cfg.rows, cfg.ids_seed)
+    say("building the pinned-host table with 4,884,500 hot rows")
+    t = make_table(LUT, recs, cfg.d, cfg.kv, residency=cp.CP_RESIDENCY_HOST_MAPPED, chunk_rows=1 << 24)
+    try:
+        assert t.set_hot_rows(hot) == hot.size
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), "host_d512 zipf replay, hot rows")
+    finally:
+        t.close()

@@ -29,6 +29,7 @@ __all__ = [
     "cp_record_bytes", "cp_supported", "cp_table_create", "cp_table_upload", "cp_lookup_decode",
     "cp_lookup_decode_raw", "cp_dedup_workspace_bytes", "cp_lookup_decode_dedup",
     "cp_table_download", "cp_encode_workspace_bytes", "cp_table_encode",
+    "cp_table_set_hot_rows", "cp_table_hot_rows",
     "cp_table_create_mixed", "cp_table_record_range", "cp_table_describe_mixed", "cp_mixed_desc", "MixedTable",
     "cp_table_check", "cp_table_describe", "cp_table_destroy",
     "cp_status_string", "cp_last_hip_error",
@@ -109,6 +110,8 @@ def load_library() -> ctypes.CDLL:
         "cp_table_download": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp]),
         "cp_encode_workspace_bytes": (ctypes.c_uint64, [vp, ctypes.c_uint64]),
         "cp_table_encode": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp]),
+        "cp_table_set_hot_rows": (ctypes.c_int, [vp, vp, ctypes.c_uint64]),
+        "cp_table_hot_rows": (ctypes.c_uint64, [vp]),
         "cp_table_check": (ctypes.c_int, [vp, vp]),
         "cp_table_describe": (ctypes.c_int, [vp, ctypes.POINTER(cp_table_desc)]),
         "cp_table_destroy": (ctypes.c_int, [vp]),
@@ -210,6 +213,14 @@ def cp_encode_workspace_bytes(table: int, nrows: int) -> int:
 def cp_table_encode(table: int, first_row: int, nrows: int, rows_ptr: int, workspace_ptr: int,
                     workspace_bytes: int, stream: int | None) -> int:
     return _L.cp_table_encode(table, first_row, nrows, rows_ptr, workspace_ptr, workspace_bytes, stream)
+
+
+def cp_table_set_hot_rows(table: int, rows_ptr: int, count: int) -> int:
+    return _L.cp_table_set_hot_rows(table, rows_ptr, count)
+
+
+def cp_table_hot_rows(table: int) -> int:
+    return int(_L.cp_table_hot_rows(table))
 
 
 def cp_table_check(table: int, stream: int | None) -> int:
@@ -352,6 +363,15 @@ class Table:
                              workspace.numel() * workspace.element_size(), _stream_handle(stream))
         if st != CP_OK:
             raise CPError(st, "cp_table_encode")
+
+    def set_hot_rows(self, rows) -> int:
+        """Keeps device copies of these rows' records (pinned-host tables);
+        returns the number of distinct rows cached. Empty: drop the copies."""
+        r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        st = cp_table_set_hot_rows(self.handle, r.ctypes.data if r.size else 0, r.size)
+        if st != CP_OK:
+            raise CPError(st, "cp_table_set_hot_rows")
+        return cp_table_hot_rows(self.handle)
 
     def check(self, stream=None) -> bool:
         """Synchronises; False (and the flag cleared) if an id was out of range."""

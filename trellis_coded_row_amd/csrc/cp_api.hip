@@ -18,6 +18,11 @@ struct cp_table {
     cpk::MixedRates rates;
     cpk::MixedEntry *index_dev;
     cpk::MixedEntry *index_host;
+    // hot-row cache of a host-resident table (none when hot_count == 0)
+    uint64_t hot_count;
+    cpk::HotEntry *hot_index_dev;
+    cpk::HotEntry *hot_index_host;
+    uint8_t *hot_recs;  // device copies of the hot rows' records, in row order
     uint8_t *records;      // hipMalloc'd (device) or hipHostMalloc'd (host)
     uint8_t *records_dev;  // device-accessible address of the same memory
     uint32_t *lut_dev;
@@ -69,9 +74,21 @@ const char *cp_status_string(cp_status s)
 
 int cp_last_hip_error(void) { return g_last_hip_error; }
 
+static void drop_hot(cp_table *t)
+{
+    if (t->hot_index_dev) (void)hipFree(t->hot_index_dev);
+    if (t->hot_recs) (void)hipFree(t->hot_recs);
+    free(t->hot_index_host);
+    t->hot_index_dev = nullptr;
+    t->hot_recs = nullptr;
+    t->hot_index_host = nullptr;
+    t->hot_count = 0;
+}
+
 static void release(cp_table *t)
 {
     if (!t) return;
+    drop_hot(t);
     if (t->records) {
         if (t->desc.residency == CP_RESIDENCY_HOST_MAPPED)
             (void)hipHostFree(t->records);
@@ -227,6 +244,82 @@ cp_status cp_table_record_range(const cp_table *t, uint64_t row, uint64_t *offse
     return CP_OK;
 }
 
+// Slot of row r in the hot-row cache (r must be hot).
+static uint64_t hot_slot(const cp_table *t, uint64_t r)
+{
+    const cpk::HotEntry &h = t->hot_index_host[r >> 5];
+    const uint32_t j = (uint32_t)r & 31u;
+    return h.base + (uint64_t)__builtin_popcount(h.bits & ((1u << j) - 1u));
+}
+
+static bool is_hot(const cp_table *t, uint64_t r) { return (t->hot_index_host[r >> 5].bits >> (r & 31u)) & 1u; }
+
+// Copies the host records of the hot rows among [first_row, first_row + nrows)
+// into their cache slots (consecutive rows' hot copies are consecutive slots).
+static cp_status refresh_hot(cp_table *t, uint64_t first_row, uint64_t nrows)
+{
+    uint64_t lo = UINT64_MAX, hi = 0;
+    for (uint64_t r = first_row; r < first_row + nrows; ++r) {
+        if ((r & 31u) == 0 && t->hot_index_host[r >> 5].bits == 0 && r + 32 <= first_row + nrows) {
+            r += 31;  // no hot row in this block
+            continue;
+        }
+        if (!is_hot(t, r)) continue;
+        if (lo == UINT64_MAX) lo = r;
+        hi = r;
+    }
+    if (lo == UINT64_MAX) return CP_OK;
+    const uint64_t R = t->record_bytes, s0 = hot_slot(t, lo), s1 = hot_slot(t, hi);
+    uint8_t *stage = (uint8_t *)malloc((s1 - s0 + 1) * R);
+    if (!stage) return CP_ERR_OUT_OF_MEMORY;
+    for (uint64_t r = lo; r <= hi; ++r)
+        if (is_hot(t, r)) memcpy(stage + (hot_slot(t, r) - s0) * R, t->records + r * R, R);
+    hipError_t e = hipMemcpy(t->hot_recs + s0 * R, stage, (s1 - s0 + 1) * R, hipMemcpyHostToDevice);
+    free(stage);
+    return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
+cp_status cp_table_set_hot_rows(cp_table *t, const int64_t *rows, uint64_t count)
+{
+    if (!t || (count && !rows)) return CP_ERR_INVALID_ARGUMENT;
+    if (t->mixed || t->desc.residency != CP_RESIDENCY_HOST_MAPPED) return CP_ERR_UNSUPPORTED;
+    for (uint64_t i = 0; i < count; ++i)
+        if (rows[i] < 0 || (uint64_t)rows[i] >= t->desc.rows) return CP_ERR_INVALID_ARGUMENT;
+    hipError_t e = hipSetDevice(t->device);
+    if (e == hipSuccess) e = hipDeviceSynchronize();  // no lookup may still read the old cache
+    if (e != hipSuccess) return hip_fail(e);
+    drop_hot(t);
+    if (count == 0) return CP_OK;
+    const uint64_t nblk = (t->desc.rows + 31) / 32;
+    t->hot_index_host = (cpk::HotEntry *)calloc(nblk, sizeof(cpk::HotEntry));
+    if (!t->hot_index_host) return CP_ERR_OUT_OF_MEMORY;
+    for (uint64_t i = 0; i < count; ++i) t->hot_index_host[rows[i] >> 5].bits |= 1u << (rows[i] & 31);
+    uint64_t slots = 0;
+    for (uint64_t b = 0; b < nblk; ++b) {
+        if (slots > UINT32_MAX) {
+            drop_hot(t);
+            return CP_ERR_INVALID_ARGUMENT;  // more than 2^32 hot rows
+        }
+        t->hot_index_host[b].base = (uint32_t)slots;
+        slots += (uint64_t)__builtin_popcount(t->hot_index_host[b].bits);
+    }
+    t->hot_count = slots;
+    e = hipMalloc((void **)&t->hot_index_dev, nblk * sizeof(cpk::HotEntry));
+    if (e == hipSuccess)
+        e = hipMemcpy(t->hot_index_dev, t->hot_index_host, nblk * sizeof(cpk::HotEntry), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMalloc((void **)&t->hot_recs, slots * t->record_bytes + kTailPad);
+    if (e == hipSuccess) e = hipMemset(t->hot_recs + slots * t->record_bytes, 0, kTailPad);
+    if (e != hipSuccess) {
+        drop_hot(t);
+        return hip_fail(e);
+    }
+    const cp_status st = refresh_hot(t, 0, t->desc.rows);
+    if (st != CP_OK) drop_hot(t);
+    return st;
+}
+
+uint64_t cp_table_hot_rows(const cp_table *t) { return t ? t->hot_count : 0; }
+
 cp_status cp_table_upload(cp_table *t, uint64_t first_row, uint64_t nrows, const void *src)
 {
     if (!t) return CP_ERR_INVALID_ARGUMENT;
@@ -237,7 +330,7 @@ cp_status cp_table_upload(cp_table *t, uint64_t first_row, uint64_t nrows, const
     record_span(t, first_row, nrows, &off, &bytes);
     if (t->desc.residency == CP_RESIDENCY_HOST_MAPPED) {
         memcpy(t->records + off, src, bytes);
-        return CP_OK;
+        return t->hot_count ? refresh_hot(t, first_row, nrows) : CP_OK;
     }
     hipError_t e = hipMemcpy(t->records + off, src, bytes, hipMemcpyHostToDevice);
     return e == hipSuccess ? CP_OK : hip_fail(e);
@@ -266,6 +359,14 @@ static cp_status lookup(const cp_table *t, const int64_t *ids, uint64_t n, uint1
     }
     cpk::LaunchArgs a;
     a.records = t->records_dev;
+    if (t->hot_count) {
+        const uintptr_t host = (uintptr_t)t->records_dev, hot = (uintptr_t)t->hot_recs;
+        const uintptr_t base = host < hot ? host : hot;
+        a.records = (const uint8_t *)base;
+        a.hot_index = t->hot_index_dev;
+        a.host_off0 = host - base;
+        a.hot_off0 = hot - base;
+    }
     a.rows = t->desc.rows;
     a.lut = t->lut_dev;
     a.ids = ids;
@@ -367,7 +468,9 @@ cp_status cp_table_encode(cp_table *t, uint64_t first_row, uint64_t nrows, const
     if (nrows == 0) return CP_OK;
     if (!rows || ((uintptr_t)rows & 3u) || first_row > t->desc.rows || nrows > t->desc.rows - first_row)
         return CP_ERR_INVALID_ARGUMENT;
-    if (t->mixed || !cpk::encode_supported(t->desc.d, t->desc.bits_per_step)) return CP_ERR_UNSUPPORTED;
+    // a table with hot-row copies would need them refreshed after the kernel
+    if (t->mixed || t->hot_count || !cpk::encode_supported(t->desc.d, t->desc.bits_per_step))
+        return CP_ERR_UNSUPPORTED;
     uint32_t blocks = 0;
     hipError_t e = cpk::encode_grid(t->desc.bits_per_step, t->num_cus, nrows, &blocks);
     if (e != hipSuccess) return hip_fail(e);

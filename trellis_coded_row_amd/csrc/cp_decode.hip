@@ -40,12 +40,19 @@
 
 namespace cpk {
 
-template <int D, int KV, bool RAW, int COPIES, int BLOCK, int CHUNK>
+// With HOT, some rows' records also sit in a device-memory copy (a cache of
+// looked-up-often rows of a table in pinned host memory): hot_index holds per
+// block of 32 rows the cache slot of its first hot row and a bitmap of its hot
+// rows, so hot row 32b + j is slot base + popcount(bits below j). Offsets are
+// then taken from `tab` = the lower of the two regions' addresses, the host
+// records starting at host_off0 and the cache at hot_off0.
+template <int D, int KV, bool RAW, int COPIES, int BLOCK, int CHUNK, bool HOT>
 __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict__ tab, const uint64_t rows,
                                                        const uint32_t *__restrict__ lut,
                                                        const int64_t *__restrict__ ids, const uint64_t n,
                                                        uint32_t *__restrict__ out, int *__restrict__ err,
-                                                       const bool by_offset)
+                                                       const bool by_offset, const HotEntry *__restrict__ hot_index,
+                                                       const uint64_t host_off0, const uint64_t hot_off0)
 {
     constexpr int LANES = D / 8;        // lanes per row
     constexpr int GROUPS = 64 / LANES;  // rows decoded side by side in a wave
@@ -98,7 +105,18 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
         // by_offset a record's byte offset in a staging area (-1: invalid)
         const bool ok = in && (by_offset ? my_id >= 0 : (uint64_t)my_id < rows);
         bad |= in && !ok;
-        const uint64_t my_off = !ok ? 0 : by_offset ? (uint64_t)my_id : (uint64_t)my_id * R;  // even
+        uint64_t my_off;
+        if constexpr (HOT) {
+            // an invalid id reads the first host record (its row is zeroed below)
+            const uint64_t rid = ok ? (uint64_t)my_id : 0;
+            const HotEntry h = hot_index[rid >> 5];
+            const uint32_t j = (uint32_t)rid & 31u;
+            my_off = ((h.bits >> j) & 1u)
+                         ? hot_off0 + (uint64_t)(h.base + __builtin_popcount(h.bits & ((1u << j) - 1u))) * R
+                         : host_off0 + rid * R;
+        } else {
+            my_off = !ok ? 0 : by_offset ? (uint64_t)my_id : (uint64_t)my_id * R;  // even
+        }
         const uint64_t okmask = __ballot(ok);
         my_id = load_id(c + waves);
 
@@ -190,7 +208,7 @@ struct Tune {
     static constexpr int CHUNK = CPK_CHUNK;
 };
 
-template <int D, int KV, bool RAW>
+template <int D, int KV, bool RAW, bool HOT>
 static hipError_t launch_one(const LaunchArgs &a)
 {
     using T = Tune<D, KV>;
@@ -203,9 +221,9 @@ static hipError_t launch_one(const LaunchArgs &a)
         const uint64_t cap = (uint64_t)T::BLOCKS_PER_CU * (a.num_cus > 0 ? a.num_cus : 256);
         if (blocks > cap) blocks = cap;
     }
-    hipLaunchKernelGGL((gather_decode<D, KV, RAW, T::COPIES, T::BLOCK, CHUNK>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((gather_decode<D, KV, RAW, T::COPIES, T::BLOCK, CHUNK, HOT>), dim3((unsigned)blocks),
                        dim3(T::BLOCK), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err,
-                       a.by_offset);
+                       a.by_offset, a.hot_index, a.host_off0, a.hot_off0);
     return hipGetLastError();
 }
 
@@ -213,10 +231,12 @@ typedef hipError_t (*launch_fn)(const LaunchArgs &);
 
 struct Entry {
     uint32_t d, kv;
-    launch_fn scaled, raw;
+    launch_fn scaled, raw, hot_scaled, hot_raw;
 };
 
-#define CPK_ENTRY(D, KV) {D, KV, &launch_one<D, KV, false>, &launch_one<D, KV, true>}
+#define CPK_ENTRY(D, KV)                                                                                   \
+    {D, KV, &launch_one<D, KV, false, false>, &launch_one<D, KV, true, false>, &launch_one<D, KV, false, true>, \
+     &launch_one<D, KV, true, true>}
 
 static const Entry kTable[] = {
     CPK_ENTRY(64, 3),  CPK_ENTRY(64, 4),  CPK_ENTRY(64, 5),  CPK_ENTRY(64, 6),
@@ -238,6 +258,7 @@ hipError_t launch(uint32_t d, uint32_t kv, bool raw, const LaunchArgs &a)
 {
     const Entry *e = find(d, kv);
     if (!e) return hipErrorInvalidValue;
+    if (a.hot_index) return raw ? e->hot_raw(a) : e->hot_scaled(a);
     return raw ? e->raw(a) : e->scaled(a);
 }
 

@@ -7,6 +7,12 @@
 
 namespace cpk {
 
+// Hot-row cache of a host-resident table: one entry per 32 rows.
+struct alignas(8) HotEntry {
+    uint32_t base;  // cache slot of the block's first hot row
+    uint32_t bits;  // bit j: row 32b + j has a copy in the cache
+};
+
 // Launch parameters of one gather-decode call.
 struct LaunchArgs {
     const uint8_t *records;   // device-accessible base of the packed records
@@ -19,6 +25,10 @@ struct LaunchArgs {
     int *err;                 // sticky out-of-range flag
     int num_cus;              // compute units of the device
     hipStream_t stream;
+    // hot-row cache (hot_index null: none): records = the lower of the host
+    // records' and the cache's addresses, each region at its offset from it
+    const HotEntry *hot_index = nullptr;
+    uint64_t host_off0 = 0, hot_off0 = 0;
 };
 
 // Byte offsets of the regions of a dedup workspace (see cp_dedup.hip).
