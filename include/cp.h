@@ -39,8 +39,15 @@
  * cp_table_check() reports and clears.
  *
  * Threading: lookups only read the table and may run concurrently on any
- * streams. cp_table_upload and cp_table_destroy must not overlap lookups on
- * the same table; the caller synchronises.
+ * streams. cp_table_upload, cp_table_encode and cp_table_destroy write or free
+ * the table and must not overlap lookups of the rows they touch; the caller
+ * synchronises (cp_table_set_hot_rows and cp_table_download synchronise the
+ * device themselves).
+ *
+ * Devices: a table lives on the device that was current at creation. Every
+ * call that touches it makes that device current for the duration of the
+ * call and restores the caller's device afterwards; a stream passed in must
+ * belong to the table's device.
  */
 #ifndef CP_H
 #define CP_H

@@ -40,6 +40,27 @@ static cp_status hip_fail(hipError_t e)
                                                                          : CP_ERR_HIP;
 }
 
+// Makes the table's device current for the duration of a call and restores
+// the caller's device afterwards (launches on the null stream, copies and
+// synchronisation then all address the device that holds the table).
+struct DeviceGuard {
+    int prev = -1;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev)
+    {
+        int cur = -1;
+        err = hipGetDevice(&cur);
+        if (err == hipSuccess && cur != dev) {
+            err = hipSetDevice(dev);
+            if (err == hipSuccess) prev = cur;
+        }
+    }
+    ~DeviceGuard()
+    {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
 // Bytes after the last record that loads of the last record may touch
 // (aligned dwords straddling the record end); zeroed at creation.
 static const uint64_t kTailPad = 64;
@@ -285,7 +306,8 @@ cp_status cp_table_set_hot_rows(cp_table *t, const int64_t *rows, uint64_t count
     if (t->mixed || t->desc.residency != CP_RESIDENCY_HOST_MAPPED) return CP_ERR_UNSUPPORTED;
     for (uint64_t i = 0; i < count; ++i)
         if (rows[i] < 0 || (uint64_t)rows[i] >= t->desc.rows) return CP_ERR_INVALID_ARGUMENT;
-    hipError_t e = hipSetDevice(t->device);
+    DeviceGuard guard(t->device);
+    hipError_t e = guard.err;
     if (e == hipSuccess) e = hipDeviceSynchronize();  // no lookup may still read the old cache
     if (e != hipSuccess) return hip_fail(e);
     drop_hot(t);
@@ -326,6 +348,8 @@ cp_status cp_table_upload(cp_table *t, uint64_t first_row, uint64_t nrows, const
     if (nrows == 0) return CP_OK;
     if (!src || first_row > t->desc.rows || nrows > t->desc.rows - first_row)
         return CP_ERR_INVALID_ARGUMENT;
+    DeviceGuard guard(t->device);
+    if (guard.err != hipSuccess) return hip_fail(guard.err);
     uint64_t off, bytes;
     record_span(t, first_row, nrows, &off, &bytes);
     if (t->desc.residency == CP_RESIDENCY_HOST_MAPPED) {
@@ -342,6 +366,8 @@ static cp_status lookup(const cp_table *t, const int64_t *ids, uint64_t n, uint1
     if (!t) return CP_ERR_INVALID_ARGUMENT;
     if (n == 0) return CP_OK;
     if (!ids || !out || ((uintptr_t)out & 15u) || ((uintptr_t)ids & 7u)) return CP_ERR_INVALID_ARGUMENT;
+    DeviceGuard guard(t->device);
+    if (guard.err != hipSuccess) return hip_fail(guard.err);
     if (t->mixed) {
         cpk::MixedLaunchArgs m;
         m.records = t->records_dev;
@@ -407,6 +433,8 @@ cp_status cp_lookup_decode_dedup(const cp_table *t, const int64_t *ids, uint64_t
     if (t->mixed) return CP_ERR_UNSUPPORTED;
     const cpk::DedupLayout L = cpk::dedup_layout(n, t->record_bytes, kTailPad);
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total) return CP_ERR_INVALID_ARGUMENT;
+    DeviceGuard guard(t->device);
+    if (guard.err != hipSuccess) return hip_fail(guard.err);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     cpk::DedupArgs d;
     d.records = t->records_dev;
@@ -442,7 +470,8 @@ cp_status cp_table_download(const cp_table *t, uint64_t first_row, uint64_t nrow
     if (!dst || first_row > t->desc.rows || nrows > t->desc.rows - first_row) return CP_ERR_INVALID_ARGUMENT;
     uint64_t off, bytes;
     record_span(t, first_row, nrows, &off, &bytes);
-    hipError_t e = hipSetDevice(t->device);
+    DeviceGuard guard(t->device);
+    hipError_t e = guard.err;
     if (e == hipSuccess) e = hipDeviceSynchronize();  // encodes in flight on any stream land first
     if (e != hipSuccess) return hip_fail(e);
     if (t->desc.residency == CP_RESIDENCY_HOST_MAPPED) {
@@ -456,6 +485,8 @@ cp_status cp_table_download(const cp_table *t, uint64_t first_row, uint64_t nrow
 uint64_t cp_encode_workspace_bytes(const cp_table *t, uint64_t nrows)
 {
     if (!t || nrows == 0 || t->mixed) return 0;
+    DeviceGuard guard(t->device);
+    if (guard.err != hipSuccess) return 0;
     uint32_t blocks = 0;
     if (cpk::encode_grid(t->desc.bits_per_step, t->num_cus, nrows, &blocks) != hipSuccess) return 0;
     return (uint64_t)blocks * cpk::encode_workspace_per_block(t->desc.d, t->desc.bits_per_step);
@@ -471,6 +502,8 @@ cp_status cp_table_encode(cp_table *t, uint64_t first_row, uint64_t nrows, const
     // a table with hot-row copies would need them refreshed after the kernel
     if (t->mixed || t->hot_count || !cpk::encode_supported(t->desc.d, t->desc.bits_per_step))
         return CP_ERR_UNSUPPORTED;
+    DeviceGuard guard(t->device);
+    if (guard.err != hipSuccess) return hip_fail(guard.err);
     uint32_t blocks = 0;
     hipError_t e = cpk::encode_grid(t->desc.bits_per_step, t->num_cus, nrows, &blocks);
     if (e != hipSuccess) return hip_fail(e);
@@ -494,6 +527,8 @@ cp_status cp_table_encode(cp_table *t, uint64_t first_row, uint64_t nrows, const
 cp_status cp_table_check(cp_table *t, void *stream)
 {
     if (!t) return CP_ERR_INVALID_ARGUMENT;
+    DeviceGuard guard(t->device);
+    if (guard.err != hipSuccess) return hip_fail(guard.err);
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
     int flag = 0;
     if (e == hipSuccess) e = hipMemcpy(&flag, t->err_dev, sizeof(int), hipMemcpyDeviceToHost);
@@ -531,9 +566,13 @@ cp_status cp_table_describe_mixed(const cp_table *t, cp_mixed_desc *desc_out)
 cp_status cp_table_destroy(cp_table *t)
 {
     if (!t) return CP_OK;
-    hipError_t e = hipSetDevice(t->device);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    release(t);
+    hipError_t e;
+    {
+        DeviceGuard guard(t->device);
+        e = guard.err;
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        release(t);
+    }
     return e == hipSuccess ? CP_OK : hip_fail(e);
 }
 
