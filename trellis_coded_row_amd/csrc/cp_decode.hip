@@ -149,11 +149,13 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
                 if ((uint32_t)i < cn) store16(out + row_of(c, i) * (D / 2) + 4u * l, v);
             }
         } else {
-            // several rows side by side: group g decodes rows g*CI .. g*CI+CI-1
+            // several rows side by side: group g decodes rows g, g + GROUPS, ...
+            // of the chunk, so each store instruction writes GROUPS adjacent
+            // rows (1 KB contiguous) rather than GROUPS separate pieces
             uint32_t nb[CI], ab[CI];
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const int r = (int)(g * CI + i);
+                const int r = (int)(i * GROUPS + g);
                 const uint64_t o = __shfl(my_off, r, 64);
                 if constexpr (KV == 4) {
                     nb[i] = *reinterpret_cast<const uint16_t *>(tab + o + 2u * l);
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
             }
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const uint32_t r = g * CI + i;
+                const uint32_t r = i * GROUPS + g;
                 const u32x4 v = decode_lane<D, KV, RAW, COPIES, false>(nb[i], ab[i], l, g, s_lut, lds_off);
                 if (r < cn) store16(out + row_of(c, r) * (D / 2) + 4u * l, v);
             }
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
             __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const uint32_t r = g * CI + i;
+                const uint32_t r = i * GROUPS + g;
                 if ((badmask >> r) & 1u)
                     store16(out + row_of(c, r) * (D / 2) + 4u * l, (u32x4){0u, 0u, 0u, 0u});
             }

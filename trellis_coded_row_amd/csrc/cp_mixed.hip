@@ -142,7 +142,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
             uint32_t nb[CI], ab[CI], kv[CI];
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const int r = (int)(g * CI + i);
+                const int r = (int)(i * GROUPS + g);
                 const uint64_t o = __shfl(my_off, r, 64);
                 kv[i] = (uint32_t)__shfl((int)my_kv, r, 64);
                 nb[i] = lane_bits(tab, o, 4u * kv[i], l);
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
             }
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const uint32_t r = g * CI + i;
+                const uint32_t r = i * GROUPS + g;
                 const u32x4 v = decode_any_rate<D, RAW, false>(nb[i], kv[i], ab[i], l, g, s_lut, lds_off);
                 if (r < cn) store16(out + row_of(c, r) * (D / 2) + 4u * l, v);
             }
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
             __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const uint32_t r = g * CI + i;
+                const uint32_t r = i * GROUPS + g;
                 if ((badmask >> r) & 1u)
                     store16(out + row_of(c, r) * (D / 2) + 4u * l, (u32x4){0u, 0u, 0u, 0u});
             }
