@@ -70,13 +70,19 @@ struct Tcq {
     static constexpr uint32_t IPT = S / kThreads;      // next memories per thread
     static constexpr uint32_t TPG = BR / IPT;          // threads per group
     static constexpr uint32_t SP = S + (S >> 4);       // padded metric array length
+    // copies of each branch cost, lane l reading copy l mod CC: lanes reading
+    // different copies never meet on an LDS bank. Measured per rate on the
+    // d512 batch (ms for 4,096 rows with 1 / 2 / 4 copies): kv 4: 41.2 / 36.1
+    // / 33.3; kv 5: 40.0 / 32.0 / 34.9; kv 6: 37.1 / 37.5 / 55.7; kv 3 has
+    // no LDS left for a second copy.
+    static constexpr uint32_t CC = KV == 4 ? 4 : KV == 5 ? 2 : 1;
     static_assert(IPT >= 1 && TPG * G == (uint32_t)kThreads, "thread mapping");
 };
 
 template <int KV>
 struct Shared {
     double D[2][Tcq<KV>::SP];
-    double cost[2][1024];  // branch costs of one step, entry 2 * idx + negated
+    double cost[2][1024 * Tcq<KV>::CC];  // branch costs of one step, entry (2 idx + negated) * CC + copy
     double z[512];
     uint32_t lut[512];
     uint8_t code[6 * 512 / 16 + 2];
@@ -86,7 +92,9 @@ struct Shared {
     double norm;
 };
 
-// cost[2 idx + neg] = (z0 - g0)^2 + (z1 - g1)^2 for the pair g = +-LUT[idx].
+// cost[(2 idx + neg) * CC + c] = (z0 - g0)^2 + (z1 - g1)^2 for the pair
+// g = +-LUT[idx], for every copy c.
+template <uint32_t CC>
 __device__ __forceinline__ void fill_costs(double *cost, const uint32_t *lut, double z0, double z1)
 {
     const uint32_t i = threadIdx.x;
@@ -97,7 +105,9 @@ __device__ __forceinline__ void fill_costs(double *cost, const uint32_t *lut, do
         g1 = -g1;
     }
     const double e0 = z0 - g0, e1 = z1 - g1;
-    cost[i] = e0 * e0 + e1 * e1;
+    const double c = e0 * e0 + e1 * e1;
+#pragma unroll
+    for (uint32_t k = 0; k < CC; ++k) cost[i * CC + k] = c;
 }
 
 // One store of a thread's IPT back-pointers (consecutive bytes).
@@ -143,9 +153,10 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
     using P = Tcq<KV>;
     const uint32_t tid = threadIdx.x;
     const uint32_t L = tid % P::G, tq = tid / P::G;
+    const uint32_t cpy = tid & (P::CC - 1);
     for (uint32_t m = tid; m < P::S; m += kThreads)
         sh.D[0][pad(m)] = (start < 0 || (int32_t)m == start) ? 0.0 : __builtin_inf();
-    fill_costs(sh.cost[0], sh.lut, sh.z[2 * (rot % T)], sh.z[2 * (rot % T) + 1]);
+    fill_costs<P::CC>(sh.cost[0], sh.lut, sh.z[2 * (rot % T)], sh.z[2 * (rot % T) + 1]);
     __syncthreads();
     int cur = 0;
     for (uint32_t k = 0; k < T; ++k) {
@@ -167,7 +178,7 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
             const uint32_t u = tq * P::IPT + i;
             const uint32_t s = (L << KV) | (u << P::M);
             const uint32_t h = s * s + s;
-            cv[0][i] = cst[((h >> 6) & 0x3FEu) | (u >> (KV - 1))];
+            cv[0][i] = cst[(((h >> 6) & 0x3FEu) | (u >> (KV - 1))) * P::CC + cpy];
         }
 #pragma unroll
         for (uint32_t r = 0; r < P::BR; ++r) {
@@ -177,7 +188,7 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
                     const uint32_t u = tq * P::IPT + i;
                     const uint32_t s = (L << KV) | (u << P::M) | (r + 1);
                     const uint32_t h = s * s + s;
-                    cv[(r + 1) & 1][i] = cst[((h >> 6) & 0x3FEu) | (u >> (KV - 1))];
+                    cv[(r + 1) & 1][i] = cst[(((h >> 6) & 0x3FEu) | (u >> (KV - 1))) * P::CC + cpy];
                 }
             }
             const double dv = Dc[pad((L << KV) | r)];
@@ -200,7 +211,7 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
         store_bp<P::IPT>(bp + (uint64_t)k * P::S + tid * P::IPT, br);
         if (k + 1 < T) {
             const uint32_t t1 = (k + 1 + rot) % T;
-            fill_costs(sh.cost[(k + 1) & 1], sh.lut, sh.z[2 * t1], sh.z[2 * t1 + 1]);
+            fill_costs<P::CC>(sh.cost[(k + 1) & 1], sh.lut, sh.z[2 * t1], sh.z[2 * t1 + 1]);
         }
         __syncthreads();
         cur ^= 1;
