@@ -29,7 +29,8 @@
  *
  * Record layout (this library's choice): N/8 code bytes, then alpha as a
  * little-endian bf16; records packed back to back with no padding, record i
- * at byte offset i * cp_record_bytes(d, kv).
+ * at byte offset i * cp_record_bytes(d, kv) (a mixed-rate table packs records
+ * of different sizes; see cp_mixed_desc).
  *
  * Error convention: every call returns a cp_status; nothing aborts. A status
  * of CP_ERR_HIP keeps the HIP error code for cp_last_hip_error() (per
@@ -64,7 +65,7 @@ typedef struct cp_table cp_table; /* opaque; owned by the library */
 typedef enum {
     CP_OK = 0,
     CP_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, size mismatch, bad descriptor */
-    CP_ERR_UNSUPPORTED = 2,      /* (d, bits_per_step) has no compiled kernel */
+    CP_ERR_UNSUPPORTED = 2,      /* no kernel for the shape, or the call does not apply to this table */
     CP_ERR_OUT_OF_MEMORY = 3,    /* device or pinned host allocation failed */
     CP_ERR_HIP = 4,              /* a HIP runtime call failed; see cp_last_hip_error */
     CP_ERR_ID_OUT_OF_RANGE = 5   /* reported by cp_table_check: some id was outside [0, rows) */
