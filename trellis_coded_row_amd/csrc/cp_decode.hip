@@ -219,6 +219,7 @@ static hipError_t launch_one(const LaunchArgs &a)
     constexpr int CHUNK = (T::CHUNK / GROUPS > 0 ? T::CHUNK / GROUPS : 1) * GROUPS;
     const uint64_t nchunks = (a.n + CHUNK - 1) / CHUNK;
     uint64_t blocks = (nchunks + T::BLOCK / 64 - 1) / (T::BLOCK / 64);
+    if (blocks > 0x7FFFFFFFull) blocks = 0x7FFFFFFFull;  // the chunk loop strides over any excess
     if (T::BLOCKS_PER_CU > 0) {  // persistent grid: at most this many workgroups per CU
         const uint64_t cap = (uint64_t)T::BLOCKS_PER_CU * (a.num_cus > 0 ? a.num_cus : 256);
         if (blocks > cap) blocks = cap;

@@ -178,7 +178,8 @@ hipError_t launch_mixed_one(const MixedLaunchArgs &a)
     constexpr int GROUPS = 64 / (D / 8);
     constexpr int CHUNK = (CPK_CHUNK / GROUPS > 0 ? CPK_CHUNK / GROUPS : 1) * GROUPS;
     const uint64_t nchunks = (a.n + CHUNK - 1) / CHUNK;
-    const uint64_t blocks = (nchunks + BLOCK / 64 - 1) / (BLOCK / 64);
+    uint64_t blocks = (nchunks + BLOCK / 64 - 1) / (BLOCK / 64);
+    if (blocks > 0x7FFFFFFFull) blocks = 0x7FFFFFFFull;  // the chunk loop strides over any excess
     hipLaunchKernelGGL((gather_decode_mixed<D, RAW, BLOCK, CHUNK>), dim3((unsigned)blocks), dim3(BLOCK), 0,
                        a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err, a.index, a.rates);
     return hipGetLastError();
