@@ -142,8 +142,9 @@ cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, c
  * record with a few popcounts. cp_table_upload / cp_table_download /
  * cp_lookup_decode / cp_lookup_decode_raw / cp_table_check /
  * cp_table_destroy work as for single-rate tables (record ranges given by the
- * rows' own sizes); cp_table_describe reports bits_per_step = 0;
- * cp_lookup_decode_dedup and cp_table_encode return UNSUPPORTED.
+ * rows' own sizes); cp_table_encode codes each row at its own class's rate;
+ * cp_table_describe reports bits_per_step = 0; cp_lookup_decode_dedup returns
+ * UNSUPPORTED.
  * Errors: INVALID_ARGUMENT (NULL pointers, struct_size, rows == 0, nclass,
  * a class's rate without whole-byte records, a nonzero unused rate, a row
  * class >= nclass, residency or flags), UNSUPPORTED (no kernel for d or a
@@ -216,8 +217,9 @@ cp_status cp_table_download(const cp_table *table, uint64_t first_row, uint64_t 
 /* Device workspace bytes that cp_table_encode needs for nrows rows on this
  * table (0 for a NULL table or nrows == 0): one byte per trellis memory and
  * step, (d / 2) * 2^(16 - kv) bytes, for each row encoded concurrently (at
- * most one per resident 1024-thread workgroup). 1 MB per concurrent row at
- * d = 512, kv = 4. */
+ * most one per resident 1024-thread workgroup), 1 MB per concurrent row at
+ * d = 512, kv = 4; for a mixed-rate table the largest such need of its
+ * rates plus 12 bytes per row for the per-rate row lists. */
 uint64_t cp_encode_workspace_bytes(const cp_table *table, uint64_t nrows);
 
 /* Encodes rows e_j (fp32, device, row-major nrows x d) into records
@@ -236,12 +238,16 @@ uint64_t cp_encode_workspace_bytes(const cp_table *table, uint64_t nrows);
  *   workspace - device memory, 256-byte aligned, at least
  *               cp_encode_workspace_bytes(table, nrows) bytes, caller-owned
  *               scratch; calls sharing a workspace must not overlap.
- *   stream    - as in cp_lookup_decode. Asynchronous; no allocation.
+ *   stream    - as in cp_lookup_decode. Asynchronous, except that for a
+ *               mixed-rate table the call first copies its per-rate row lists
+ *               into the workspace on `stream` and waits for that copy; no
+ *               device allocation.
  * Lookups of the rows being encoded must not overlap the call.
  * Errors: INVALID_ARGUMENT (NULL table/rows/workspace, range beyond rows,
- * misaligned pointers, workspace too small), UNSUPPORTED (no encoder for the
- * shape, a mixed-rate table, or a table with hot-row copies: set those after
- * encoding), HIP. */
+ * misaligned pointers, workspace too small, more than 2^32 - 1 rows at once
+ * for a mixed-rate table), UNSUPPORTED (no encoder for the shape, or a table
+ * with hot-row copies: set those after encoding), OUT_OF_MEMORY (host lists
+ * of a mixed-rate table), HIP. */
 cp_status cp_table_encode(cp_table *table, uint64_t first_row, uint64_t nrows, const float *rows, void *workspace,
                           uint64_t workspace_bytes, void *stream);
 

@@ -89,17 +89,51 @@ def test_mixed_host_resident():
     t.close()
 
 
-def test_mixed_unsupported_paths():
+def test_mixed_dedup_is_unsupported():
     d, kvs = 64, (4, 3)
     cls = np.zeros(64, dtype=np.uint8)
     t = cp.MixedTable(d, kvs, cls, LUT)
-    assert t.dedup_workspace_bytes(10) == 0 and t.encode_workspace_bytes(10) == 0
+    assert t.dedup_workspace_bytes(10) == 0
     ids = torch.zeros(4, dtype=torch.int64, device="cuda")
     out = torch.empty((4, d), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
     assert cp.cp_lookup_decode_dedup(t.handle, ids.data_ptr(), 4, out.data_ptr(), ws.data_ptr(), 1 << 20,
                                      None) == cp.CP_ERR_UNSUPPORTED
-    rows = torch.zeros((4, d), dtype=torch.float32, device="cuda")
-    assert cp.cp_table_encode(t.handle, 0, 4, rows.data_ptr(), ws.data_ptr(), 1 << 20, None) == \
-        cp.CP_ERR_UNSUPPORTED
+    t.close()
+
+
+@pytest.mark.parametrize("d,kvs", [(64, (6, 5, 4, 3)), (128, (3, 5)), (512, (6, 4, 3))])
+def test_mixed_encode_matches_oracle(d, kvs):
+    """Rows encoded on the GPU into a mixed-rate table: each row's record equals
+    the oracle's heuristic encoding of that row at its own class's rate."""
+    rows = 301 if d < 512 else 37
+    rng = np.random.default_rng(d)
+    cls = rng.integers(0, len(kvs), size=rows).astype(np.uint8)
+    e = workload.gaussian_rows(rows, d, seed=500 + d).astype(np.float32)
+    e[3] = 0.0                                     # a zero row
+    say(f"mixed encode d={d} rates={kvs} rows={rows}")
+    exp_parts = [None] * rows
+    for c, kv in enumerate(kvs):
+        sel = np.nonzero(cls == c)[0]
+        if sel.size:
+            recs, _ = oracle.encode_rows(e[sel].astype(np.float64), d, kv, LUT, mode=oracle.ENC_HEURISTIC)
+            for k, r in enumerate(sel):
+                exp_parts[r] = recs[k]
+    exp = np.concatenate(exp_parts)
+    t = cp.MixedTable(d, kvs, cls, LUT)
+    t.upload_bytes(np.zeros(exp.size, dtype=np.uint8), 0, rows)
+    # two calls: rows [0, 120) then the rest, the second into a sub-range
+    dev = torch.from_numpy(e).cuda()
+    k = min(120, rows)
+    t.encode(dev[:k].contiguous(), first_row=0)
+    if k < rows:
+        t.encode(dev[k:].contiguous(), first_row=k)
+    got = t.download()
+    assert got.size == exp.size
+    if not (got == exp).all():
+        off = oracle.mixed_offsets(d, kvs, cls)
+        bad = [r for r in range(rows) if not (got[off[r]:off[r + 1]] == exp[off[r]:off[r + 1]]).all()]
+        raise AssertionError(f"{len(bad)} of {rows} records differ, first row {bad[0]} (class {cls[bad[0]]})")
+    # and the table decodes them like the oracle
+    check_mixed(t, d, kvs, cls, got, np.arange(rows, dtype=np.int64)[::-1].copy(), f"decode of encoded d{d}")
     t.close()

@@ -482,14 +482,41 @@ cp_status cp_table_download(const cp_table *t, uint64_t first_row, uint64_t nrow
     return e == hipSuccess ? CP_OK : hip_fail(e);
 }
 
+// Workspace of an encode call: for a mixed-rate table the per-class row lists
+// (input row index, record offset) come first, then the back-pointers (sized
+// for the largest need of any rate, each class being encoded in turn).
+struct EncodeLayout {
+    uint64_t src_row, dst_off, bp, total;
+};
+
+static hipError_t encode_layout(const cp_table *t, uint64_t nrows, EncodeLayout *L)
+{
+    uint64_t bp = 0;
+    const uint32_t nclass = t->mixed ? t->nclass : 1;
+    for (uint32_t c = 0; c < nclass; ++c) {
+        const uint32_t kv = t->mixed ? t->kv_of_class[c] : t->desc.bits_per_step;
+        uint32_t blocks = 0;
+        const hipError_t e = cpk::encode_grid(kv, t->num_cus, nrows, &blocks);
+        if (e != hipSuccess) return e;
+        const uint64_t need = (uint64_t)blocks * cpk::encode_workspace_per_block(t->desc.d, kv);
+        if (need > bp) bp = need;
+    }
+    auto up = [](uint64_t x) { return (x + 255) & ~(uint64_t)255; };
+    L->src_row = 0;
+    L->dst_off = t->mixed ? up(nrows * sizeof(uint32_t)) : 0;
+    L->bp = t->mixed ? L->dst_off + up(nrows * sizeof(uint64_t)) : 0;
+    L->total = L->bp + bp;
+    return hipSuccess;
+}
+
 uint64_t cp_encode_workspace_bytes(const cp_table *t, uint64_t nrows)
 {
-    if (!t || nrows == 0 || t->mixed) return 0;
+    if (!t || nrows == 0) return 0;
     DeviceGuard guard(t->device);
     if (guard.err != hipSuccess) return 0;
-    uint32_t blocks = 0;
-    if (cpk::encode_grid(t->desc.bits_per_step, t->num_cus, nrows, &blocks) != hipSuccess) return 0;
-    return (uint64_t)blocks * cpk::encode_workspace_per_block(t->desc.d, t->desc.bits_per_step);
+    EncodeLayout L;
+    if (encode_layout(t, nrows, &L) != hipSuccess) return 0;
+    return L.total;
 }
 
 cp_status cp_table_encode(cp_table *t, uint64_t first_row, uint64_t nrows, const float *rows, void *workspace,
@@ -499,29 +526,94 @@ cp_status cp_table_encode(cp_table *t, uint64_t first_row, uint64_t nrows, const
     if (nrows == 0) return CP_OK;
     if (!rows || ((uintptr_t)rows & 3u) || first_row > t->desc.rows || nrows > t->desc.rows - first_row)
         return CP_ERR_INVALID_ARGUMENT;
+    if (t->mixed && nrows > UINT32_MAX) return CP_ERR_INVALID_ARGUMENT;  // 32-bit row lists
     // a table with hot-row copies would need them refreshed after the kernel
-    if (t->mixed || t->hot_count || !cpk::encode_supported(t->desc.d, t->desc.bits_per_step))
-        return CP_ERR_UNSUPPORTED;
+    if (t->hot_count) return CP_ERR_UNSUPPORTED;
+    for (uint32_t c = 0; c < (t->mixed ? t->nclass : 1); ++c)
+        if (!cpk::encode_supported(t->desc.d, t->mixed ? t->kv_of_class[c] : t->desc.bits_per_step))
+            return CP_ERR_UNSUPPORTED;
     DeviceGuard guard(t->device);
     if (guard.err != hipSuccess) return hip_fail(guard.err);
-    uint32_t blocks = 0;
-    hipError_t e = cpk::encode_grid(t->desc.bits_per_step, t->num_cus, nrows, &blocks);
+    EncodeLayout L;
+    hipError_t e = encode_layout(t, nrows, &L);
     if (e != hipSuccess) return hip_fail(e);
-    const uint64_t need = (uint64_t)blocks * cpk::encode_workspace_per_block(t->desc.d, t->desc.bits_per_step);
-    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return CP_ERR_INVALID_ARGUMENT;
-    cpk::EncodeArgs a;
-    a.rows = rows;
-    a.nrows = nrows;
-    a.d = t->desc.d;
-    a.kv = t->desc.bits_per_step;
-    a.lut = t->lut_dev;
-    a.out = t->records_dev + first_row * t->record_bytes;
-    a.record_bytes = t->record_bytes;
-    a.workspace = static_cast<uint8_t *>(workspace);
-    a.blocks = blocks;
-    a.stream = (hipStream_t)stream;
-    e = cpk::encode(a);
-    return e == hipSuccess ? CP_OK : hip_fail(e);
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total) return CP_ERR_INVALID_ARGUMENT;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const hipStream_t st = (hipStream_t)stream;
+    if (!t->mixed) {
+        uint32_t blocks = 0;
+        e = cpk::encode_grid(t->desc.bits_per_step, t->num_cus, nrows, &blocks);
+        if (e != hipSuccess) return hip_fail(e);
+        cpk::EncodeArgs a;
+        a.rows = rows;
+        a.nrows = nrows;
+        a.d = t->desc.d;
+        a.kv = t->desc.bits_per_step;
+        a.lut = t->lut_dev;
+        a.out = t->records_dev + first_row * t->record_bytes;
+        a.record_bytes = t->record_bytes;
+        a.workspace = ws + L.bp;
+        a.blocks = blocks;
+        a.stream = st;
+        e = cpk::encode(a);
+        return e == hipSuccess ? CP_OK : hip_fail(e);
+    }
+    // mixed rates: the rows of each class, as (input row, record offset) lists
+    uint32_t *src = (uint32_t *)malloc(nrows * sizeof(uint32_t));
+    uint64_t *dst = (uint64_t *)malloc(nrows * sizeof(uint64_t));
+    uint8_t *cls = (uint8_t *)malloc(nrows);
+    if (!src || !dst || !cls) {
+        free(src);
+        free(dst);
+        free(cls);
+        return CP_ERR_OUT_OF_MEMORY;
+    }
+    uint64_t start[5] = {0, 0, 0, 0, 0};
+    for (uint64_t r = 0; r < nrows; ++r) {
+        uint32_t c = 0;
+        (void)cpk::mixed_record_offset(t->index_host, t->rates.R, first_row + r, &c);
+        cls[r] = (uint8_t)c;
+        ++start[c + 1];
+    }
+    for (uint32_t c = 1; c < 5; ++c) start[c] += start[c - 1];
+    uint64_t fill[4] = {start[0], start[1], start[2], start[3]};
+    for (uint64_t r = 0; r < nrows; ++r) {
+        const uint64_t k = fill[cls[r]]++;
+        src[k] = (uint32_t)r;
+        dst[k] = cpk::mixed_record_offset(t->index_host, t->rates.R, first_row + r, nullptr);
+    }
+    free(cls);
+    // the lists land on the stream before the kernels; the host copies are freed
+    // once they have
+    e = hipMemcpyAsync(ws + L.src_row, src, nrows * sizeof(uint32_t), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(ws + L.dst_off, dst, nrows * sizeof(uint64_t), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    free(src);
+    free(dst);
+    if (e != hipSuccess) return hip_fail(e);
+    for (uint32_t c = 0; c < t->nclass; ++c) {
+        const uint64_t cnt = start[c + 1] - start[c];
+        if (cnt == 0) continue;
+        uint32_t blocks = 0;
+        e = cpk::encode_grid(t->kv_of_class[c], t->num_cus, cnt, &blocks);
+        if (e != hipSuccess) return hip_fail(e);
+        cpk::EncodeArgs a;
+        a.rows = rows;
+        a.nrows = cnt;
+        a.d = t->desc.d;
+        a.kv = t->kv_of_class[c];
+        a.lut = t->lut_dev;
+        a.out = t->records_dev;
+        a.record_bytes = t->rates.R[c];
+        a.workspace = ws + L.bp;
+        a.blocks = blocks;
+        a.stream = st;
+        a.src_row = reinterpret_cast<const uint32_t *>(ws + L.src_row) + start[c];
+        a.dst_off = reinterpret_cast<const uint64_t *>(ws + L.dst_off) + start[c];
+        e = cpk::encode(a);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    return CP_OK;
 }
 
 cp_status cp_table_check(cp_table *t, void *stream)

@@ -264,11 +264,17 @@ __device__ __forceinline__ uint32_t argmin_memory(Shared<KV> &sh, const double *
     return r;
 }
 
+// Rows row = 0 .. nrows-1 of the launch; with src_row / dst_off (a
+// mixed-rate table, one launch per rate class) row `row` reads input row
+// src_row[row] and writes the record at byte dst_off[row] of `out`, else it
+// reads input row `row` and writes record `row`.
 template <int KV>
 __global__ __launch_bounds__(kThreads) void tcq_encode_rows(const float *__restrict__ e, uint64_t nrows,
                                                             uint32_t d, const uint32_t *__restrict__ lut,
                                                             uint8_t *__restrict__ out, uint64_t record_bytes,
-                                                            uint8_t *__restrict__ workspace)
+                                                            uint8_t *__restrict__ workspace,
+                                                            const uint32_t *__restrict__ src_row,
+                                                            const uint64_t *__restrict__ dst_off)
 {
     using P = Tcq<KV>;
     __shared__ Shared<KV> sh;
@@ -278,8 +284,8 @@ __global__ __launch_bounds__(kThreads) void tcq_encode_rows(const float *__restr
     if (tid < 512) sh.lut[tid] = lut[tid];
 
     for (uint64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
-        const float *er = e + row * d;
-        uint8_t *rec = out + row * record_bytes;
+        const float *er = e + (src_row ? (uint64_t)src_row[row] : row) * d;
+        uint8_t *rec = out + (dst_off ? dst_off[row] : row * record_bytes);
         for (uint32_t b = tid; b < NB + 2; b += kThreads) sh.code[b] = 0;
         if (tid == 0) {
             double n2 = 0.0;
@@ -403,19 +409,19 @@ hipError_t encode(const EncodeArgs &a)
     switch (a.kv) {
     case 3:
         hipLaunchKernelGGL(tcq_encode_rows<3>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
-                           a.lut, a.out, a.record_bytes, a.workspace);
+                           a.lut, a.out, a.record_bytes, a.workspace, a.src_row, a.dst_off);
         break;
     case 4:
         hipLaunchKernelGGL(tcq_encode_rows<4>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
-                           a.lut, a.out, a.record_bytes, a.workspace);
+                           a.lut, a.out, a.record_bytes, a.workspace, a.src_row, a.dst_off);
         break;
     case 5:
         hipLaunchKernelGGL(tcq_encode_rows<5>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
-                           a.lut, a.out, a.record_bytes, a.workspace);
+                           a.lut, a.out, a.record_bytes, a.workspace, a.src_row, a.dst_off);
         break;
     case 6:
         hipLaunchKernelGGL(tcq_encode_rows<6>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
-                           a.lut, a.out, a.record_bytes, a.workspace);
+                           a.lut, a.out, a.record_bytes, a.workspace, a.src_row, a.dst_off);
         break;
     default:
         return hipErrorInvalidValue;

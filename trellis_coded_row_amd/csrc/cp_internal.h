@@ -67,6 +67,10 @@ struct EncodeArgs {
     uint8_t *workspace;        // blocks * encode_workspace_per_block(d, kv) bytes
     uint32_t blocks;           // from encode_grid
     hipStream_t stream;
+    // mixed-rate tables: launch row r reads input row src_row[r] and writes
+    // the record at byte dst_off[r] of out (device arrays; null: identity)
+    const uint32_t *src_row = nullptr;
+    const uint64_t *dst_off = nullptr;
 };
 
 bool encode_supported(uint32_t d, uint32_t kv);
