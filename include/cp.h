@@ -219,7 +219,8 @@ cp_status cp_table_download(const cp_table *table, uint64_t first_row, uint64_t 
  * step, (d / 2) * 2^(16 - kv) bytes, for each row encoded concurrently (at
  * most one per resident 1024-thread workgroup), 1 MB per concurrent row at
  * d = 512, kv = 4; for a mixed-rate table the largest such need of its
- * rates plus 12 bytes per row for the per-rate row lists. */
+ * rates plus, per row, 12 bytes of row lists, a staged copy of the input row
+ * (4d bytes) and a staged record. */
 uint64_t cp_encode_workspace_bytes(const cp_table *table, uint64_t nrows);
 
 /* Encodes rows e_j (fp32, device, row-major nrows x d) into records

@@ -486,7 +486,7 @@ cp_status cp_table_download(const cp_table *t, uint64_t first_row, uint64_t nrow
 // (input row index, record offset) come first, then the back-pointers (sized
 // for the largest need of any rate, each class being encoded in turn).
 struct EncodeLayout {
-    uint64_t src_row, dst_off, bp, total;
+    uint64_t src_row, dst_off, staged_rows, staged_recs, bp, total;
 };
 
 static hipError_t encode_layout(const cp_table *t, uint64_t nrows, EncodeLayout *L)
@@ -502,9 +502,13 @@ static hipError_t encode_layout(const cp_table *t, uint64_t nrows, EncodeLayout 
         if (need > bp) bp = need;
     }
     auto up = [](uint64_t x) { return (x + 255) & ~(uint64_t)255; };
+    uint64_t rmax = 0;
+    for (uint32_t c = 0; c < nclass && t->mixed; ++c) rmax = t->rates.R[c] > rmax ? t->rates.R[c] : rmax;
     L->src_row = 0;
     L->dst_off = t->mixed ? up(nrows * sizeof(uint32_t)) : 0;
-    L->bp = t->mixed ? L->dst_off + up(nrows * sizeof(uint64_t)) : 0;
+    L->staged_rows = t->mixed ? L->dst_off + up(nrows * sizeof(uint64_t)) : 0;
+    L->staged_recs = t->mixed ? L->staged_rows + up(nrows * t->desc.d * sizeof(float)) : 0;
+    L->bp = t->mixed ? L->staged_recs + up(nrows * rmax) : 0;
     L->total = L->bp + bp;
     return hipSuccess;
 }
@@ -608,9 +612,9 @@ cp_status cp_table_encode(cp_table *t, uint64_t first_row, uint64_t nrows, const
         a.workspace = ws + L.bp;
         a.blocks = blocks;
         a.stream = st;
-        a.src_row = reinterpret_cast<const uint32_t *>(ws + L.src_row) + start[c];
-        a.dst_off = reinterpret_cast<const uint64_t *>(ws + L.dst_off) + start[c];
-        e = cpk::encode(a);
+        e = cpk::encode_listed(a, reinterpret_cast<const uint32_t *>(ws + L.src_row) + start[c],
+                               reinterpret_cast<const uint64_t *>(ws + L.dst_off) + start[c],
+                               reinterpret_cast<float *>(ws + L.staged_rows), ws + L.staged_recs);
         if (e != hipSuccess) return hip_fail(e);
     }
     return CP_OK;

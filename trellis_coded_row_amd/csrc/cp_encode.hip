@@ -264,17 +264,11 @@ __device__ __forceinline__ uint32_t argmin_memory(Shared<KV> &sh, const double *
     return r;
 }
 
-// Rows row = 0 .. nrows-1 of the launch; with src_row / dst_off (a
-// mixed-rate table, one launch per rate class) row `row` reads input row
-// src_row[row] and writes the record at byte dst_off[row] of `out`, else it
-// reads input row `row` and writes record `row`.
 template <int KV>
 __global__ __launch_bounds__(kThreads) void tcq_encode_rows(const float *__restrict__ e, uint64_t nrows,
                                                             uint32_t d, const uint32_t *__restrict__ lut,
                                                             uint8_t *__restrict__ out, uint64_t record_bytes,
-                                                            uint8_t *__restrict__ workspace,
-                                                            const uint32_t *__restrict__ src_row,
-                                                            const uint64_t *__restrict__ dst_off)
+                                                            uint8_t *__restrict__ workspace)
 {
     using P = Tcq<KV>;
     __shared__ Shared<KV> sh;
@@ -284,8 +278,8 @@ __global__ __launch_bounds__(kThreads) void tcq_encode_rows(const float *__restr
     if (tid < 512) sh.lut[tid] = lut[tid];
 
     for (uint64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
-        const float *er = e + (src_row ? (uint64_t)src_row[row] : row) * d;
-        uint8_t *rec = out + (dst_off ? dst_off[row] : row * record_bytes);
+        const float *er = e + row * d;
+        uint8_t *rec = out + row * record_bytes;
         for (uint32_t b = tid; b < NB + 2; b += kThreads) sh.code[b] = 0;
         if (tid == 0) {
             double n2 = 0.0;
@@ -409,23 +403,69 @@ hipError_t encode(const EncodeArgs &a)
     switch (a.kv) {
     case 3:
         hipLaunchKernelGGL(tcq_encode_rows<3>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
-                           a.lut, a.out, a.record_bytes, a.workspace, a.src_row, a.dst_off);
+                           a.lut, a.out, a.record_bytes, a.workspace);
         break;
     case 4:
         hipLaunchKernelGGL(tcq_encode_rows<4>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
-                           a.lut, a.out, a.record_bytes, a.workspace, a.src_row, a.dst_off);
+                           a.lut, a.out, a.record_bytes, a.workspace);
         break;
     case 5:
         hipLaunchKernelGGL(tcq_encode_rows<5>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
-                           a.lut, a.out, a.record_bytes, a.workspace, a.src_row, a.dst_off);
+                           a.lut, a.out, a.record_bytes, a.workspace);
         break;
     case 6:
         hipLaunchKernelGGL(tcq_encode_rows<6>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
-                           a.lut, a.out, a.record_bytes, a.workspace, a.src_row, a.dst_off);
+                           a.lut, a.out, a.record_bytes, a.workspace);
         break;
     default:
         return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+// Copy kernels for encoding into a mixed-rate table: the rows of one rate
+// class are gathered into a contiguous batch, encoded by the kernel above into
+// contiguous records, and the records scattered to their offsets (the encode
+// kernel itself stays as it is measured fastest).
+__global__ void gather_rows(const float *__restrict__ e, const uint32_t *__restrict__ src_row, uint64_t n,
+                            uint32_t d, float *__restrict__ staged)
+{
+    const uint64_t total = n * d;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        staged[i] = e[(uint64_t)src_row[i / d] * d + i % d];
+}
+
+__global__ void scatter_records(const uint8_t *__restrict__ staged, uint64_t record_bytes,
+                                const uint64_t *__restrict__ dst_off, uint64_t n, uint8_t *__restrict__ out)
+{
+    const uint64_t total = n * record_bytes;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        out[dst_off[i / record_bytes] + i % record_bytes] = staged[i];
+}
+
+static unsigned copy_grid(uint64_t items)
+{
+    const uint64_t b = (items + 255) / 256;
+    return (unsigned)(b < 1 ? 1 : (b > 65536 ? 65536 : b));
+}
+
+hipError_t encode_listed(const EncodeArgs &a, const uint32_t *src_row, const uint64_t *dst_off, float *staged_rows,
+                         uint8_t *staged_recs)
+{
+    if (a.nrows == 0 || a.blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_rows, dim3(copy_grid(a.nrows * a.d)), dim3(256), 0, a.stream, a.rows, src_row,
+                       a.nrows, a.d, staged_rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    EncodeArgs b = a;
+    b.rows = staged_rows;
+    b.out = staged_recs;
+    e = encode(b);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scatter_records, dim3(copy_grid(a.nrows * a.record_bytes)), dim3(256), 0, a.stream,
+                       staged_recs, a.record_bytes, dst_off, a.nrows, a.out);
     return hipGetLastError();
 }
 

@@ -67,10 +67,6 @@ struct EncodeArgs {
     uint8_t *workspace;        // blocks * encode_workspace_per_block(d, kv) bytes
     uint32_t blocks;           // from encode_grid
     hipStream_t stream;
-    // mixed-rate tables: launch row r reads input row src_row[r] and writes
-    // the record at byte dst_off[r] of out (device arrays; null: identity)
-    const uint32_t *src_row = nullptr;
-    const uint64_t *dst_off = nullptr;
 };
 
 bool encode_supported(uint32_t d, uint32_t kv);
@@ -79,6 +75,11 @@ hipError_t encode_grid(uint32_t kv, int num_cus, uint64_t nrows, uint32_t *block
 // Back-pointer bytes per workgroup: (d / 2) steps * 2^(16 - kv) memories.
 uint64_t encode_workspace_per_block(uint32_t d, uint32_t kv);
 hipError_t encode(const EncodeArgs &a);
+// Mixed-rate tables: encodes input rows src_row[0..nrows) (of a.rows) at a.kv
+// and writes record r at byte dst_off[r] of a.out, through staging buffers of
+// nrows * d floats and nrows * record_bytes bytes (device, caller workspace).
+hipError_t encode_listed(const EncodeArgs &a, const uint32_t *src_row, const uint64_t *dst_off, float *staged_rows,
+                         uint8_t *staged_recs);
 
 // Mixed-rate tables (see cp_mixed.hip): one index entry per 32 rows.
 struct alignas(16) MixedEntry {
