@@ -251,7 +251,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "multi-GPU runs are not part of this build", file=sys.stderr)
+              "the lookup is measured on one GPU's share of the table", file=sys.stderr)
         return 2
 
     import numpy as np
