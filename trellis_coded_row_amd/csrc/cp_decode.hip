@@ -68,7 +68,6 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     static_assert(CHUNK <= 64 && CI >= 1 && CI * GROUPS == CHUNK, "one id per lane per chunk");
 
     __shared__ __attribute__((aligned(16))) uint32_t s_lut[kLdsLutWords];
-    stage_lut<BLOCK>(s_lut, lut);
 
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t l = lane % LANES;
@@ -94,7 +93,10 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
         const uint64_t j = row_of(c, lane);
         return (c < nchunks && lane < CHUNK && j < n) ? ids[j] : 0;
     };
+    // the first chunk's ids are requested before the codebook is staged, so
+    // the two loads' latencies overlap (what a small batch waits for)
     int64_t my_id = load_id(wave);
+    stage_lut<BLOCK>(s_lut, lut);
     for (uint64_t c = wave; c < nchunks; c += waves) {
         // rows in this chunk
         uint32_t cn = __builtin_amdgcn_readfirstlane((uint32_t)((n - c * CHUNK) < CHUNK ? (n - c * CHUNK) : CHUNK));

@@ -79,7 +79,6 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
     static_assert(CHUNK <= 64 && CI >= 1 && CI * GROUPS == CHUNK, "one id per lane per chunk");
 
     __shared__ __attribute__((aligned(16))) uint32_t s_lut[kLdsLutWords];
-    stage_lut<BLOCK>(s_lut, lut);
 
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t l = lane % LANES;
@@ -101,8 +100,11 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
     auto entry_of = [&](int64_t id) -> MixedEntry {
         return index[((uint64_t)id < rows ? (uint64_t)id : 0) >> 5];
     };
+    // the first chunk's ids and index entries are requested before the
+    // codebook is staged, so their latencies overlap
     int64_t my_id = load_id(wave);
     MixedEntry e = entry_of(my_id);
+    stage_lut<BLOCK>(s_lut, lut);
     for (uint64_t c = wave; c < nchunks; c += waves) {
         uint32_t cn = __builtin_amdgcn_readfirstlane((uint32_t)((n - c * CHUNK) < CHUNK ? (n - c * CHUNK) : CHUNK));
         asm volatile("" : "+s"(cn));
