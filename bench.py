@@ -102,6 +102,75 @@ def time_each(fn, steps: int, torch, before=None) -> list[float]:
     return out
 
 
+def graph_timing(step, out, steps: int, torch, per_graph: int = 16) -> dict:
+    """Per-lookup ms when `per_graph` lookups are captured in one HIP graph
+    and the graph is replayed (no host launch cost per lookup). Every check
+    replay is compared bit for bit with the eager result, with eager work and
+    a synchronisation between replays."""
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            step()
+    same = 0
+    checks = 4
+    for _ in range(checks):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same += int(torch.equal(out.view(torch.int16), ref.view(torch.int16)))
+    reps = max(2, steps // per_graph)
+    for _ in range(2):
+        g.replay()
+    ms = time_region(g.replay, reps, torch)
+    del g
+    return {"lookups_per_graph": per_graph, "replays": reps, "launch_ms_mean": ms / (reps * per_graph),
+            "replays_matching_eager": f"{same}/{checks}"}
+
+
+def batch_scan(table, ids_np, d: int, bytes_per_lookup: float, torch, np) -> dict:
+    """ms per launch for batches of growing size (the replay's ids tiled),
+    launched one by one and replayed from a captured graph (device time
+    without the host's launch cost), and the marginal rate between the two
+    largest: what one more lookup costs once the launch's fixed start-up and
+    drain are paid."""
+    sizes = [96, 1536, 12288, 49152, 98304, 196608, 393216, 786432, 1572864]
+    rows = []
+    for n in sizes:
+        reps = -(-n // len(ids_np))
+        ids = torch.from_numpy(np.tile(ids_np, reps)[:n]).cuda()
+        out = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+        step = lambda: table.lookup_decode(ids, out)
+        for _ in range(20):
+            step()
+        steps = max(20, min(400, int(4e7 // n)))
+        ms = time_region(step, steps, torch) / steps
+        g = graph_timing(step, out, steps, torch, per_graph=8)
+        if not g["replays_matching_eager"].startswith("4/"):
+            raise RuntimeError(f"a graph replay differs from the eager lookup at n = {n}")
+        gms = g["launch_ms_mean"]
+        rows.append({"n": n, "launch_ms": ms, "graph_launch_ms": gms,
+                     "effective_GBps": n * bytes_per_lookup / (ms / 1e3) / 1e9,
+                     "graph_effective_GBps": n * bytes_per_lookup / (gms / 1e3) / 1e9})
+        del ids, out
+    a, b = rows[-2], rows[-1]
+    marg_s = (b["launch_ms"] - a["launch_ms"]) / 1e3 / (b["n"] - a["n"])
+    fixed_ms = a["launch_ms"] - a["n"] * marg_s * 1e3
+    torch.cuda.empty_cache()
+    return {"points": rows, "marginal_rows_per_s": 1.0 / marg_s,
+            "marginal_effective_GBps": bytes_per_lookup / marg_s / 1e9,
+            "marginal_pct_hbm_peak": 100.0 * bytes_per_lookup / marg_s / 1e9 / HBM_PEAK_GBPS,
+            "fixed_ms_per_launch": fixed_ms}
+
+
 def probes(torch, mib: int = 1024) -> dict:
     """Achievable HBM bandwidth of a plain copy and a plain fill (torch's own
     kernels) of `mib` MiB, for context next to the 8 TB/s peak."""
@@ -244,6 +313,10 @@ def main() -> int:
     ap.add_argument("--encode-rows", type=int, default=4096)
     ap.add_argument("--encode-d", type=int, default=512)
     ap.add_argument("--encode-kv", type=int, default=4)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time lookups replayed from a captured HIP graph (no host launch cost per lookup)")
+    ap.add_argument("--batch-scan", action="store_true",
+                    help="also time batches of 96 .. 1,572,864 ids (the replay tiled) and report the marginal rate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     args = ap.parse_args()
@@ -418,6 +491,16 @@ def main() -> int:
     if args.extra or args.probes:
         res["probes"] = probes(torch)
 
+    if args.graph:
+        res["graph"] = graph_timing(step, out, args.steps, torch)
+        if not res["graph"]["replays_matching_eager"].startswith("4/"):
+            print("a graph replay differs from the eager lookup", file=sys.stderr)
+            return 1
+    if args.batch_scan:
+        if mixed or args.dedup:
+            print("--batch-scan times the single-rate cp_lookup_decode only", file=sys.stderr)
+            return 2
+        res["batch_scan"] = batch_scan(table, ids_np, cfg.d, algo_bytes / n, torch, np)
     if not args.no_cpu_baseline:
         import oracle  # CPU baseline leg only
 

@@ -19,6 +19,15 @@ import trellis_coded_row_amd as cp
 BF16_REL = 2.0 ** -8
 
 
+def shape_change_sizes() -> list[int]:
+    """Batch sizes just below, at and above the two sizes where the lookup
+    launch moves to longer wave chunks (1 -> 4 rows at 32 lookups per compute
+    unit, 4 -> 16 at 128 per compute unit), with ragged tails."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    b4, b16 = 32 * cus, 128 * cus
+    return [b4 - 1, b4, b4 + 37, b16 - 1, b16, b16 + 1001]
+
+
 def say(msg: str) -> None:
     print(f"[gpu-case] {msg}", flush=True)
     sys.stdout.flush()

@@ -9,7 +9,7 @@ import torch
 
 import trellis_coded_row_amd as cp
 import workload
-from parity import check_lookup, make_table, say
+from parity import check_lookup, make_table, say, shape_change_sizes
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,20 @@ def test_hot_rows_give_the_same_rows(d, kv):
     # dropping the copies changes nothing either
     assert t.set_hot_rows([]) == 0
     check_lookup(t, LUT, recs, d, kv, ids[:2000], f"hot rows dropped d{d} kv{kv}")
+    t.close()
+
+
+@pytest.mark.parametrize("d,kv", [(256, 4), (512, 4)])
+def test_hot_rows_at_every_launch_shape(d, kv):
+    rows = 9_001
+    recs = workload.random_records(rows, d, kv, seed=40 + d)
+    t = make_table(LUT, recs, d, kv, residency=cp.CP_RESIDENCY_HOST_MAPPED)
+    rng = np.random.default_rng(d)
+    assert t.set_hot_rows(rng.choice(rows, size=1_500, replace=False)) == 1_500
+    for n in shape_change_sizes():
+        ids = rng.integers(0, rows, n, dtype=np.int64)
+        ids[n // 2] = rows + 1
+        check_lookup(t, LUT, recs, d, kv, ids, f"hot rows d{d} kv{kv} n{n}", expect_bad=1)
     t.close()
 
 

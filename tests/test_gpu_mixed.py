@@ -10,7 +10,7 @@ import torch
 import oracle
 import trellis_coded_row_amd as cp
 import workload
-from parity import assert_bf16_within_ulp, assert_bit_exact, device_lookup, say
+from parity import assert_bf16_within_ulp, assert_bit_exact, device_lookup, say, shape_change_sizes
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +62,21 @@ def test_mixed_lookup_matches_oracle(d, kvs):
                 expect_bad=int(((bad < 0) | (bad >= rows)).sum()))
     st, desc = cp.cp_table_describe_mixed(t.handle)
     assert st == cp.CP_OK and desc.nclass == len(kvs) and list(desc.bits_per_step)[:len(kvs)] == list(kvs)
+    t.close()
+
+
+@pytest.mark.parametrize("d", [128, 512])
+def test_mixed_at_every_launch_shape(d):
+    kvs = (6, 4, 3)
+    rows = 6007
+    rng = np.random.default_rng(d + 1)
+    cls = rng.integers(0, len(kvs), size=rows).astype(np.uint8)
+    packed = workload.random_mixed_records(d, kvs, cls, seed=d + 21)
+    t = make_mixed(d, kvs, cls, packed)
+    for n in shape_change_sizes():
+        ids = rng.integers(0, rows, n).astype(np.int64)
+        ids[1] = -1
+        check_mixed(t, d, kvs, cls, packed, ids, f"mixed d{d} n{n}", expect_bad=1)
     t.close()
 
 

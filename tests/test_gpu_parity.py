@@ -10,7 +10,7 @@ import torch
 import oracle
 import trellis_coded_row_amd as cp
 import workload
-from parity import assert_bf16_within_ulp, check_lookup, device_lookup, make_table, say
+from parity import assert_bf16_within_ulp, check_lookup, device_lookup, make_table, say, shape_change_sizes
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,26 @@ def test_every_instance_ragged_batches(d, kv):
         for n in (1, 2, 7, 64, 1000, 4099):
             ids = rng.integers(0, rows, n, dtype=np.int64)
             check_lookup(t, LUT, recs, d, kv, ids, f"d{d} kv{kv} n{n}")
+    finally:
+        t.close()
+
+
+@pytest.mark.parametrize("d,kv", [(64, 4), (128, 5), (256, 3), (512, 4), (512, 6)])
+def test_batch_sizes_around_launch_shape_changes(d, kv):
+    # the launch picks 1-, 4- or 16-lookup wave chunks by batch size: every
+    # shape, at its edges and with ragged tails, against the oracle (with a
+    # few ids outside the table in each batch); the dedup path at one size
+    rows = 5003
+    recs = workload.random_records(rows, d, kv, seed=800 + d + kv)
+    t = make_table(LUT, recs, d, kv)
+    rng = np.random.default_rng(d + kv)
+    try:
+        for n in shape_change_sizes():
+            ids = rng.integers(0, rows, n, dtype=np.int64)
+            ids[n // 3] = rows
+            ids[-1] = -5
+            check_lookup(t, LUT, recs, d, kv, ids, f"d{d} kv{kv} n{n}", expect_bad=2,
+                         dedup=(n == shape_change_sizes()[2]))
     finally:
         t.close()
 

@@ -379,6 +379,7 @@ static cp_status lookup(const cp_table *t, const int64_t *ids, uint64_t n, uint1
         m.err = t->err_dev;
         m.index = t->index_dev;
         m.rates = t->rates;
+        m.num_cus = t->num_cus;
         m.stream = (hipStream_t)stream;
         hipError_t e = cpk::launch_mixed(t->desc.d, raw, m);
         return e == hipSuccess ? CP_OK : hip_fail(e);

@@ -31,7 +31,8 @@
 //   - a wave takes a chunk of consecutive lookups: one load brings all their
 //     ids (one per lane), then every record of the chunk is requested before
 //     any is decoded and the next chunk's ids are requested before decoding,
-//     so a whole chunk of record loads is in flight per wave;
+//     so a whole chunk of record loads is in flight per wave; chunks hold 16
+//     lookups for batches that fill the chip, and 4 or 1 for smaller ones;
 //   - the scale, the window hash and the fp16 -> fp32 widening run on the
 //     scalar unit, v_mad_u32_u24 and v_fma_mix_f32 respectively;
 //   - outputs are written with nontemporal stores: they are not re-read, and
@@ -201,9 +202,10 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
 
 // Launch shape (measured on MI355X, d = 512 replay): the codebook in LDS as
 // 16 copies x 2 signs (64 KB) in 1024-thread workgroups (2 per CU = 32
-// waves); one wave
-// holds a chunk of 16 lookups; the grid covers all chunks (no persistent cap),
-// which balances the tail better than a fixed number of workgroups per CU.
+// waves); one wave holds a chunk of up to 16 lookups (fewer for small
+// batches, lookup_chunk_rows); the grid covers all chunks (no persistent
+// cap), which balances the tail better than a fixed number of workgroups
+// per CU.
 template <int D, int KV>
 struct Tune {
     static constexpr int COPIES = CPK_COPIES;
@@ -212,13 +214,13 @@ struct Tune {
     static constexpr int CHUNK = CPK_CHUNK;
 };
 
-template <int D, int KV, bool RAW, bool HOT>
-static hipError_t launch_one(const LaunchArgs &a)
+template <int D, int KV, bool RAW, bool HOT, int CHUNK_ROWS>
+static hipError_t launch_shape(const LaunchArgs &a)
 {
     using T = Tune<D, KV>;
     constexpr int GROUPS = 64 / (D / 8);
     // lookups per wave chunk: a multiple of the rows decoded side by side, <= 64
-    constexpr int CHUNK = (T::CHUNK / GROUPS > 0 ? T::CHUNK / GROUPS : 1) * GROUPS;
+    constexpr int CHUNK = (CHUNK_ROWS / GROUPS > 0 ? CHUNK_ROWS / GROUPS : 1) * GROUPS;
     const uint64_t nchunks = (a.n + CHUNK - 1) / CHUNK;
     uint64_t blocks = (nchunks + T::BLOCK / 64 - 1) / (T::BLOCK / 64);
     if (blocks > 0x7FFFFFFFull) blocks = 0x7FFFFFFFull;  // the chunk loop strides over any excess
@@ -230,6 +232,16 @@ static hipError_t launch_one(const LaunchArgs &a)
                        dim3(T::BLOCK), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err,
                        a.by_offset, a.hot_index, a.host_off0, a.hot_off0);
     return hipGetLastError();
+}
+
+template <int D, int KV, bool RAW, bool HOT>
+static hipError_t launch_one(const LaunchArgs &a)
+{
+    switch (lookup_chunk_rows(a.n, a.num_cus)) {
+    case 1: return launch_shape<D, KV, RAW, HOT, 1>(a);
+    case 4: return launch_shape<D, KV, RAW, HOT, 4>(a);
+    default: return launch_shape<D, KV, RAW, HOT, Tune<D, KV>::CHUNK>(a);
+    }
 }
 
 typedef hipError_t (*launch_fn)(const LaunchArgs &);

@@ -13,6 +13,21 @@ struct alignas(8) HotEntry {
     uint32_t bits;  // bit j: row 32b + j has a copy in the cache
 };
 
+// Rows per wave chunk for a batch of n lookups on a device with num_cus
+// compute units: the largest of 16, 4 and 1 rows that still gives the batch
+// at least 8 waves per CU. A wave decodes its chunk's rows one after another
+// behind one round of record loads, so long chunks suit batches that fill the
+// chip (fewer id loads and codebook stagings per row), and short ones let a
+// small batch (one decode step: tens to thousands of ids) spread over more
+// waves and finish sooner.
+inline int lookup_chunk_rows(uint64_t n, int num_cus)
+{
+    const uint64_t waves = (uint64_t)(num_cus > 0 ? num_cus : 256) * 8u;
+    if (n >= 16u * waves) return 16;
+    if (n >= 4u * waves) return 4;
+    return 1;
+}
+
 // Launch parameters of one gather-decode call.
 struct LaunchArgs {
     const uint8_t *records;   // device-accessible base of the packed records
@@ -103,6 +118,7 @@ struct MixedLaunchArgs {
     int *err;
     const MixedEntry *index;  // device
     MixedRates rates;
+    int num_cus;             // compute units of the device
     hipStream_t stream;
 };
 

@@ -173,18 +173,29 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
     if (bad) atomicOr(err, 1);
 }
 
-template <int D, bool RAW>
-hipError_t launch_mixed_one(const MixedLaunchArgs &a)
+template <int D, bool RAW, int CHUNK_ROWS>
+hipError_t launch_mixed_shape(const MixedLaunchArgs &a)
 {
     constexpr int BLOCK = CPK_BLOCK;
     constexpr int GROUPS = 64 / (D / 8);
-    constexpr int CHUNK = (CPK_CHUNK / GROUPS > 0 ? CPK_CHUNK / GROUPS : 1) * GROUPS;
+    constexpr int CHUNK = (CHUNK_ROWS / GROUPS > 0 ? CHUNK_ROWS / GROUPS : 1) * GROUPS;
     const uint64_t nchunks = (a.n + CHUNK - 1) / CHUNK;
     uint64_t blocks = (nchunks + BLOCK / 64 - 1) / (BLOCK / 64);
     if (blocks > 0x7FFFFFFFull) blocks = 0x7FFFFFFFull;  // the chunk loop strides over any excess
     hipLaunchKernelGGL((gather_decode_mixed<D, RAW, BLOCK, CHUNK>), dim3((unsigned)blocks), dim3(BLOCK), 0,
                        a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err, a.index, a.rates);
     return hipGetLastError();
+}
+
+// chunk length by batch size, as for single-rate tables (lookup_chunk_rows)
+template <int D, bool RAW>
+hipError_t launch_mixed_one(const MixedLaunchArgs &a)
+{
+    switch (lookup_chunk_rows(a.n, a.num_cus)) {
+    case 1: return launch_mixed_shape<D, RAW, 1>(a);
+    case 4: return launch_mixed_shape<D, RAW, 4>(a);
+    default: return launch_mixed_shape<D, RAW, CPK_CHUNK>(a);
+    }
 }
 
 }  // namespace
