@@ -305,7 +305,7 @@ def main() -> int:
     ap.add_argument("--hot-share", type=float, default=0.0,
                     help="host_d512: keep device copies of this share of the rows, the most looked-up first")
     ap.add_argument("--flushed", action="store_true",
-                    help="also time launches with L2/MALL flushed (512 MiB written) before each")
+                    help="also time launches with L2/MALL flushed before each (512 MiB read; and 512 MiB written)")
     ap.add_argument("--probes", action="store_true", help="also run 1 GiB copy and fill probes")
     ap.add_argument("--extra", action="store_true", help="--flushed and --probes")
     ap.add_argument("--encode", action="store_true",
@@ -480,13 +480,25 @@ def main() -> int:
     }
 
     if args.extra or args.flushed:
-        flush = torch.empty(512 << 18, dtype=torch.int32, device="cuda")  # 512 MiB > L2 + MALL
-        per = time_each(step, max(5, args.steps // 2), torch, before=lambda: flush.fill_(0))
+        # 512 MiB > L2 + MALL. A read of it leaves the caches holding clean
+        # lines of the flush buffer (cold records, nothing to write back); a
+        # write of it leaves dirty lines, whose write-back then competes with
+        # the lookup's own traffic (as after a layer that wrote its output).
+        flush = torch.empty(512 << 18, dtype=torch.int32, device="cuda")
+        flush.fill_(1)
+        sink = torch.empty((), dtype=torch.int64, device="cuda")
+        reps = max(5, args.steps // 2)
+        per = time_each(step, reps, torch, before=lambda: torch.sum(flush, 0, dtype=torch.int64, out=sink))
         flushed_ms = sum(per) / len(per)
         res["flushed_launch_ms_mean"] = flushed_ms
         res["flushed_rows_per_s"] = n / (flushed_ms / 1e3)
         res["flushed_pct_hbm_peak"] = 100.0 * algo_bytes / (flushed_ms / 1e3) / 1e9 / HBM_PEAK_GBPS
-        del flush
+        per = time_each(step, reps, torch, before=lambda: flush.fill_(0))
+        dirty_ms = sum(per) / len(per)
+        res["flushed_dirty_launch_ms_mean"] = dirty_ms
+        res["flushed_dirty_pct_hbm_peak"] = 100.0 * algo_bytes / (dirty_ms / 1e3) / 1e9 / HBM_PEAK_GBPS
+        res["flush"] = "512 MiB read before each launch (clean eviction); dirty: 512 MiB written before each launch"
+        del flush, sink
         torch.cuda.empty_cache()
     if args.extra or args.probes:
         res["probes"] = probes(torch)
