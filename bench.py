@@ -479,6 +479,10 @@ def main() -> int:
         "kernel": f"gather_decode_mixed<{cfg.d}>" if mixed else f"gather_decode<{cfg.d},{cfg.kv}>",
     }
 
+    # per-launch distribution (each launch between its own pair of events)
+    per = sorted(time_each(step, min(100, max(10, args.steps)), torch))
+    q = lambda a, f: a[min(len(a) - 1, int(f * len(a)))]
+    res["launch_ms_p10_p50_p90"] = [q(per, 0.1), q(per, 0.5), q(per, 0.9)]
     if args.extra or args.flushed:
         # 512 MiB > L2 + MALL. A read of it leaves the caches holding clean
         # lines of the flush buffer (cold records, nothing to write back); a
@@ -490,6 +494,8 @@ def main() -> int:
         reps = max(5, args.steps // 2)
         per = time_each(step, reps, torch, before=lambda: torch.sum(flush, 0, dtype=torch.int64, out=sink))
         flushed_ms = sum(per) / len(per)
+        per.sort()
+        res["flushed_launch_ms_p10_p50_p90"] = [q(per, 0.1), q(per, 0.5), q(per, 0.9)]
         res["flushed_launch_ms_mean"] = flushed_ms
         res["flushed_rows_per_s"] = n / (flushed_ms / 1e3)
         res["flushed_pct_hbm_peak"] = 100.0 * algo_bytes / (flushed_ms / 1e3) / 1e9 / HBM_PEAK_GBPS
