@@ -1,0 +1,106 @@
+"""Seeded random sweep of the HIP lookup against the CPU oracle: table shape
+(d, kv), table size, batch size (every launch shape), id distribution with
+out-of-range ids sprinkled in, residency, and entry point (raw, scaled,
+dedup), plus mixed-rate tables. Each case runs twice, so a result that
+changed from one launch to the next would fail as well as a wrong one."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import trellis_coded_row_amd as cp
+import workload
+from parity import assert_bf16_within_ulp, assert_bit_exact, device_lookup, make_table, say, shape_change_sizes
+
+pytestmark = pytest.mark.gpu
+
+LUT = workload.lut_fp16(0)
+CASES = 24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    torch.cuda.init()
+
+
+def draw_ids(rng, rows, n):
+    kind = rng.integers(0, 3)
+    if kind == 0:
+        ids = rng.integers(0, rows, n, dtype=np.int64)
+    elif kind == 1:
+        ids = workload.zipf_ids(rows, n, seed=int(rng.integers(1 << 30)))
+    else:  # runs of consecutive rows (neighbouring records share cache lines)
+        start = rng.integers(0, rows, (n + 15) // 16)
+        ids = ((start[:, None] + np.arange(16)[None, :]) % rows).reshape(-1)[:n].astype(np.int64)
+    nbad = int(rng.integers(0, 4))
+    pos = rng.choice(n, size=min(nbad, n), replace=False)
+    ids[pos] = rng.choice(np.array([-1, rows, rows + 7, 2**62, -(2**40)], dtype=np.int64), size=pos.size)
+    return ids
+
+
+def sizes():
+    s = shape_change_sizes()
+    return [1, 5, 96, 777, 3001, s[0], s[2], s[3], s[5]]
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_single_rate(case):
+    rng = np.random.default_rng(9000 + case)
+    d = int(rng.choice([64, 128, 256, 512]))
+    kv = int(rng.choice([3, 4, 5, 6]))
+    rows = int(rng.choice([1, 2, 33, 1000, 20_011]))
+    n = int(rng.choice(sizes()))
+    host = bool(rng.random() < 0.25)
+    recs = workload.random_records(rows, d, kv, seed=int(rng.integers(1 << 30)))
+    ids = draw_ids(rng, rows, n)
+    label = f"case {case}: d{d} kv{kv} rows {rows} n {n} {'host' if host else 'hbm'}"
+    say(label)
+    t = make_table(LUT, recs, d, kv, residency=cp.CP_RESIDENCY_HOST_MAPPED if host else cp.CP_RESIDENCY_DEVICE)
+    try:
+        exp_raw, nbad = oracle.lookup_decode(LUT, recs, rows, d, kv, ids, raw=True)
+        exp, _ = oracle.lookup_decode(LUT, recs, rows, d, kv, ids)
+        for rep in range(2):
+            got_raw = device_lookup(t, ids, raw=True)
+            assert t.check() == (nbad == 0), label
+            assert_bit_exact(got_raw, exp_raw, f"{label} f(c) run {rep}")
+            got = device_lookup(t, ids)
+            assert t.check() == (nbad == 0), label
+            assert_bf16_within_ulp(got, exp, f"{label} rows run {rep}")
+            got_d = device_lookup(t, ids, dedup=True)
+            assert t.check() == (nbad == 0), label
+            assert_bit_exact(got_d, got, f"{label} dedup run {rep}")
+    finally:
+        t.close()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_mixed_rate(case):
+    rng = np.random.default_rng(9500 + case)
+    d = int(rng.choice([64, 128, 256, 512]))
+    nclass = int(rng.integers(1, 5))
+    kvs = tuple(int(k) for k in rng.choice([3, 4, 5, 6], size=nclass, replace=False))
+    rows = int(rng.choice([1, 31, 32, 33, 5000]))
+    n = int(rng.choice(sizes()))
+    cls = rng.integers(0, nclass, size=rows).astype(np.uint8)
+    packed = workload.random_mixed_records(d, kvs, cls, seed=int(rng.integers(1 << 30)))
+    ids = draw_ids(rng, rows, n)
+    label = f"mixed case {case}: d{d} rates {kvs} rows {rows} n {n}"
+    say(label)
+    t = cp.MixedTable(d, kvs, cls, LUT)
+    try:
+        t.upload_bytes(packed, 0, rows)
+        exp_raw, nbad = oracle.lookup_decode_mixed(LUT, packed, d, kvs, cls, ids, raw=True)
+        exp, _ = oracle.lookup_decode_mixed(LUT, packed, d, kvs, cls, ids)
+        for rep in range(2):
+            got_raw = device_lookup(t, ids, raw=True)
+            assert t.check() == (nbad == 0), label
+            assert_bit_exact(got_raw, exp_raw, f"{label} f(c) run {rep}")
+            got = device_lookup(t, ids)
+            assert t.check() == (nbad == 0), label
+            assert_bf16_within_ulp(got, exp, f"{label} rows run {rep}")
+    finally:
+        t.close()
