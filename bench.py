@@ -69,6 +69,17 @@ def read_counter_summary(config: str, ids_kind: str, kind: str = "single") -> di
     return {"fetch_bytes": fetch, "write_bytes": write, "bytes": fetch + write, "file": os.path.basename(path)}
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def time_region(fn, steps: int, torch) -> float:
     """ms of `steps` back-to-back calls of fn() on the current stream, between
     one pair of events (synchronised before and after)."""
@@ -525,11 +536,11 @@ def main() -> int:
         threads = max(1, min(16, os.cpu_count() or 1))
         if mixed:
             o_off = oracle.mixed_offsets(cfg.d, kvs, classes)
-            decode = lambda sel: oracle.lookup_decode_mixed(lut, records, cfg.d, kvs, classes, sel,
-                                                            offsets=o_off, nthreads=threads)
+            decode = lambda sel, th=threads: oracle.lookup_decode_mixed(lut, records, cfg.d, kvs, classes, sel,
+                                                                        offsets=o_off, nthreads=th)
         else:
-            decode = lambda sel: oracle.lookup_decode(lut, records, cfg.rows, cfg.d, cfg.kv, sel,
-                                                      nthreads=threads)
+            decode = lambda sel, th=threads: oracle.lookup_decode(lut, records, cfg.rows, cfg.d, cfg.kv, sel,
+                                                                  nthreads=th)
         cal = min(n, 2048)
         t = time.perf_counter()
         decode(ids_np[:cal])
@@ -548,6 +559,14 @@ def main() -> int:
                       f"plain C oracle, bit-by-bit trellis walk, fp64 scaling)",
             "gpu_rows_matching_oracle": int((got == exp).all(axis=1).sum()),
         }
+        # the same oracle on one thread, over a bounded slice of the replay
+        one = min(n, 32768)
+        t = time.perf_counter()
+        decode(ids_np[:one], 1)
+        one_s = time.perf_counter() - t
+        res["cpu_baseline"]["single_thread"] = {"value": one / one_s, "unit": "rows/s",
+                                                "sample": f"first {one:,} replay ids ({one_s:.2f} s)"}
+        res["cpu_baseline"]["host"] = {"cpus": os.cpu_count(), "model": host_cpu_model()}
     table.close()
     print(json.dumps(res), flush=True)
     return 0
