@@ -12,7 +12,9 @@ Prints one JSON line. value = decoded rows/s over the K timed steps (inputs
 resident in HBM before timing starts); roofline = effective bytes per launch
 (records read + bf16 rows written, n * (R + 2d)) over the average launch time
 measured with events on the launch stream, against the 8 TB/s HBM peak;
-cpu_baseline = the CPU oracle decoding a sample of the same replay.
+cpu_baseline = the CPU oracle decoding a sample of the same replay;
+flushed_* = the same launch timed one at a time after L2 and MALL are evicted
+(cold records), alongside the warm back-to-back figure that is the value.
 """
 from __future__ import annotations
 
@@ -316,9 +318,11 @@ def main() -> int:
     ap.add_argument("--hot-share", type=float, default=0.0,
                     help="host_d512: keep device copies of this share of the rows, the most looked-up first")
     ap.add_argument("--flushed", action="store_true",
-                    help="also time launches with L2/MALL flushed before each (512 MiB read; and 512 MiB written)")
+                    help="time launches with L2/MALL flushed before each (512 MiB read; and 512 MiB written); "
+                         "on by default")
+    ap.add_argument("--no-flushed", action="store_true", help="skip the flushed launches")
     ap.add_argument("--probes", action="store_true", help="also run 1 GiB copy and fill probes")
-    ap.add_argument("--extra", action="store_true", help="--flushed and --probes")
+    ap.add_argument("--extra", action="store_true", help="--probes (the flushed launches are on by default)")
     ap.add_argument("--encode", action="store_true",
                     help="time cp_table_encode instead (trellis-coded quantisation of --encode-rows rows)")
     ap.add_argument("--encode-rows", type=int, default=4096)
@@ -494,7 +498,7 @@ def main() -> int:
     per = sorted(time_each(step, min(100, max(10, args.steps)), torch))
     q = lambda a, f: a[min(len(a) - 1, int(f * len(a)))]
     res["launch_ms_p10_p50_p90"] = [q(per, 0.1), q(per, 0.5), q(per, 0.9)]
-    if args.extra or args.flushed:
+    if not args.no_flushed:
         # 512 MiB > L2 + MALL. A read of it leaves the caches holding clean
         # lines of the flush buffer (cold records, nothing to write back); a
         # write of it leaves dirty lines, whose write-back then competes with
