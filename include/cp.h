@@ -68,7 +68,10 @@ typedef enum {
     CP_ERR_UNSUPPORTED = 2,      /* no kernel for the shape, or the call does not apply to this table */
     CP_ERR_OUT_OF_MEMORY = 3,    /* device or pinned host allocation failed */
     CP_ERR_HIP = 4,              /* a HIP runtime call failed; see cp_last_hip_error */
-    CP_ERR_ID_OUT_OF_RANGE = 5   /* reported by cp_table_check: some id was outside [0, rows) */
+    CP_ERR_ID_OUT_OF_RANGE = 5,  /* reported by cp_table_check: some id was outside [0, rows) */
+    /* not a status: makes every nonnegative 32-bit value a valid cp_status, so
+     * cp_status_string may be handed any such code (it names unknown ones) */
+    CP_STATUS_MAX_ENUM = 0x7FFFFFFF
 } cp_status;
 
 typedef enum {

@@ -55,10 +55,15 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
+    """The compiled oracle; CP_ORACLE_LIBRARY names another build of the same
+    source (for instance one compiled with sanitizers)."""
     global _lib
     if _lib is None:
-        build(force=False)
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("CP_ORACLE_LIBRARY")
+        if not path:
+            build(force=False)
+            path = _LIB
+        L = ctypes.CDLL(path)
         u8p = ctypes.POINTER(ctypes.c_uint8)
         u16p = ctypes.POINTER(ctypes.c_uint16)
         u32p = ctypes.POINTER(ctypes.c_uint32)

@@ -89,6 +89,7 @@ const char *cp_status_string(cp_status s)
     case CP_ERR_OUT_OF_MEMORY: return "out of memory";
     case CP_ERR_HIP: return "HIP runtime error";
     case CP_ERR_ID_OUT_OF_RANGE: return "a lookup id was outside [0, rows)";
+    case CP_STATUS_MAX_ENUM: break;
     }
     return "unknown status";
 }
