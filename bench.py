@@ -370,12 +370,18 @@ def main() -> int:
         class_bytes = np.array([workload.record_bytes(cfg.d, k) for k in kvs], dtype=np.int64)
     else:
         records = workload.random_records(cfg.rows, cfg.d, cfg.kv, cfg.table_seed)
-    if ids_kind == "zipf":
-        ids_np = workload.zipf_ids(cfg.rows, cfg.n_ids, cfg.ids_seed)
+    if ids_kind == cfg.ids_kind:
+        ids_seed = cfg.ids_seed  # the workload's own id stream
+        ids_np = cfg.ids()
     elif ids_kind == "uniform":
-        ids_np = workload.uniform_ids(cfg.rows, cfg.n_ids, cfg.uniform_seed or cfg.ids_seed + 100)
-    else:
-        ids_np = workload.zipf_ids(cfg.rows, cfg.n_ids, cfg.ids_seed)[:96]
+        ids_seed = cfg.uniform_seed or cfg.ids_seed + 100
+        ids_np = workload.uniform_ids(cfg.rows, cfg.n_ids, ids_seed)
+    elif ids_kind == "zipf":
+        ids_seed = cfg.ids_seed
+        ids_np = workload.zipf_ids(cfg.rows, cfg.n_ids, ids_seed)
+    else:  # one token's decode step: the first 96 ids of the workload's stream
+        ids_seed = cfg.ids_seed
+        ids_np = cfg.ids()[:96]
     gen_s = time.time() - t_gen
 
     residency = cp.CP_RESIDENCY_HOST_MAPPED if cfg.host_resident else cp.CP_RESIDENCY_DEVICE
@@ -465,7 +471,10 @@ def main() -> int:
             "residency": "host" + ("-noncoherent" if args.noncoherent else "") if cfg.host_resident else "hbm",
             "hot_rows_in_hbm": hot_rows,
             "entry_point": "cp_lookup_decode_dedup" if args.dedup else "cp_lookup_decode",
+            "seeds": {"codebook": 0, "table": cfg.table_seed, "ids": ids_seed},
         },
+        "versions": {"hip": torch.version.hip, "torch": torch.__version__, "numpy": np.__version__,
+                     "library": os.path.basename(cp.library_path())},
         "effective_GBps": algo_bytes * args.steps / (total_ms / 1e3) / 1e9,
         "pct_hbm_peak": 100.0 * algo_bytes * args.steps / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
         "launch_ms_mean": launch_ms,
