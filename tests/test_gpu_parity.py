@@ -160,6 +160,21 @@ def test_caller_stream_is_used():
         s.synchronize()
         got = out.view(torch.int16).cpu().numpy().view(np.uint16)
         assert_bf16_within_ulp(got, exp, "side stream")
+        # a side stream that is not the current one: the binding allocates the
+        # output and the dedup workspace on the current stream and records
+        # their use on the side stream; allocations made meanwhile on the
+        # current stream must not take their memory
+        ids = torch.from_numpy(ids_np).cuda()
+        torch.cuda.synchronize()
+        outs = []
+        for _ in range(3):
+            outs.append(t.lookup_decode_dedup(ids, stream=s))
+            junk = [torch.full((1 << 20,), 7, dtype=torch.int32, device="cuda") for _ in range(4)]
+            del junk
+        s.synchronize()
+        for o in outs:
+            got = o.view(torch.int16).cpu().numpy().view(np.uint16)
+            assert_bf16_within_ulp(got, exp, "dedup on a side stream")
     finally:
         t.close()
 

@@ -255,6 +255,17 @@ def _stream_handle(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _keep_for_stream(tensor, stream) -> None:
+    """A tensor allocated here on torch's current stream and used by work on
+    `stream`: tell torch's caching allocator, so the memory is not handed out
+    again before that work is done."""
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if s != torch.cuda.current_stream():
+        tensor.record_stream(s)
+
+
 class Table:
     """A CP table on the current device (or in pinned host memory).
 
@@ -303,18 +314,24 @@ class Table:
 
     def lookup_decode(self, ids, out=None, stream=None):
         """bf16[n, d]: alpha * f(c) of rows ids[j], in lookup order."""
+        own = out is None
         n, out = self._check_io(ids, out, torch.bfloat16)
         st = cp_lookup_decode(self.handle, ids.data_ptr(), n, out.data_ptr(), _stream_handle(stream))
         if st != CP_OK:
             raise CPError(st, "cp_lookup_decode")
+        if own:
+            _keep_for_stream(out, stream)
         return out
 
     def lookup_decode_raw(self, ids, out=None, stream=None):
         """fp16[n, d]: the unscaled f(c) of rows ids[j], in lookup order."""
+        own = out is None
         n, out = self._check_io(ids, out, torch.float16)
         st = cp_lookup_decode_raw(self.handle, ids.data_ptr(), n, out.data_ptr(), _stream_handle(stream))
         if st != CP_OK:
             raise CPError(st, "cp_lookup_decode_raw")
+        if own:
+            _keep_for_stream(out, stream)
         return out
 
     def dedup_workspace_bytes(self, n: int) -> int:
@@ -325,14 +342,20 @@ class Table:
         workspace: a uint8 device tensor of at least dedup_workspace_bytes(n)
         bytes (allocated here when None); scratch, reusable across calls that
         do not overlap."""
+        own_out = out is None
         n, out = self._check_io(ids, out, torch.bfloat16)
         need = self.dedup_workspace_bytes(n)
-        if workspace is None:
+        own = workspace is None
+        if own:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ids.device)
         st = cp_lookup_decode_dedup(self.handle, ids.data_ptr(), n, out.data_ptr(), workspace.data_ptr(),
                                     workspace.numel() * workspace.element_size(), _stream_handle(stream))
         if st != CP_OK:
             raise CPError(st, "cp_lookup_decode_dedup")
+        if own:
+            _keep_for_stream(workspace, stream)
+        if own_out:
+            _keep_for_stream(out, stream)
         return out
 
     def download(self, first_row: int = 0, nrows: int | None = None) -> np.ndarray:
@@ -357,12 +380,15 @@ class Table:
             raise ValueError(f"rows must be a contiguous float32 device tensor of shape (n, {self.d})")
         n = rows.shape[0]
         need = self.encode_workspace_bytes(n)
-        if workspace is None:
+        own = workspace is None
+        if own:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=rows.device)
         st = cp_table_encode(self.handle, first_row, n, rows.data_ptr(), workspace.data_ptr(),
                              workspace.numel() * workspace.element_size(), _stream_handle(stream))
         if st != CP_OK:
             raise CPError(st, "cp_table_encode")
+        if own:
+            _keep_for_stream(workspace, stream)
 
     def set_hot_rows(self, rows) -> int:
         """Keeps device copies of these rows' records (pinned-host tables);
