@@ -19,12 +19,13 @@
 // Work mapping (memory-bound gather + streaming write; no MFMA):
 //   - a row is handled by d/8 lanes (a full wave64 at d = 512); lane l makes
 //     outputs [8l, 8l+8): steps 4l .. 4l+3, one 16-byte store;
-//   - lane l loads the 4kv code bits its steps introduce (one aligned dword
-//     at kv = 4, two otherwise); the 16-kv older bits each window also needs
-//     come from the neighbouring lane(s) through a lane shuffle, circular
-//     within the row, which is exactly the tail-biting wrap;
-//   - records are 2-byte aligned (R = kv*d/16 + 2 is even), so every load is
-//     an aligned dword and bits are taken out with shifts;
+//   - lane l loads the 4kv code bits its steps introduce (at kv = 4 one
+//     16-bit load of code half-word l, otherwise the two aligned dwords that
+//     cover them); the 16-kv older bits each window also needs come from the
+//     neighbouring lane(s) through a lane shuffle (DPP rotation at d = 512),
+//     circular within the row, which is exactly the tail-biting wrap;
+//   - records are only 2-byte aligned (R = kv*d/16 + 2 is even), so loads
+//     are half-words or aligned dwords and bits are taken out with shifts;
 //   - the 2 KB codebook is staged in LDS once per workgroup, replicated
 //     COPIES times so that lane k reads copy k % COPIES, which spreads the
 //     random codebook reads over more banks;
@@ -33,8 +34,9 @@
 //     any is decoded and the next chunk's ids are requested before decoding,
 //     so a whole chunk of record loads is in flight per wave; chunks hold 16
 //     lookups for batches that fill the chip, and 4 or 1 for smaller ones;
-//   - the scale, the window hash and the fp16 -> fp32 widening run on the
-//     scalar unit, v_mad_u32_u24 and v_fma_mix_f32 respectively;
+//   - the scale of a one-row wave (d = 512) comes by a scalar load and stays
+//     in an SGPR; the window hash is one v_mad_u32_u24, and the fp16 -> fp32
+//     widening and the scaling are one v_fma_mix_f32 per output;
 //   - outputs are written with nontemporal stores: they are not re-read, and
 //     keeping them out of the caches leaves room for hot (Zipf) records.
 #include "cp_lane.h"
