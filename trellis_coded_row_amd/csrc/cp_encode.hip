@@ -24,8 +24,8 @@
 // r among equal metrics; the end memory is the smallest among equal metrics).
 // The result is therefore one specific code, reproducible bit for bit.
 //
-// Layout on the GPU: one workgroup of 1024 threads per row; path metrics of
-// both time steps, the per-step branch costs, z and the codebook in LDS; the
+// Layout on the GPU: one workgroup per row (1,024 threads at kv 3 and 4, 512
+// at kv 5 and 6); path metrics of both time steps, the per-step branch costs, z and the codebook in LDS; the
 // back-pointers (one byte per memory per step) in a caller workspace.
 #pragma clang fp contract(off)
 
@@ -35,7 +35,7 @@ namespace cpk {
 
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr uint32_t kMaxThreads = 1024;
 
 __device__ __forceinline__ double half_to_double(uint32_t h16)
 {
@@ -67,37 +67,65 @@ struct Tcq {
     static constexpr uint32_t S = 1u << M;             // memories
     static constexpr uint32_t BR = 1u << KV;           // predecessors (and successors) per group
     static constexpr uint32_t G = S / BR;              // groups sharing one predecessor set
-    static constexpr uint32_t IPT = S / kThreads;      // next memories per thread
+    // threads per workgroup. At kv 5 and 6 a workgroup of 512 holds two next
+    // memories per thread or more (so kv 6 can pair them, below) and two
+    // workgroups share a CU; at kv 4 the LDS admits one workgroup either way
+    // and 1,024 threads hide more latency; kv 3 has only 8 predecessors per
+    // group for its 8 successors per thread. Measured on 4,096 rows at
+    // d = 512 (ms with 1,024 / 512 threads): kv 4: 31.4 / 35.1; kv 5: 30.7 /
+    // 26.0; kv 6: 37.1 (unpaired) / 26.8.
+    static constexpr uint32_t NT = KV >= 5 ? 512 : kMaxThreads;
+    static constexpr uint32_t IPT = S / NT;            // next memories per thread
     static constexpr uint32_t TPG = BR / IPT;          // threads per group
     static constexpr uint32_t SP = S + (S >> 4);       // padded metric array length
     // copies of each branch cost, lane l reading copy l mod CC: lanes reading
-    // different copies never meet on an LDS bank. Measured per rate on the
-    // d512 batch (ms for 4,096 rows with 1 / 2 / 4 copies): kv 4: 41.2 / 36.1
-    // / 33.3; kv 5: 40.0 / 32.0 / 34.9; kv 6: 37.1 / 37.5 / 55.7; kv 3 has
-    // no LDS left for a second copy.
+    // different copies never meet on an LDS bank. Measured with paired loads
+    // and 1,024 threads on the d512 batch (ms for 4,096 rows with 1 / 2 / 4
+    // copies): kv 4: 32.5 / 31.3 / 31.4; kv 5: 33.3 / 30.7 / 33.3; before
+    // pairing, kv 6: 37.1 / 37.5 / 55.7; kv 3 has no LDS left for a second
+    // copy.
     static constexpr uint32_t CC = KV == 4 ? 4 : KV == 5 ? 2 : 1;
-    static_assert(IPT >= 1 && TPG * G == (uint32_t)kThreads, "thread mapping");
+    // The windows s and s ^ 0x8000 hash to idx and idx ^ 256 (adding 2^15 to
+    // s flips bit 15 of s*s + s and changes only higher bits otherwise) and
+    // carry opposite signs, so both branch costs share the key
+    // idx ^ (sign << 8). With the costs stored by key (the sign in the low
+    // position) one 16-byte load fetches the pair. PAIR: a thread holds its
+    // successors in such pairs, u and u + BR/2 (needs IPT >= 2).
+    static constexpr bool PAIR = IPT >= 2;
+    static constexpr uint32_t H = PAIR ? IPT / 2 : IPT;  // cost loads per predecessor
+    static_assert(IPT >= 1 && TPG * G == NT && NT >= 512 && NT <= kMaxThreads, "thread mapping");
+
+    // successor u of slot i of thread slot tq (tq = tid / G)
+    static __device__ __forceinline__ uint32_t succ(uint32_t tq, uint32_t i)
+    {
+        if constexpr (PAIR)
+            return i < H ? tq * H + i : tq * H + (i - H) + BR / 2;
+        else
+            return tq * IPT + i;
+    }
 };
 
 template <int KV>
 struct Shared {
     double D[2][Tcq<KV>::SP];
-    double cost[2][1024 * Tcq<KV>::CC];  // branch costs of one step, entry (2 idx + negated) * CC + copy
+    // branch costs of one step: entry (2 idx + negated) * CC + copy, or with
+    // PAIR ((idx ^ negated << 8) * CC + copy) * 2 + negated
+    alignas(16) double cost[2][1024 * Tcq<KV>::CC];
     double z[512];
     uint32_t lut[512];
     uint8_t code[6 * 512 / 16 + 2];
-    double red_v[kThreads / 64];
-    uint32_t red_i[kThreads / 64];
+    double red_v[kMaxThreads / 64];
+    uint32_t red_i[kMaxThreads / 64];
     uint32_t W;
     double norm;
 };
 
-// cost[(2 idx + neg) * CC + c] = (z0 - g0)^2 + (z1 - g1)^2 for the pair
-// g = +-LUT[idx], for every copy c.
-template <uint32_t CC>
-__device__ __forceinline__ void fill_costs(double *cost, const uint32_t *lut, double z0, double z1)
+// cost of the pair g = +-LUT[idx]: (z0 - g0)^2 + (z1 - g1)^2, for every copy
+// c, at (2 idx + neg) * CC + c, or with PAIR at
+// ((idx ^ neg << 8) * CC + c) * 2 + neg; entry i = 2 idx + neg.
+template <uint32_t CC, bool PAIR>
+__device__ __forceinline__ void fill_cost(double *cost, const uint32_t *lut, double z0, double z1, uint32_t i)
 {
-    const uint32_t i = threadIdx.x;
     const uint32_t e = lut[i >> 1];
     double g0 = half_to_double(e & 0xFFFFu), g1 = half_to_double(e >> 16);
     if (i & 1u) {
@@ -106,8 +134,22 @@ __device__ __forceinline__ void fill_costs(double *cost, const uint32_t *lut, do
     }
     const double e0 = z0 - g0, e1 = z1 - g1;
     const double c = e0 * e0 + e1 * e1;
+    if constexpr (PAIR) {
+        const uint32_t key = (i >> 1) ^ ((i & 1u) << 8);
 #pragma unroll
-    for (uint32_t k = 0; k < CC; ++k) cost[i * CC + k] = c;
+        for (uint32_t k = 0; k < CC; ++k) cost[(key * CC + k) * 2 + (i & 1u)] = c;
+    } else {
+#pragma unroll
+        for (uint32_t k = 0; k < CC; ++k) cost[i * CC + k] = c;
+    }
+}
+
+template <uint32_t CC, bool PAIR, uint32_t NT>
+__device__ __forceinline__ void fill_costs(double *cost, const uint32_t *lut, double z0, double z1)
+{
+#pragma unroll
+    for (uint32_t i = threadIdx.x; i < 1024; i += NT)
+        fill_cost<CC, PAIR>(cost, lut, z0, z1, i);
 }
 
 // One store of a thread's IPT back-pointers (consecutive bytes).
@@ -130,10 +172,11 @@ __device__ __forceinline__ void store_bp(uint8_t *p, const uint32_t *br)
 
 // Thread mapping: thread tid serves group L = tid mod G (the next memories
 // m2 = L | u << (M - kv) share the predecessors L << kv | r) and its IPT
-// successors u = (tid / G) * IPT + i. Consecutive lanes thus take consecutive
-// groups, whose windows differ in their low bits, which spreads the branch
-// cost gathers over the LDS banks (lanes sharing a group would read costs at
-// indices that agree in their low bits). A thread stores the back-pointers of
+// successors u = succ(tid / G, i): (tid / G) * IPT + i, or with PAIR the
+// pairs u, u + BR/2 for u = (tid / G) * IPT/2 + j. Consecutive lanes thus
+// take consecutive groups, whose windows differ in their low bits, which
+// spreads the branch cost gathers over the LDS banks (lanes sharing a group
+// would read costs at indices that agree in their low bits). A thread stores the back-pointers of
 // its IPT next memories as IPT consecutive bytes at tid * IPT; this is the
 // position of next memory m2 within one step's S bytes.
 template <int KV>
@@ -141,7 +184,43 @@ __device__ __forceinline__ uint32_t bp_pos(uint32_t m2)
 {
     using P = Tcq<KV>;
     const uint32_t L = m2 & (P::G - 1), u = m2 >> (P::M - KV);
-    return ((u / P::IPT) * P::G + L) * P::IPT + u % P::IPT;
+    if constexpr (P::PAIR) {
+        const uint32_t lo = u & (P::BR / 2 - 1);
+        return ((lo / P::H) * P::G + L) * P::IPT + lo % P::H + (u >= P::BR / 2 ? P::H : 0u);
+    } else {
+        return ((u / P::IPT) * P::G + L) * P::IPT + u % P::IPT;
+    }
+}
+
+typedef double dbl2 __attribute__((ext_vector_type(2)));
+
+// Branch costs of predecessor r for the IPT successors of thread slot tq in
+// group L, into cv[i] for successor succ(tq, i).
+template <int KV>
+__device__ __forceinline__ void load_costs(double *cv, const double *cst, uint32_t L, uint32_t tq, uint32_t r,
+                                           uint32_t cpy)
+{
+    using P = Tcq<KV>;
+    if constexpr (P::PAIR) {
+        const dbl2 *c2 = reinterpret_cast<const dbl2 *>(cst);
+#pragma unroll
+        for (uint32_t j = 0; j < P::H; ++j) {
+            const uint32_t u = P::succ(tq, j);  // below BR/2: sign bit clear
+            const uint32_t s = (L << KV) | (u << P::M) | r;
+            const uint32_t h = s * s + s;
+            const dbl2 c = c2[((h >> 7) & 511u) * P::CC + cpy];
+            cv[j] = c.x;
+            cv[j + P::H] = c.y;
+        }
+    } else {
+#pragma unroll
+        for (uint32_t i = 0; i < P::IPT; ++i) {
+            const uint32_t u = P::succ(tq, i);
+            const uint32_t s = (L << KV) | (u << P::M) | r;
+            const uint32_t h = s * s + s;
+            cv[i] = cst[(((h >> 6) & 0x3FEu) | (u >> (KV - 1))) * P::CC + cpy];
+        }
+    }
 }
 
 // One Viterbi pass over the T steps t = (k + rot) mod T; start < 0: every
@@ -154,9 +233,9 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
     const uint32_t tid = threadIdx.x;
     const uint32_t L = tid % P::G, tq = tid / P::G;
     const uint32_t cpy = tid & (P::CC - 1);
-    for (uint32_t m = tid; m < P::S; m += kThreads)
+    for (uint32_t m = tid; m < P::S; m += P::NT)
         sh.D[0][pad(m)] = (start < 0 || (int32_t)m == start) ? 0.0 : __builtin_inf();
-    fill_costs<P::CC>(sh.cost[0], sh.lut, sh.z[2 * (rot % T)], sh.z[2 * (rot % T) + 1]);
+    fill_costs<P::CC, P::PAIR, P::NT>(sh.cost[0], sh.lut, sh.z[2 * (rot % T)], sh.z[2 * (rot % T) + 1]);
     __syncthreads();
     int cur = 0;
     for (uint32_t k = 0; k < T; ++k) {
@@ -173,24 +252,10 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
         // software-pipelined: the branch costs of predecessor r + 1 are
         // requested before the add-compare-selects of predecessor r
         double cv[2][P::IPT];
-#pragma unroll
-        for (uint32_t i = 0; i < P::IPT; ++i) {
-            const uint32_t u = tq * P::IPT + i;
-            const uint32_t s = (L << KV) | (u << P::M);
-            const uint32_t h = s * s + s;
-            cv[0][i] = cst[(((h >> 6) & 0x3FEu) | (u >> (KV - 1))) * P::CC + cpy];
-        }
+        load_costs<KV>(cv[0], cst, L, tq, 0, cpy);
 #pragma unroll
         for (uint32_t r = 0; r < P::BR; ++r) {
-            if (r + 1 < P::BR) {
-#pragma unroll
-                for (uint32_t i = 0; i < P::IPT; ++i) {
-                    const uint32_t u = tq * P::IPT + i;
-                    const uint32_t s = (L << KV) | (u << P::M) | (r + 1);
-                    const uint32_t h = s * s + s;
-                    cv[(r + 1) & 1][i] = cst[(((h >> 6) & 0x3FEu) | (u >> (KV - 1))) * P::CC + cpy];
-                }
-            }
+            if (r + 1 < P::BR) load_costs<KV>(cv[(r + 1) & 1], cst, L, tq, r + 1, cpy);
             const double dv = Dc[pad((L << KV) | r)];
 #pragma unroll
             for (uint32_t i = 0; i < P::IPT; ++i) {
@@ -200,18 +265,18 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
                     br[i] = r;
                 }
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, P::IPT + 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, P::H + 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 6 * P::IPT, 0);
         }
 #pragma unroll
         for (uint32_t i = 0; i < P::IPT; ++i) {
-            const uint32_t u = tq * P::IPT + i;
+            const uint32_t u = P::succ(tq, i);
             Dn[pad(L | (u << (P::M - KV)))] = best[i];
         }
         store_bp<P::IPT>(bp + (uint64_t)k * P::S + tid * P::IPT, br);
         if (k + 1 < T) {
             const uint32_t t1 = (k + 1 + rot) % T;
-            fill_costs<P::CC>(sh.cost[(k + 1) & 1], sh.lut, sh.z[2 * t1], sh.z[2 * t1 + 1]);
+            fill_costs<P::CC, P::PAIR, P::NT>(sh.cost[(k + 1) & 1], sh.lut, sh.z[2 * t1], sh.z[2 * t1 + 1]);
         }
         __syncthreads();
         cur ^= 1;
@@ -227,7 +292,7 @@ __device__ __forceinline__ uint32_t argmin_memory(Shared<KV> &sh, const double *
     const uint32_t tid = threadIdx.x, lane = tid & 63u, w = tid >> 6;
     double bv = __builtin_inf();
     uint32_t bi = 0xFFFFFFFFu;
-    for (uint32_t m = tid; m < P::S; m += kThreads) {
+    for (uint32_t m = tid; m < P::S; m += P::NT) {
         const double v = D[pad(m)];
         if (v < bv || (v == bv && m < bi)) {
             bv = v;
@@ -250,7 +315,7 @@ __device__ __forceinline__ uint32_t argmin_memory(Shared<KV> &sh, const double *
     if (tid == 0) {
         double v = sh.red_v[0];
         uint32_t i = sh.red_i[0];
-        for (uint32_t q = 1; q < kThreads / 64; ++q)
+        for (uint32_t q = 1; q < P::NT / 64; ++q)
             if (sh.red_v[q] < v || (sh.red_v[q] == v && sh.red_i[q] < i)) {
                 v = sh.red_v[q];
                 i = sh.red_i[q];
@@ -265,7 +330,7 @@ __device__ __forceinline__ uint32_t argmin_memory(Shared<KV> &sh, const double *
 }
 
 template <int KV>
-__global__ __launch_bounds__(kThreads) void tcq_encode_rows(const float *__restrict__ e, uint64_t nrows,
+__global__ __launch_bounds__(Tcq<KV>::NT) __attribute__((amdgpu_waves_per_eu(4))) void tcq_encode_rows(const float *__restrict__ e, uint64_t nrows,
                                                             uint32_t d, const uint32_t *__restrict__ lut,
                                                             uint8_t *__restrict__ out, uint64_t record_bytes,
                                                             uint8_t *__restrict__ workspace)
@@ -280,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void tcq_encode_rows(const float *__restr
     for (uint64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
         const float *er = e + row * d;
         uint8_t *rec = out + row * record_bytes;
-        for (uint32_t b = tid; b < NB + 2; b += kThreads) sh.code[b] = 0;
+        for (uint32_t b = tid; b < NB + 2; b += P::NT) sh.code[b] = 0;
         if (tid == 0) {
             double n2 = 0.0;
             for (uint32_t i = 0; i < d; ++i) {
@@ -293,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void tcq_encode_rows(const float *__restr
         const double norm = sh.norm;
         if (norm > 0.0) {
             const double sd = __builtin_sqrt((double)d);
-            for (uint32_t i = tid; i < d; i += kThreads) sh.z[i] = sd * (double)er[i] / norm;
+            for (uint32_t i = tid; i < d; i += P::NT) sh.z[i] = sd * (double)er[i] / norm;
             __syncthreads();
 
             // pass A (p = 0): every start, steps rotated by T/2; W = the best
@@ -330,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void tcq_encode_rows(const float *__restr
 
             // f(c) of the emitted code (in the cost buffer, free now), then alpha
             uint32_t *f = reinterpret_cast<uint32_t *>(sh.cost[0]);
-            for (uint32_t t = tid; t < T; t += kThreads) {
+            for (uint32_t t = tid; t < T; t += P::NT) {
                 uint32_t s = 0;
                 for (uint32_t q = 0; q < 16; ++q) {
                     const uint32_t j = (KV * (t + 1) + N - 16 + q) % N;
@@ -358,8 +423,19 @@ __global__ __launch_bounds__(kThreads) void tcq_encode_rows(const float *__restr
         // a zero row (or one whose norm is not finite and positive) keeps the
         // all-zero code and alpha 0
         __syncthreads();
-        for (uint32_t b = tid; b < NB + 2; b += kThreads) rec[b] = sh.code[b];
+        for (uint32_t b = tid; b < NB + 2; b += P::NT) rec[b] = sh.code[b];
         __syncthreads();
+    }
+}
+
+uint32_t encode_threads(uint32_t kv)
+{
+    switch (kv) {
+    case 3: return Tcq<3>::NT;
+    case 4: return Tcq<4>::NT;
+    case 5: return Tcq<5>::NT;
+    case 6: return Tcq<6>::NT;
+    default: return 0;
     }
 }
 
@@ -387,7 +463,7 @@ hipError_t encode_grid(uint32_t kv, int num_cus, uint64_t nrows, uint32_t *block
     const void *k = encode_kernel(kv);
     if (!k) return hipErrorInvalidValue;
     int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, (int)encode_threads(kv), 0);
     if (e != hipSuccess) return e;
     if (per_cu < 1) return hipErrorInvalidConfiguration;
     const uint64_t most = (uint64_t)per_cu * (uint64_t)(num_cus > 0 ? num_cus : 1);
@@ -402,19 +478,19 @@ hipError_t encode(const EncodeArgs &a)
     if (a.nrows == 0 || a.blocks == 0) return hipSuccess;
     switch (a.kv) {
     case 3:
-        hipLaunchKernelGGL(tcq_encode_rows<3>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
+        hipLaunchKernelGGL(tcq_encode_rows<3>, dim3(a.blocks), dim3(Tcq<3>::NT), 0, a.stream, a.rows, a.nrows, a.d,
                            a.lut, a.out, a.record_bytes, a.workspace);
         break;
     case 4:
-        hipLaunchKernelGGL(tcq_encode_rows<4>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
+        hipLaunchKernelGGL(tcq_encode_rows<4>, dim3(a.blocks), dim3(Tcq<4>::NT), 0, a.stream, a.rows, a.nrows, a.d,
                            a.lut, a.out, a.record_bytes, a.workspace);
         break;
     case 5:
-        hipLaunchKernelGGL(tcq_encode_rows<5>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
+        hipLaunchKernelGGL(tcq_encode_rows<5>, dim3(a.blocks), dim3(Tcq<5>::NT), 0, a.stream, a.rows, a.nrows, a.d,
                            a.lut, a.out, a.record_bytes, a.workspace);
         break;
     case 6:
-        hipLaunchKernelGGL(tcq_encode_rows<6>, dim3(a.blocks), dim3(kThreads), 0, a.stream, a.rows, a.nrows, a.d,
+        hipLaunchKernelGGL(tcq_encode_rows<6>, dim3(a.blocks), dim3(Tcq<6>::NT), 0, a.stream, a.rows, a.nrows, a.d,
                            a.lut, a.out, a.record_bytes, a.workspace);
         break;
     default:
