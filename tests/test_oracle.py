@@ -333,6 +333,33 @@ def test_heuristic_codes_are_consistent_tail_biting_paths(d, kv):
         assert oracle.distortion(z, LUT, ex.code, d, kv) == pytest.approx(ex.cost, rel=1e-12)
 
 
+@pytest.mark.parametrize("d,kv", [(12, 4), (16, 3), (8, 5), (8, 6)])
+def test_heuristic_code_is_best_among_codes_with_its_start_memory(d, kv):
+    # The heuristic's second pass is a Viterbi search from one start memory W
+    # that keeps the paths ending in W (onedev.kr, "How it works": the code is
+    # a tail-biting path). Its result must therefore be the exhaustive minimum
+    # of ||z - f(c)||^2 over every code whose memory before step 0 is W. That
+    # memory is the 16 - kv oldest bits of the window of step 0, which are
+    # the last 16 - kv bits of the circular code.
+    N = oracle.code_bits(d, kv)
+    M = 16 - kv
+    rng = np.random.default_rng(4000 + 10 * d + kv)
+    for _ in range(2):
+        z = rng.standard_normal(d)
+        heur = oracle.tcq_encode(z, d, kv, LUT, oracle.ENC_HEURISTIC)
+        bits = np.unpackbits(heur.code, bitorder="little")[:N]
+        best = np.inf
+        for free in range(1 << (N - M)):
+            b = bits.copy()
+            b[:N - M] = (free >> np.arange(N - M)) & 1
+            code = np.packbits(b, bitorder="little")
+            best = min(best, oracle.distortion(z, LUT, code, d, kv))
+        assert heur.cost == pytest.approx(best, rel=1e-12, abs=1e-15)
+        # and the exhaustive minimum over all codes is no larger
+        full, _ = oracle.bruteforce_min(z, d, kv, LUT)
+        assert full <= best * (1 + 1e-12)
+
+
 def test_norm_restoring_scale():
     # alpha = ||e|| / ||f(c)|| (onedev.kr, "How it differs"): with the exact
     # alpha the rebuilt row has the original norm; with the stored bf16 alpha
