@@ -51,6 +51,8 @@ def check_records(got: np.ndarray, exp: np.ndarray, label: str) -> None:
     (64, 3, 300),
     (64, 5, 257),
     (64, 6, 129),
+    (64, 5, 1100),  # kv 5 and 6 run two 512-thread workgroups per CU: past 512 rows
+    (64, 6, 1100),
     (128, 4, 97),
     (256, 5, 33),
     (256, 6, 31),
