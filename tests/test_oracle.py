@@ -360,6 +360,50 @@ def test_heuristic_code_is_best_among_codes_with_its_start_memory(d, kv):
         assert full <= best * (1 + 1e-12)
 
 
+def test_heuristic_start_memory_is_that_of_the_best_rotated_free_start_path():
+    # The heuristic's first pass searches, from every start memory, the
+    # steps in the order T/2, ..., T-1, 0, ..., T/2-1, and takes the memory
+    # its best path holds just before step 0. Brute force at d = 8, kv = 4:
+    # a free-start path over the T = 4 rotated steps is any 28-bit string,
+    # whose k-th window is bits [4k, 4k + 16); the memory before step 0
+    # (visited as k = T - T/2) is bits [4(T - T/2), 4(T - T/2) + 12). It
+    # must be the start memory of the heuristic's code, its last 12 bits.
+    # Branch costs follow the trellis reading of the decoder: +-LUT[idx] with
+    # idx and the sign from the window hash, fp16 values taken by numpy.
+    d, kv = 8, 4
+    T, M = d // 2, 16 - kv
+    rot = T // 2
+    N = oracle.code_bits(d, kv)
+    idx = np.empty(65536, dtype=np.int64)
+    neg = np.empty(65536, dtype=np.int64)
+    for w in range(65536):
+        idx[w], neg[w] = oracle.hash_window(w)
+    g = LUT.view(np.float16).astype(np.float64)[idx]
+    g[neg == 1] *= -1.0
+    rng = np.random.default_rng(5)
+    for _ in range(2):
+        z = rng.standard_normal(d)
+        step_cost = [(z[2 * t] - g[:, 0]) ** 2 + (z[2 * t + 1] - g[:, 1]) ** 2 for t in range(T)]
+        order = [(k + rot) % T for k in range(T)]
+        best, arg = np.inf, []
+        chunk = 1 << 22
+        for base in range(0, 1 << (M + T * kv), chunk):
+            b = np.arange(base, base + chunk, dtype=np.int64)
+            tot = step_cost[order[0]][b & 0xFFFF]
+            for k in range(1, T):
+                tot = tot + step_cost[order[k]][(b >> (kv * k)) & 0xFFFF]
+            m = tot.min()
+            if m < best:
+                best, arg = m, list(base + np.nonzero(tot == m)[0])
+            elif m == best:
+                arg += list(base + np.nonzero(tot == m)[0])
+        assert len(arg) == 1  # a unique best path for these seeds: no tie rule involved
+        w_best = (int(arg[0]) >> (kv * (T - rot))) & ((1 << M) - 1)
+        heur = oracle.tcq_encode(z, d, kv, LUT, oracle.ENC_HEURISTIC)
+        w_code = (_code_int(heur.code) >> (N - M)) & ((1 << M) - 1)
+        assert w_code == w_best
+
+
 def test_norm_restoring_scale():
     # alpha = ||e|| / ||f(c)|| (onedev.kr, "How it differs"): with the exact
     # alpha the rebuilt row has the original norm; with the stored bf16 alpha
