@@ -70,8 +70,8 @@ struct Tcq {
     // threads per workgroup. At kv 5 and 6 a workgroup of 512 holds two next
     // memories per thread or more (so kv 6 can pair them, below) and two
     // workgroups share a CU; at kv 4 the LDS admits one workgroup either way
-    // and 1,024 threads hide more latency; kv 3 has only 8 predecessors per
-    // group for its 8 successors per thread. Measured on 4,096 rows at
+    // and 1,024 threads hide more latency; kv 3 with 512 threads would need
+    // 16 next memories per thread, more than a group's 8. Measured on 4,096 rows at
     // d = 512 (ms with 1,024 / 512 threads): kv 4: 31.4 / 35.1; kv 5: 30.7 /
     // 26.0; kv 6: 37.1 (unpaired) / 26.8.
     static constexpr uint32_t NT = KV >= 5 ? 512 : kMaxThreads;
@@ -89,27 +89,23 @@ struct Tcq {
     // s flips bit 15 of s*s + s and changes only higher bits otherwise) and
     // carry opposite signs, so both branch costs share the key
     // idx ^ (sign << 8). With the costs stored by key (the sign in the low
-    // position) one 16-byte load fetches the pair. PAIR: a thread holds its
-    // successors in such pairs, u and u + BR/2 (needs IPT >= 2).
-    static constexpr bool PAIR = IPT >= 2;
-    static constexpr uint32_t H = PAIR ? IPT / 2 : IPT;  // cost loads per predecessor
-    static_assert(IPT >= 1 && TPG * G == NT && NT >= 512 && NT <= kMaxThreads, "thread mapping");
+    // position) one 16-byte load fetches the pair. A thread holds its
+    // successors in such pairs, u and u + BR/2, which needs IPT >= 2.
+    static constexpr uint32_t H = IPT / 2;             // cost loads per predecessor
+    static_assert(IPT >= 2 && TPG * G == NT && NT >= 512 && NT <= kMaxThreads, "thread mapping");
 
     // successor u of slot i of thread slot tq (tq = tid / G)
     static __device__ __forceinline__ uint32_t succ(uint32_t tq, uint32_t i)
     {
-        if constexpr (PAIR)
-            return i < H ? tq * H + i : tq * H + (i - H) + BR / 2;
-        else
-            return tq * IPT + i;
+        return i < H ? tq * H + i : tq * H + (i - H) + BR / 2;
     }
 };
 
 template <int KV>
 struct Shared {
     double D[2][Tcq<KV>::SP];
-    // branch costs of one step: entry (2 idx + negated) * CC + copy, or with
-    // PAIR ((idx ^ negated << 8) * CC + copy) * 2 + negated
+    // branch costs of one step, entry ((idx ^ negated << 8) * CC + copy) * 2
+    // + negated
     alignas(16) double cost[2][1024 * Tcq<KV>::CC];
     double z[512];
     uint32_t lut[512];
@@ -121,9 +117,8 @@ struct Shared {
 };
 
 // cost of the pair g = +-LUT[idx]: (z0 - g0)^2 + (z1 - g1)^2, for every copy
-// c, at (2 idx + neg) * CC + c, or with PAIR at
-// ((idx ^ neg << 8) * CC + c) * 2 + neg; entry i = 2 idx + neg.
-template <uint32_t CC, bool PAIR>
+// c, at ((idx ^ neg << 8) * CC + c) * 2 + neg; i = 2 idx + neg.
+template <uint32_t CC>
 __device__ __forceinline__ void fill_cost(double *cost, const uint32_t *lut, double z0, double z1, uint32_t i)
 {
     const uint32_t e = lut[i >> 1];
@@ -134,22 +129,17 @@ __device__ __forceinline__ void fill_cost(double *cost, const uint32_t *lut, dou
     }
     const double e0 = z0 - g0, e1 = z1 - g1;
     const double c = e0 * e0 + e1 * e1;
-    if constexpr (PAIR) {
-        const uint32_t key = (i >> 1) ^ ((i & 1u) << 8);
+    const uint32_t key = (i >> 1) ^ ((i & 1u) << 8);
 #pragma unroll
-        for (uint32_t k = 0; k < CC; ++k) cost[(key * CC + k) * 2 + (i & 1u)] = c;
-    } else {
-#pragma unroll
-        for (uint32_t k = 0; k < CC; ++k) cost[i * CC + k] = c;
-    }
+    for (uint32_t k = 0; k < CC; ++k) cost[(key * CC + k) * 2 + (i & 1u)] = c;
 }
 
-template <uint32_t CC, bool PAIR, uint32_t NT>
+template <uint32_t CC, uint32_t NT>
 __device__ __forceinline__ void fill_costs(double *cost, const uint32_t *lut, double z0, double z1)
 {
 #pragma unroll
     for (uint32_t i = threadIdx.x; i < 1024; i += NT)
-        fill_cost<CC, PAIR>(cost, lut, z0, z1, i);
+        fill_cost<CC>(cost, lut, z0, z1, i);
 }
 
 // One store of a thread's IPT back-pointers (consecutive bytes).
@@ -172,24 +162,20 @@ __device__ __forceinline__ void store_bp(uint8_t *p, const uint32_t *br)
 
 // Thread mapping: thread tid serves group L = tid mod G (the next memories
 // m2 = L | u << (M - kv) share the predecessors L << kv | r) and its IPT
-// successors u = succ(tid / G, i): (tid / G) * IPT + i, or with PAIR the
-// pairs u, u + BR/2 for u = (tid / G) * IPT/2 + j. Consecutive lanes thus
-// take consecutive groups, whose windows differ in their low bits, which
-// spreads the branch cost gathers over the LDS banks (lanes sharing a group
-// would read costs at indices that agree in their low bits). A thread stores the back-pointers of
-// its IPT next memories as IPT consecutive bytes at tid * IPT; this is the
-// position of next memory m2 within one step's S bytes.
+// successors u = succ(tid / G, i), the pairs u, u + BR/2 for
+// u = (tid / G) * IPT/2 + j. Consecutive lanes thus take consecutive groups,
+// whose windows differ in their low bits, which spreads the branch cost
+// gathers over the LDS banks (lanes sharing a group would read costs at
+// indices that agree in their low bits). A thread stores the back-pointers
+// of its IPT next memories as IPT consecutive bytes at tid * IPT; this is
+// the position of next memory m2 within one step's S bytes.
 template <int KV>
 __device__ __forceinline__ uint32_t bp_pos(uint32_t m2)
 {
     using P = Tcq<KV>;
     const uint32_t L = m2 & (P::G - 1), u = m2 >> (P::M - KV);
-    if constexpr (P::PAIR) {
-        const uint32_t lo = u & (P::BR / 2 - 1);
-        return ((lo / P::H) * P::G + L) * P::IPT + lo % P::H + (u >= P::BR / 2 ? P::H : 0u);
-    } else {
-        return ((u / P::IPT) * P::G + L) * P::IPT + u % P::IPT;
-    }
+    const uint32_t lo = u & (P::BR / 2 - 1);
+    return ((lo / P::H) * P::G + L) * P::IPT + lo % P::H + (u >= P::BR / 2 ? P::H : 0u);
 }
 
 typedef double dbl2 __attribute__((ext_vector_type(2)));
@@ -201,25 +187,15 @@ __device__ __forceinline__ void load_costs(double *cv, const double *cst, uint32
                                            uint32_t cpy)
 {
     using P = Tcq<KV>;
-    if constexpr (P::PAIR) {
-        const dbl2 *c2 = reinterpret_cast<const dbl2 *>(cst);
+    const dbl2 *c2 = reinterpret_cast<const dbl2 *>(cst);
 #pragma unroll
-        for (uint32_t j = 0; j < P::H; ++j) {
-            const uint32_t u = P::succ(tq, j);  // below BR/2: sign bit clear
-            const uint32_t s = (L << KV) | (u << P::M) | r;
-            const uint32_t h = s * s + s;
-            const dbl2 c = c2[((h >> 7) & 511u) * P::CC + cpy];
-            cv[j] = c.x;
-            cv[j + P::H] = c.y;
-        }
-    } else {
-#pragma unroll
-        for (uint32_t i = 0; i < P::IPT; ++i) {
-            const uint32_t u = P::succ(tq, i);
-            const uint32_t s = (L << KV) | (u << P::M) | r;
-            const uint32_t h = s * s + s;
-            cv[i] = cst[(((h >> 6) & 0x3FEu) | (u >> (KV - 1))) * P::CC + cpy];
-        }
+    for (uint32_t j = 0; j < P::H; ++j) {
+        const uint32_t u = P::succ(tq, j);  // below BR/2: sign bit clear
+        const uint32_t s = (L << KV) | (u << P::M) | r;
+        const uint32_t h = s * s + s;
+        const dbl2 c = c2[((h >> 7) & 511u) * P::CC + cpy];
+        cv[j] = c.x;
+        cv[j + P::H] = c.y;
     }
 }
 
@@ -235,7 +211,7 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
     const uint32_t cpy = tid & (P::CC - 1);
     for (uint32_t m = tid; m < P::S; m += P::NT)
         sh.D[0][pad(m)] = (start < 0 || (int32_t)m == start) ? 0.0 : __builtin_inf();
-    fill_costs<P::CC, P::PAIR, P::NT>(sh.cost[0], sh.lut, sh.z[2 * (rot % T)], sh.z[2 * (rot % T) + 1]);
+    fill_costs<P::CC, P::NT>(sh.cost[0], sh.lut, sh.z[2 * (rot % T)], sh.z[2 * (rot % T) + 1]);
     __syncthreads();
     int cur = 0;
     for (uint32_t k = 0; k < T; ++k) {
@@ -276,7 +252,7 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
         store_bp<P::IPT>(bp + (uint64_t)k * P::S + tid * P::IPT, br);
         if (k + 1 < T) {
             const uint32_t t1 = (k + 1 + rot) % T;
-            fill_costs<P::CC, P::PAIR, P::NT>(sh.cost[(k + 1) & 1], sh.lut, sh.z[2 * t1], sh.z[2 * t1 + 1]);
+            fill_costs<P::CC, P::NT>(sh.cost[(k + 1) & 1], sh.lut, sh.z[2 * t1], sh.z[2 * t1 + 1]);
         }
         __syncthreads();
         cur ^= 1;
