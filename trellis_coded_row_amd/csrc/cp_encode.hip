@@ -305,6 +305,43 @@ __device__ __forceinline__ uint32_t argmin_memory(Shared<KV> &sh, const double *
     return r;
 }
 
+// Walk of the back-pointers from the next memory `end` after the last step
+// down to step 0, run by one whole wave (every lane follows the same path).
+// Two steps per load latency: while the back-pointer r of step k loads, lane
+// j < BR loads the back-pointer at step k - 1 of the memory that r = j leads
+// to, and r then picks the lane. Returns the memory held after step kw; with
+// `emit` sets each step's kv new bits in the code.
+template <int KV>
+__device__ __forceinline__ uint32_t walk_back(const uint8_t *bp, uint32_t T, uint32_t end, uint32_t kw, bool emit,
+                                              uint8_t *code)
+{
+    using P = Tcq<KV>;
+    const uint32_t lane = threadIdx.x & 63u;
+    uint32_t m2 = end, w = 0;
+    auto step = [&](uint32_t k, uint32_t r) {
+        if (k == kw) w = m2;
+        const uint32_t s = ((m2 << KV) | r) & 0xFFFFu;
+        if (emit && lane == 0) {
+            const uint32_t u = s >> P::M;
+            for (uint32_t i = 0; i < (uint32_t)KV; ++i)
+                if ((u >> i) & 1u) {
+                    const uint32_t j = KV * k + i;
+                    code[j >> 3] |= (uint8_t)(1u << (j & 7));
+                }
+        }
+        m2 = s & (P::S - 1);
+    };
+    for (int32_t k = (int32_t)T - 1; k >= 0; k -= 2) {
+        const uint32_t rk = bp[(uint64_t)k * P::S + bp_pos<KV>(m2)];
+        uint32_t cand = 0;
+        if (k >= 1 && lane < P::BR)
+            cand = bp[(uint64_t)(k - 1) * P::S + bp_pos<KV>(((m2 << KV) | lane) & (P::S - 1))];
+        step((uint32_t)k, rk);
+        if (k >= 1) step((uint32_t)k - 1, (uint32_t)__shfl((int)cand, (int)rk, 64));
+    }
+    return w;
+}
+
 template <int KV>
 __global__ __launch_bounds__(Tcq<KV>::NT) __attribute__((amdgpu_waves_per_eu(4))) void tcq_encode_rows(const float *__restrict__ e, uint64_t nrows,
                                                             uint32_t d, const uint32_t *__restrict__ lut,
@@ -346,23 +383,9 @@ __global__ __launch_bounds__(Tcq<KV>::NT) __attribute__((amdgpu_waves_per_eu(4))
             for (int p = 0; p < 2; ++p) {
                 const int cend = viterbi_pass<KV>(sh, T, p == 0 ? -1 : (int32_t)W, p == 0 ? rot : 0, bp);
                 const uint32_t end = p == 0 ? argmin_memory<KV>(sh, sh.D[cend]) : W;
-                if (tid == 0) {
-                    uint32_t m2 = end, w = 0;
-                    for (int32_t k = (int32_t)T - 1; k >= 0; --k) {
-                        if ((uint32_t)k == T - rot - 1) w = m2;
-                        const uint32_t r = bp[(uint64_t)k * P::S + bp_pos<KV>(m2)];
-                        const uint32_t s = ((m2 << KV) | r) & 0xFFFFu;
-                        if (p == 1) {
-                            const uint32_t u = s >> P::M;
-                            for (uint32_t i = 0; i < (uint32_t)KV; ++i)
-                                if ((u >> i) & 1u) {
-                                    const uint32_t j = KV * (uint32_t)k + i;
-                                    sh.code[j >> 3] |= (uint8_t)(1u << (j & 7));
-                                }
-                        }
-                        m2 = s & (P::S - 1);
-                    }
-                    sh.W = w;
+                if (tid < 64) {
+                    const uint32_t w = walk_back<KV>(bp, T, end, T - rot - 1, p == 1, sh.code);
+                    if (tid == 0) sh.W = w;
                 }
                 __syncthreads();
                 if (p == 0) W = sh.W;
