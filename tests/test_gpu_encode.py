@@ -53,7 +53,12 @@ def check_records(got: np.ndarray, exp: np.ndarray, label: str) -> None:
     (64, 6, 129),
     (64, 5, 1100),  # kv 5 and 6 run two 512-thread workgroups per CU: past 512 rows
     (64, 6, 1100),
+    (128, 3, 41),
     (128, 4, 97),
+    (128, 5, 45),
+    (128, 6, 39),
+    (256, 3, 23),
+    (256, 4, 29),
     (256, 5, 33),
     (256, 6, 31),
     (512, 3, 19),
