@@ -310,7 +310,8 @@ __device__ __forceinline__ uint32_t argmin_memory(Shared<KV> &sh, const double *
 // Two steps per load latency: while the back-pointer r of step k loads, lane
 // j < BR loads the back-pointer at step k - 1 of the memory that r = j leads
 // to, and r then picks the lane. Returns the memory held after step kw; with
-// `emit` sets each step's kv new bits in the code.
+// `emit` sets each step's kv new bits in the code, without it the walk ends
+// once step kw is reached.
 template <int KV>
 __device__ __forceinline__ uint32_t walk_back(const uint8_t *bp, uint32_t T, uint32_t end, uint32_t kw, bool emit,
                                               uint8_t *code)
@@ -332,6 +333,7 @@ __device__ __forceinline__ uint32_t walk_back(const uint8_t *bp, uint32_t T, uin
         m2 = s & (P::S - 1);
     };
     for (int32_t k = (int32_t)T - 1; k >= 0; k -= 2) {
+        if (!emit && (uint32_t)k < kw) break;  // step kw is done: w is set
         const uint32_t rk = bp[(uint64_t)k * P::S + bp_pos<KV>(m2)];
         uint32_t cand = 0;
         if (k >= 1 && lane < P::BR)
