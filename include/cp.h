@@ -24,8 +24,12 @@
  *     of the circular code, oldest bit lowest (tail-biting: indices mod N);
  *   - h = (s*s + s) mod 2^32, idx = (h >> 7) & 511; outputs 2t and 2t+1 are
  *     LUT[idx][0] and LUT[idx][1] (fp16), both negated when bit 15 of s is 1;
- *   - e_hat = bf16_rne(alpha * f), the product formed exactly (bf16 x fp16
- *     fits in fp32) and rounded once to nearest even.
+ *   - e_hat = bf16_rne(alpha * f): the exact product rounded once to nearest
+ *     even. A bf16 times an fp16 has at most 19 significant bits, so the
+ *     kernels form it in fp32, where it is exact unless it lies below 2^-126;
+ *     rows whose scale is below 2^-102 (the only ones where that can happen)
+ *     are rounded from a copy scaled by 2^64 instead, so every row is the
+ *     single rounding of the exact product.
  *
  * Record layout (this library's choice): N/8 code bytes, then alpha as a
  * little-endian bf16; records packed back to back with no padding, record i
@@ -125,13 +129,19 @@ int cp_supported(uint32_t d, uint32_t bits_per_step);
 /* Creates a table on the current HIP device.
  *   desc     - shape and residency; copied.
  *   lut_fp16 - host pointer to the shared codebook, 512 x 2 fp16 bit patterns
- *              (entry idx: lut_fp16[2*idx], lut_fp16[2*idx+1]); copied.
+ *              (entry idx: lut_fp16[2*idx], lut_fp16[2*idx+1]); copied. Every
+ *              entry must be finite (the codebook of a Gaussian trellis).
  *   out      - receives the table handle (NULL on failure).
- * The records are uninitialised until cp_table_upload fills them; device
- * memory is rows * R bytes (+ a small zeroed tail), pinned host memory the
- * same for CP_RESIDENCY_HOST_MAPPED.
+ * The records are not passed here: the table is created empty and
+ * cp_table_upload (or cp_table_encode) fills it, in as many row ranges as the
+ * caller likes, so a table of many GB never needs a second full copy in host
+ * memory. They are uninitialised until then; device memory is rows * R bytes
+ * (+ a small zeroed tail), pinned host memory the same for
+ * CP_RESIDENCY_HOST_MAPPED.
  * Errors: INVALID_ARGUMENT (NULL pointers, struct_size, rows == 0, unknown
- * residency or flags), UNSUPPORTED, OUT_OF_MEMORY, HIP. */
+ * residency or flags, a codebook entry that is +-inf or NaN), UNSUPPORTED,
+ * OUT_OF_MEMORY (the records do not fit in device or pinned host memory; the
+ * library stays usable), HIP. */
 cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, cp_table **out);
 
 /* Creates a mixed-rate table on the current HIP device.
@@ -148,7 +158,8 @@ cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, c
  * rows' own sizes); cp_table_encode codes each row at its own class's rate;
  * cp_table_describe reports bits_per_step = 0; cp_lookup_decode_dedup returns
  * UNSUPPORTED.
- * Errors: INVALID_ARGUMENT (NULL pointers, struct_size, rows == 0, nclass,
+ * Errors: INVALID_ARGUMENT (NULL pointers, struct_size, rows == 0, nclass, a
+ * codebook entry that is +-inf or NaN,
  * a class's rate without whole-byte records, a nonzero unused rate, a row
  * class >= nclass, residency or flags), UNSUPPORTED (no kernel for d or a
  * rate), OUT_OF_MEMORY, HIP. */
@@ -174,7 +185,10 @@ cp_status cp_table_upload(cp_table *table, uint64_t first_row, uint64_t nrows, c
  *            16-byte aligned; fully overwritten.
  *   stream - hipStream_t to launch on (NULL: the null stream). Asynchronous:
  *            returns after the launch; synchronise the stream before reading.
- * Duplicate ids decode once per occurrence. n == 0 launches nothing.
+ * Duplicate ids decode once per occurrence. n == 0 launches nothing; any
+ * larger n is accepted (beyond 2^31 - 1 workgroups the kernel's chunk loop
+ * strides over the rest). The call allocates nothing and does not
+ * synchronise, so it may be captured in a HIP graph.
  * Errors: INVALID_ARGUMENT (NULL table, NULL ids/out with n > 0, misaligned
  * out), HIP (launch failure). Bad ids: see the error convention above. */
 cp_status cp_lookup_decode(const cp_table *table, const int64_t *ids, uint64_t n, uint16_t *out,
@@ -235,9 +249,9 @@ uint64_t cp_encode_workspace_bytes(const cp_table *table, uint64_t nrows);
  * heuristic: a pass from every start over the steps rotated by half a row
  * picks the start memory, a pass from that memory alone picks the code. All
  * arithmetic is fp64 in a fixed order with fixed tie rules, so the records
- * are fully determined by the input. A row with zero norm is stored as the
- * all-zero code with alpha = 0. Rows must be finite (otherwise the record is
- * unspecified).
+ * are fully determined by the input. A row whose norm is zero or not finite
+ * (a row of zeros, or one holding an inf or a NaN) is stored as the all-zero
+ * code with alpha = 0. A scale too large for bf16 is stored as +inf.
  *   rows      - device fp32[nrows][d], 4-byte aligned; read only.
  *   workspace - device memory, 256-byte aligned, at least
  *               cp_encode_workspace_bytes(table, nrows) bytes, caller-owned

@@ -573,8 +573,9 @@ double cpo_distortion(const double *z, const uint16_t *lut, const uint8_t *code,
  * Encodes one row e (length d) into a packed record [KO "How it differs"]:
  * z = sqrt(d) e / ||e||; tail-biting TCQ of z; f(c) recomputed by decoding the
  * emitted code; alpha = ||e|| / ||f(c)|| in fp64, rounded once to bf16;
- * record = code bytes then alpha (R5). A zero row gets an all-zero code and
- * alpha = 0. alpha_exact (optional) receives the unrounded fp64 alpha.
+ * record = code bytes then alpha (R5). A row whose norm is zero or not finite
+ * gets an all-zero code and alpha = 0. alpha_exact (optional) receives the
+ * unrounded fp64 alpha.
  */
 int cpo_encode_row(const double *e, uint32_t d, uint32_t kv, const uint16_t *lut, int mode,
                    uint32_t max_starts, uint8_t *record, cpo_encode_info *info,
@@ -589,7 +590,11 @@ int cpo_encode_row(const double *e, uint32_t d, uint32_t kv, const uint16_t *lut
     if (!z) return -2;
     memset(record, 0, nbits / 8 + 2);
     double alpha = 0.0;
-    if (norm > 0.0) {
+    /* z = sqrt(d) e / ||e|| and alpha = ||e|| / ||f(c)|| [KO "How it
+     * differs"] are defined for a finite nonzero norm only. A row of zeros, or
+     * one holding an inf or a NaN (norm inf or NaN), is stored as the all-zero
+     * code with alpha = 0 (a reading: the pages do not treat such rows). */
+    if (norm > 0.0 && norm < INFINITY) {
         double sd = sqrt((double)d);
         for (uint32_t i = 0; i < d; ++i) z[i] = sd * e[i] / norm;
         cpo_tcq_encode(z, d, kv, lut, mode, max_starts, record, info);

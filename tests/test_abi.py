@@ -188,3 +188,16 @@ def test_one_hip_runtime_in_the_process():
 def test_hot_rows_without_a_table():
     assert cp.cp_table_set_hot_rows(0, 0, 0) == cp.CP_ERR_INVALID_ARGUMENT
     assert cp.cp_table_hot_rows(0) == 0
+
+
+@pytest.mark.parametrize("bad", [0x7C00, 0xFC00, 0x7E00, 0xFFFF])
+def test_create_rejects_a_codebook_entry_that_is_not_finite(bad):
+    # the shared codebook of a Gaussian trellis holds finite values; +-inf and
+    # NaN entries are refused before any device memory is touched
+    lut = (ctypes.c_uint16 * 1024)()
+    lut[517] = bad
+    st, h = cp.cp_table_create(_desc(), ctypes.addressof(lut))
+    assert (st, h) == (cp.CP_ERR_INVALID_ARGUMENT, 0)
+    cls = (ctypes.c_uint8 * 8)(0, 1, 0, 1, 1, 1, 0, 0)
+    st, h = cp.cp_table_create_mixed(_mdesc(), ctypes.addressof(lut), ctypes.addressof(cls))
+    assert (st, h) == (cp.CP_ERR_INVALID_ARGUMENT, 0)

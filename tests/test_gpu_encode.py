@@ -13,7 +13,7 @@ import torch
 import oracle
 import trellis_coded_row_amd as cp
 import workload
-from parity import assert_bit_exact, check_lookup, say
+from parity import assert_bit_exact, assert_scaled_matches, check_lookup, device_lookup, say
 
 pytestmark = pytest.mark.gpu
 
@@ -72,16 +72,22 @@ def test_encode_matches_oracle(d, kv, n):
     exp = oracle_encode(e, d, kv)
     t, got = gpu_encode(e, d, kv)
     check_records(got, exp, f"encode d{d} kv{kv}")
-    # the encoded table decodes like the oracle's records
+    # the encoded table decodes like the oracle's records (the oracle decodes
+    # its own encoding, equal to the table's as just checked)
     ids = np.arange(n, dtype=np.int64)[::-1].copy()
-    check_lookup(t, LUT, got, d, kv, ids, f"decode of encoded d{d} kv{kv}")
+    check_lookup(t, LUT, exp, d, kv, ids, f"decode of encoded d{d} kv{kv}")
     t.close()
     say(f"encode d={d} kv={kv} n={n}: ok")
 
 
-def test_encode_special_rows():
-    d, kv = 64, 4
+@pytest.mark.parametrize("d", [64, 512])
+def test_encode_special_rows(d):
+    kv = 4
     rng = np.random.default_rng(77)
+    with_inf = rng.standard_normal(d)
+    with_inf[3] = np.inf
+    with_nan = rng.standard_normal(d)
+    with_nan[d - 1] = np.nan
     rows = [
         np.zeros(d),                                   # zero row: zero code, alpha 0
         np.eye(d)[5] * 3.0,                            # one non-zero coordinate
@@ -90,15 +96,26 @@ def test_encode_special_rows():
         rng.standard_normal(d) * 3e37,                 # large values, alpha near the bf16 top
         np.full(d, 3.3e38),                            # alpha rounds past the largest bf16
         -np.full(d, 1.0),
+        with_inf,                                      # norm not finite: the zero record
+        with_nan,
+        -with_inf,
         rng.standard_normal(d),
     ]
     e = np.stack(rows).astype(np.float32)
     e = np.concatenate([e, e[::-1]])                   # duplicates in another order
     say(f"encode special rows d={d} kv={kv} n={e.shape[0]}")
     exp = oracle_encode(e, d, kv)
-    assert (exp[0] == 0).all()
+    assert (exp[0] == 0).all() and (exp[7:10] == 0).all()
     t, got = gpu_encode(e, d, kv)
     check_records(got, exp, "special rows")
+    # and the rows decode like the oracle's, raw and scaled (alpha a bf16
+    # subnormal, +inf, 0): bit-exact, NaN where the oracle has NaN
+    ids = np.arange(e.shape[0], dtype=np.int64)
+    n = e.shape[0]
+    exp_raw, _ = oracle.lookup_decode(LUT, exp, n, d, kv, ids, raw=True)
+    exp_rows, _ = oracle.lookup_decode(LUT, exp, n, d, kv, ids)
+    assert_bit_exact(device_lookup(t, ids, raw=True), exp_raw, "special rows f(c)")
+    assert_scaled_matches(device_lookup(t, ids), exp_rows, "special rows scaled")
     t.close()
 
 

@@ -14,7 +14,7 @@ import torch
 import oracle
 import trellis_coded_row_amd as cp
 import workload
-from parity import assert_bf16_within_ulp, assert_bit_exact, make_table, say, shape_change_sizes
+from parity import assert_scaled_matches, assert_bit_exact, make_table, say, shape_change_sizes
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def replay_and_compare(step, out, expected, label, exact=False):
         if exact:
             assert_bit_exact(got, expected, f"{label} replay {r}")
         else:
-            assert_bf16_within_ulp(got, expected, f"{label} replay {r}")
+            assert_scaled_matches(got, expected, f"{label} replay {r}")
     say(f"{label}: {REPLAYS} graph replays match the oracle")
     del g
 

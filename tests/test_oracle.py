@@ -7,6 +7,7 @@ conversions), an algebraic invariant of the trellis, or exhaustive search.
 from __future__ import annotations
 
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -501,3 +502,242 @@ def test_rank_classes_follow_access_rank():
     ids = workload.zipf_ids(rows, 50_000, seed=202)
     share = np.bincount(cls[ids], minlength=4) / ids.size
     assert share[0] > 0.8 and share[3] < 0.05  # hot rows are the high-rate ones
+
+
+# ---------------------------------------------------------------------------
+# tie rule of the encoder, pinned by brute force over paths
+# ---------------------------------------------------------------------------
+
+def _window_costs(lut: np.ndarray, z: np.ndarray, T: int) -> list[np.ndarray]:
+    """Branch cost of every 16-bit window at each step t, as the oracle forms
+    it ((z0 - g0)^2 + (z1 - g1)^2 in fp64, g the signed codebook pair), from
+    the hash written out here."""
+    w = np.arange(1 << 16, dtype=np.int64)
+    idx, neg = ((w * w + w) % (1 << 32) >> 7) & 511, (w >> 15) & 1
+    g = lut.view(np.float16).astype(np.float64)[idx]
+    g[neg == 1] *= -1.0
+    return [(z[2 * t] - g[:, 0]) ** 2 + (z[2 * t + 1] - g[:, 1]) ** 2 for t in range(T)]
+
+
+def _assert_exact(lut: np.ndarray, z: np.ndarray, costs: list[np.ndarray]) -> None:
+    """The premise of the tie derivation: every cost is the exact value of
+    its formula, a multiple of 2^-44 below 2^7, so every sum of four of them
+    is exact in fp64 and "optimal" does not depend on the order of addition."""
+    w = np.arange(1 << 16, dtype=np.int64)
+    idx, neg = ((w * w + w) % (1 << 32) >> 7) & 511, (w >> 15) & 1
+    g = lut.view(np.float16).astype(np.float64)[idx]
+    g[neg == 1] *= -1.0
+    for t, c in enumerate(costs):
+        e0, e1 = z[2 * t] - g[:, 0], z[2 * t + 1] - g[:, 1]
+        # differences and squares exact (few-bit z, fp16 g); the sum exact
+        # when its rounding error (TwoSum) is zero
+        assert ((e0 + g[:, 0]) == z[2 * t]).all() and ((e1 + g[:, 1]) == z[2 * t + 1]).all()
+        a, b = e0 * e0, e1 * e1
+        bb = c - a
+        assert ((a - (c - bb)) + (b - bb) == 0).all()
+        q = c * 2.0**44
+        assert (q == np.floor(q)).all() and (c < 128).all()
+
+
+def _free_start_sums(costs, order, chunk=1 << 22):
+    """Yields (base, sums) over every free-start path b of 28 bits at d = 8,
+    kv = 4: b's bits [4k, 4k + 16) are the window of the k-th visited step
+    (bits 0..11 the start memory), sums[b - base] its cost."""
+    for base in range(0, 1 << 28, chunk):
+        b = np.arange(base, base + chunk, dtype=np.int64)
+        tot = costs[order[0]][b & 0xFFFF]
+        for k in range(1, 4):
+            tot = tot + costs[order[k]][(b >> (4 * k)) & 0xFFFF]
+        yield base, tot
+
+
+def _tie_lut(kind: str) -> np.ndarray:
+    """Codebooks under which many paths cost the same: "paired" makes
+    entries 2j and 2j + 1 equal; "constant" gives every entry (1, -0.5), so
+    a window's cost depends on its sign bit alone; "two-valued" gives even
+    and odd entries two different pairs."""
+    if kind == "gaussian":
+        return LUT
+    lut = LUT.copy()
+    if kind == "paired":
+        lut[1::2] = lut[0::2]
+    elif kind == "constant":
+        lut[:] = [0x3C00, 0xB800]
+    else:
+        lut[0::2] = [0x3C00, 0xB800]
+        lut[1::2] = [0xBA00, 0x3E00]
+    return lut
+
+
+@pytest.mark.parametrize("lut_kind,z", [
+    ("gaussian", np.zeros(8)),                      # every window ties with its complement
+    ("paired", np.zeros(8)),
+    ("constant", np.array([0.5, -1.25, 0, 0, 0, 0, 1.0, 0])),
+    ("two-valued", np.array([2.0, 0, 0, 0.75, -1.0, 0, 0.25, 0.5])),
+], ids=["gaussian-zero", "paired-zero", "constant-sparse", "two-valued"])
+def test_encoder_tie_rule_matches_brute_force_over_paths(lut_kind, z):
+    """The encoders keep, among equal path metrics, the smallest predecessor r
+    (the oldest kv bits of the window) at each step, and the smallest end
+    memory in the start-finding pass. With exact arithmetic every optimal
+    path has optimal prefixes, so walking back from the end and taking the
+    smallest r that stays optimal picks, among all optimal paths ending in
+    that memory, the one whose r's read from the last step back are smallest
+    in lexicographic order. At d = 8, kv = 4 a free-start path is a 28-bit
+    string b whose k-th visited window is bits [4k, 4k + 16), so r_k = bits
+    [4k, 4k + 4) and the end memory = bits [16, 28): that order is the order
+    of b as an integer. So the start-finding pass picks the smallest b of
+    least cost, and the code pass (start memory fixed: only the first step's
+    4 bits are free) the smallest code of least cost. Derived here by
+    enumeration, not by calling the encoder."""
+    d, kv, T = 8, 4, 4
+    lut = _tie_lut(lut_kind)
+    costs = _window_costs(lut, z, T)
+    _assert_exact(lut, z, costs)
+    rot = T // 2
+    order = [(k + rot) % T for k in range(T)]
+    best, best_b = np.inf, None
+    ties = 0
+    for base, tot in _free_start_sums(costs, order):
+        m = tot.min()
+        if m < best:
+            best, best_b, ties = m, base + int(np.argmax(tot == m)), int((tot == m).sum())
+        elif m == best:
+            ties += int((tot == m).sum())
+    # memory before step 0 = after the visited step T - rot - 1 (step T - 1)
+    k = T - rot - 1
+    w_h = (best_b >> (4 * k + 4)) & 0xFFF
+    # code pass: codes whose last 12 bits are w_h; windows of the closed path
+    # b' = w_h | code << 12 in natural step order
+    cand = np.arange(16, dtype=np.int64) | (w_h << 4)
+    bp = (cand >> 4) | (cand << 12)
+    tot = sum(costs[t][(bp >> (4 * t)) & 0xFFFF] for t in range(T))
+    code = int(cand[int(np.argmax(tot == tot.min()))])
+    # the case has ties for the rule to decide
+    assert ties > 1
+    heur = oracle.tcq_encode(z, d, kv, lut, oracle.ENC_HEURISTIC)
+    assert _code_int(heur.code) == code
+    assert heur.cost == tot.min()
+
+    # exact mode: the heuristic's code is the incumbent and a start replaces
+    # it only when strictly better; starts are tried by increasing free-start
+    # bound, then by memory
+    allc = np.arange(1 << 16, dtype=np.int64)
+    ball = (allc >> 4) | (allc << 12)
+    closed = sum(costs[t][(ball >> (4 * t)) & 0xFFFF] for t in range(T))
+    gmin = closed.min()
+    exact = oracle.tcq_encode(z, d, kv, lut, oracle.ENC_EXACT)
+    assert exact.cost == gmin
+    if tot.min() == gmin:
+        assert _code_int(exact.code) == code
+    else:
+        F = np.full(1 << 12, np.inf)
+        for base, s_ in _free_start_sums(costs, list(range(T))):
+            ends = (np.arange(base, base + s_.size, dtype=np.int64) >> 16)
+            np.minimum.at(F, ends, s_)
+        starts = sorted(range(1 << 12), key=lambda w: (F[w], w))
+        first = next(w for w in starts if (closed[(allc >> 4) == w] == gmin).any())
+        sel = np.nonzero(((allc >> 4) == first) & (closed == gmin))[0]
+        assert _code_int(exact.code) == int(sel.min())
+
+
+# ---------------------------------------------------------------------------
+# the scaled output for tiny products, against exact rational arithmetic
+# ---------------------------------------------------------------------------
+
+def _bf16_rne_exact(q: Fraction) -> int:
+    """bf16 bits of the rational q rounded to nearest, ties to even, worked
+    out on the bf16 grid itself (spacing 2^(E-7) in binade E, 2^-133 below
+    2^-126)."""
+    sgn = 0x8000 if q < 0 else 0
+    a = abs(q)
+    if a == 0:
+        return sgn
+    E = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** E > a:
+        E -= 1
+    E = max(E, -126)
+    unit = Fraction(2) ** (E - 7)
+    k, rem = divmod(a, unit)
+    k = int(k)
+    if rem * 2 > unit or (rem * 2 == unit and k % 2 == 1):
+        k += 1
+    bits = ((E + 127) << 7) + (k - 128)
+    return sgn | min(bits, 0x7F80)
+
+
+def _fp16_fraction(h: int) -> Fraction:
+    e, m = (h >> 10) & 31, h & 1023
+    v = Fraction(m, 1 << 24) if e == 0 else Fraction(1024 + m) * Fraction(2) ** (e - 25)
+    return -v if h & 0x8000 else v
+
+
+def _bf16_fraction(b: int) -> Fraction:
+    e, m = (b >> 7) & 255, b & 127
+    v = Fraction(m) * Fraction(2) ** -133 if e == 0 else Fraction(128 + m) * Fraction(2) ** (e - 134)
+    return -v if b & 0x8000 else v
+
+
+def test_scaled_row_of_tiny_products_is_the_single_rounding_of_the_exact_product():
+    # decode_record against exact rationals where the product alpha * f falls
+    # below 2^-126 (bf16 subnormals) or near it: no intermediate fp32 rounding
+    rng = np.random.default_rng(77)
+    lut = rng.integers(0, 0x7BFF, size=1024, dtype=np.uint16)
+    lut[::7] = rng.integers(0, 0x0400, size=lut[::7].size, dtype=np.uint16)  # fp16 subnormals
+    lut[::5] |= 0x8000
+    lut[:4] = [0x0000, 0x8000, 0x0001, 0x03FF]
+    lut = lut.reshape(512, 2)
+    d, kv = 64, 4
+    nb = kv * d // 16
+    alphas = [0x0001, 0x8001, 0x007F, 0x0080, 0x00FF, 0x0100, 0x0C7F, 0x0C00, 0x0880, 0x0455]
+    checked = 0
+    for ab in alphas:
+        rec = np.empty(nb + 2, dtype=np.uint8)
+        rec[:nb] = rng.integers(0, 256, size=nb, dtype=np.uint8)
+        rec[nb], rec[nb + 1] = ab & 0xFF, ab >> 8
+        f = oracle.decode_code(lut, rec[:nb], d, kv)
+        y = oracle.decode_record(lut, rec, d, kv)
+        a = _bf16_fraction(ab)
+        for fi, yi in zip(f, y):
+            assert int(yi) == _bf16_rne_exact(a * _fp16_fraction(int(fi))), (hex(ab), hex(int(fi)))
+            checked += 1
+    assert checked == len(alphas) * d
+
+
+def test_bf16_rounding_of_subnormal_products_against_exact_rationals():
+    # every bf16 scale with a small exponent field times random fp16 values:
+    # the oracle's one-step rounding equals the exact rational rounding; also
+    # products that lie just below a midpoint of the bf16 subnormal grid
+    # (closer than fp32's spacing there), where rounding through fp32 first
+    # would end 1 ulp off
+    near_mid_bf16 = [0x00B9, 0x00CF, 0x0139, 0x014F, 0x01B9, 0x01CF, 0x0239, 0x024F, 0x02B9, 0x02CF,
+                     0x0339, 0x034F, 0x03CF, 0x044F, 0x80B9, 0x80CF, 0x8139, 0x814F, 0x81B9, 0x81CF,
+                     0x8239, 0x824F, 0x82B9, 0x82CF, 0x8339, 0x834F, 0x83CF, 0x844F]
+    near_mid_fp16 = [0x0589, 0x062F, 0x0989, 0x0A2F, 0x0D89, 0x0E2F, 0x1189, 0x122F, 0x1589, 0x162F,
+                     0x1989, 0x1A2F, 0x1E2F, 0x222F, 0x8589, 0x862F, 0x8989, 0x8A2F, 0x8D89, 0x8E2F,
+                     0x9189, 0x922F, 0x9589, 0x962F, 0x9989, 0x9A2F, 0x9E2F, 0xA22F]
+    for ab in near_mid_bf16:
+        for h in near_mid_fp16:
+            q = _bf16_fraction(ab) * _fp16_fraction(h)
+            assert oracle.bf16_from_double(float(q)) == _bf16_rne_exact(q), (hex(ab), hex(h))
+    rng = np.random.default_rng(78)
+    for ab in list(range(0, 0x1000, 37)) + [0x0001, 0x007F, 0x0080, 0x0C7F, 0x0C80]:
+        for h in rng.integers(0, 0x7C00, size=24):
+            q = _bf16_fraction(ab) * _fp16_fraction(int(h))
+            assert oracle.bf16_from_double(float(q)) == _bf16_rne_exact(q), (hex(ab), hex(int(h)))
+
+
+# ---------------------------------------------------------------------------
+# rows whose norm is not finite
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
+def test_rows_with_non_finite_norm_encode_to_the_zero_record(bad):
+    # z = sqrt(d) e / ||e|| and alpha = ||e|| / ||f(c)|| need a finite nonzero
+    # norm; a row holding an inf or a NaN is stored like a zero row
+    d, kv = 64, 4
+    e = workload.gaussian_rows(1, d, seed=31)[0]
+    e[5] = bad
+    rec, _, alpha = oracle.encode_row(e, d, kv, LUT, oracle.ENC_HEURISTIC)
+    assert alpha == 0.0 and (rec == 0).all()
+    recs, _ = oracle.encode_rows(e[None, :], d, kv, LUT, oracle.ENC_HEURISTIC)
+    assert (recs == 0).all()

@@ -78,8 +78,8 @@ _lib: ctypes.CDLL | None = None
 
 
 def library_path() -> str:
-    # CP_LIBRARY lets a tuning run load a differently-built copy of the library
-    return os.environ.get("CP_LIBRARY") or _build.LIB
+    """The in-tree libcp.so this package loads (the only one it loads)."""
+    return _build.LIB
 
 
 def load_library() -> ctypes.CDLL:
@@ -89,8 +89,6 @@ def load_library() -> ctypes.CDLL:
         return _lib
     path = library_path()
     if not os.path.exists(path):
-        if path != _build.LIB:
-            raise ImportError(f"CP_LIBRARY={path} does not exist")
         _build.build()
     L = ctypes.CDLL(path)
     vp = ctypes.c_void_p

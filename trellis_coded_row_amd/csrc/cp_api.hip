@@ -33,21 +33,29 @@ struct cp_table {
 
 static thread_local int g_last_hip_error = 0;
 
+// Records a failed HIP call's error for cp_last_hip_error and takes it off
+// the runtime's per-thread "last error", so that neither the caller's next
+// hipGetLastError nor a later launch check of this library reports it again.
 static cp_status hip_fail(hipError_t e)
 {
     g_last_hip_error = (int)e;
+    (void)hipGetLastError();
     return (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) ? CP_ERR_OUT_OF_MEMORY
                                                                          : CP_ERR_HIP;
 }
 
 // Makes the table's device current for the duration of a call and restores
 // the caller's device afterwards (launches on the null stream, copies and
-// synchronisation then all address the device that holds the table).
+// synchronisation then all address the device that holds the table). It
+// also clears the runtime's per-thread "last error" first: the launches read
+// their status with hipGetLastError, which would otherwise return an earlier
+// failure of an unrelated call as their own.
 struct DeviceGuard {
     int prev = -1;
     hipError_t err = hipSuccess;
     explicit DeviceGuard(int dev)
     {
+        (void)hipGetLastError();
         int cur = -1;
         err = hipGetDevice(&cur);
         if (err == hipSuccess && cur != dev) {
@@ -150,6 +158,16 @@ static cp_status allocate(cp_table *t, const uint16_t *lut_fp16)
     return e == hipSuccess ? CP_OK : hip_fail(e);
 }
 
+// The shared codebook holds the values of a Gaussian trellis (onedev.kr
+// digest, "How it differs"): every entry must be a finite fp16 (exponent
+// field below 31), which the tiny-scale arithmetic of the kernels relies on.
+static bool finite_codebook(const uint16_t *lut_fp16)
+{
+    for (int i = 0; i < 1024; ++i)
+        if ((lut_fp16[i] & 0x7C00u) == 0x7C00u) return false;
+    return true;
+}
+
 static bool valid_residency(uint32_t residency, uint32_t flags)
 {
     if (residency != CP_RESIDENCY_DEVICE && residency != CP_RESIDENCY_HOST_MAPPED) return false;
@@ -162,7 +180,7 @@ cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, c
     if (!desc || !lut_fp16 || !out) return CP_ERR_INVALID_ARGUMENT;
     if (desc->struct_size != sizeof(cp_table_desc) || desc->rows == 0 || desc->reserved != 0)
         return CP_ERR_INVALID_ARGUMENT;
-    if (!valid_residency(desc->residency, desc->flags)) return CP_ERR_INVALID_ARGUMENT;
+    if (!valid_residency(desc->residency, desc->flags) || !finite_codebook(lut_fp16)) return CP_ERR_INVALID_ARGUMENT;
     const uint64_t R = cp_record_bytes(desc->d, desc->bits_per_step);
     if (R == 0) return CP_ERR_INVALID_ARGUMENT;
     if (!cpk::supported(desc->d, desc->bits_per_step)) return CP_ERR_UNSUPPORTED;
@@ -190,7 +208,7 @@ cp_status cp_table_create_mixed(const cp_mixed_desc *desc, const uint16_t *lut_f
     if (desc->struct_size != sizeof(cp_mixed_desc) || desc->rows == 0 || desc->reserved != 0)
         return CP_ERR_INVALID_ARGUMENT;
     if (desc->nclass < 1 || desc->nclass > 4) return CP_ERR_INVALID_ARGUMENT;
-    if (!valid_residency(desc->residency, desc->flags)) return CP_ERR_INVALID_ARGUMENT;
+    if (!valid_residency(desc->residency, desc->flags) || !finite_codebook(lut_fp16)) return CP_ERR_INVALID_ARGUMENT;
     uint32_t R[4] = {0, 0, 0, 0};
     for (uint32_t c = 0; c < desc->nclass; ++c) {
         R[c] = (uint32_t)cp_record_bytes(desc->d, desc->bits_per_step[c]);

@@ -125,33 +125,55 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
         const uint64_t okmask = __ballot(ok);
         my_id = load_id(c + waves);
 
+        // Code bits of lane l, and the scale (fp32 bits), of the record at
+        // byte offset o.
+        auto row_bits = [&](uint64_t o) -> uint32_t {
+            if constexpr (KV == 4) {
+                // lane l's 16 new bits are code half-word l (records are 2-byte aligned)
+                return *reinterpret_cast<const uint16_t *>(tab + o + 2u * l);
+            } else {
+                const uint64_t bit = o * 8 + (uint64_t)NEWB * l;
+                const uint8_t *p = tab + ((bit >> 5) << 2);
+                const uint64_t both = ((uint64_t)ld32(p + 4) << 32) | ld32(p);
+                return (uint32_t)(both >> (bit & 31)) & ((1u << NEWB) - 1u);
+            }
+        };
+        auto row_scale = [&](uint64_t o) -> uint32_t {
+            const uint64_t ao = o + NB;  // bf16 at bytes [NB, NB + 2)
+            const uint32_t adw = ld32(tab + (ao & ~(uint64_t)3));
+            return ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16;
+        };
+        // record offset of the row that lane group g decodes i-th in the chunk
+        auto row_offset = [&](uint32_t i) -> uint64_t {
+            if constexpr (GROUPS == 1) return readlane_u64(my_off, i);
+            else return __shfl(my_off, (int)(i * GROUPS + g), 64);
+        };
+        // smallest exponent field (in place) among the chunk's scales; the
+        // rows past the chunk's end, which decode record 0, may count too
+        uint32_t amin = 0x7F800000u;
+
         if constexpr (GROUPS == 1) {
             // d = 512: one row at a time across the whole wave; the row's
             // record offset is uniform (scalar), the scale comes by a scalar load
             uint32_t nb[CI], ab[CI];
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const uint64_t o = readlane_u64(my_off, (uint32_t)i);
-                const uint8_t *rec = tab + o;
-                if constexpr (KV == 4) {
-                    // lane l's 16 new bits are code half-word l (records are 2-byte aligned)
-                    nb[i] = *reinterpret_cast<const uint16_t *>(rec + 2u * l);
-                } else {
-                    const uint64_t bit = o * 8 + (uint64_t)NEWB * l;
-                    const uint8_t *p = tab + ((bit >> 5) << 2);
-                    const uint64_t both = ((uint64_t)ld32(p + 4) << 32) | ld32(p);
-                    nb[i] = (uint32_t)(both >> (bit & 31)) & ((1u << NEWB) - 1u);
-                }
-                const uint64_t ao = o + NB;  // scale: bf16 at bytes [NB, NB + 2)
-                const uint32_t adw = ld32(tab + (ao & ~(uint64_t)3));
-                ab[i] = ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16;
+                const uint64_t o = row_offset((uint32_t)i);
+                nb[i] = row_bits(o);
+                ab[i] = row_scale(o);
             }
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
                 // every row is decoded (an invalid id reads record 0), so the
                 // loads above stay ahead of their uses
-                const u32x4 v = decode_lane<D, KV, RAW, COPIES, true>(nb[i], ab[i], l, g, s_lut, lds_off);
+                const u32x4 v = decode_lane<D, KV, RAW ? kRaw : kScaled, COPIES, true>(nb[i], ab[i], l, g, s_lut,
+                                                                                        lds_off);
                 if ((uint32_t)i < cn) store16(out + row_of(c, i) * (D / 2) + 4u * l, v);
+                if constexpr (!RAW) {
+                    amin = __builtin_elementwise_min(amin, ab[i] & 0x7F800000u);
+                    // taken here, so the row's scale register is free afterwards
+                    asm volatile("" : "+s"(amin));
+                }
             }
         } else {
             // several rows side by side: group g decodes rows g, g + GROUPS, ...
@@ -160,25 +182,41 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
             uint32_t nb[CI], ab[CI];
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const int r = (int)(i * GROUPS + g);
-                const uint64_t o = __shfl(my_off, r, 64);
-                if constexpr (KV == 4) {
-                    nb[i] = *reinterpret_cast<const uint16_t *>(tab + o + 2u * l);
-                } else {
-                    const uint64_t bit = o * 8 + (uint64_t)NEWB * l;
-                    const uint8_t *p = tab + ((bit >> 5) << 2);
-                    const uint64_t both = ((uint64_t)ld32(p + 4) << 32) | ld32(p);
-                    nb[i] = (uint32_t)(both >> (bit & 31)) & ((1u << NEWB) - 1u);
-                }
-                const uint64_t ao = o + NB;
-                const uint32_t adw = ld32(tab + (ao & ~(uint64_t)3));
-                ab[i] = ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16;
+                const uint64_t o = row_offset((uint32_t)i);
+                nb[i] = row_bits(o);
+                ab[i] = row_scale(o);
             }
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
                 const uint32_t r = i * GROUPS + g;
-                const u32x4 v = decode_lane<D, KV, RAW, COPIES, false>(nb[i], ab[i], l, g, s_lut, lds_off);
+                const u32x4 v = decode_lane<D, KV, RAW ? kRaw : kScaled, COPIES, false>(nb[i], ab[i], l, g, s_lut,
+                                                                                         lds_off);
                 if (r < cn) store16(out + row_of(c, r) * (D / 2) + 4u * l, v);
+                if constexpr (!RAW) {
+                    amin = __builtin_elementwise_min(amin, ab[i] & 0x7F800000u);
+                    asm volatile("" : "+v"(amin));
+                }
+            }
+        }
+        // Rows whose scale is below 2^-102 went through the fast scaling
+        // above, which can round twice when a product falls below 2^-126:
+        // decode them again with the exact tiny-scale arithmetic. Rare (a row
+        // norm that small), so kept off the main path like the bad-row pass
+        // below; the wait orders the two stores to the same address, and the
+        // bad-row pass comes after it (an invalid id decodes record 0, whose
+        // scale may be tiny).
+        if constexpr (!RAW) {
+            if (__builtin_expect(__ballot(scale_is_tiny(amin)) != 0, 0)) {
+                __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll 1
+                for (uint32_t i = 0; i < (uint32_t)CI; ++i) {
+                    const uint32_t r = i * GROUPS + g;
+                    const uint64_t o = row_offset(i);
+                    const uint32_t ab = row_scale(o);
+                    const u32x4 v = decode_lane<D, KV, kTiny, COPIES, (GROUPS == 1)>(row_bits(o), ab, l, g, s_lut,
+                                                                                      lds_off);
+                    if (r < cn && scale_is_tiny(ab)) store16(out + row_of(c, r) * (D / 2) + 4u * l, v);
+                }
             }
         }
         // Rows with an id outside the table were decoded from record 0 above;
@@ -202,36 +240,25 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
 // dispatch
 // ---------------------------------------------------------------------------
 
-// Launch shape (measured on MI355X, d = 512 replay): the codebook in LDS as
-// 16 copies x 2 signs (64 KB) in 1024-thread workgroups (2 per CU = 32
-// waves); one wave holds a chunk of up to 16 lookups (fewer for small
-// batches, lookup_chunk_rows); the grid covers all chunks (no persistent
-// cap), which balances the tail better than a fixed number of workgroups
-// per CU.
-template <int D, int KV>
-struct Tune {
-    static constexpr int COPIES = CPK_COPIES;
-    static constexpr int BLOCK = CPK_BLOCK;
-    static constexpr int BLOCKS_PER_CU = CPK_BLOCKS_PER_CU;
-    static constexpr int CHUNK = CPK_CHUNK;
-};
-
+// Launch shape (measured on MI355X, d = 512 replay): 1024-thread workgroups
+// with the codebook in LDS as 16 copies x 2 signs (64 KB); one wave holds a
+// chunk of up to 16 lookups (fewer for small batches, lookup_chunk_rows); the
+// grid covers all chunks (no persistent cap), which balances the tail better
+// than a fixed number of workgroups per CU. How many workgroups a CU runs at
+// once depends on the instance's registers: the d = 512 kernels hold 16 rows'
+// record offsets and scales in SGPRs, which leaves room for one 1024-thread
+// workgroup per CU (16 waves), the next one starting as its waves retire.
 template <int D, int KV, bool RAW, bool HOT, int CHUNK_ROWS>
 static hipError_t launch_shape(const LaunchArgs &a)
 {
-    using T = Tune<D, KV>;
     constexpr int GROUPS = 64 / (D / 8);
     // lookups per wave chunk: a multiple of the rows decoded side by side, <= 64
     constexpr int CHUNK = (CHUNK_ROWS / GROUPS > 0 ? CHUNK_ROWS / GROUPS : 1) * GROUPS;
     const uint64_t nchunks = (a.n + CHUNK - 1) / CHUNK;
-    uint64_t blocks = (nchunks + T::BLOCK / 64 - 1) / (T::BLOCK / 64);
+    uint64_t blocks = (nchunks + kBlock / 64 - 1) / (kBlock / 64);
     if (blocks > 0x7FFFFFFFull) blocks = 0x7FFFFFFFull;  // the chunk loop strides over any excess
-    if (T::BLOCKS_PER_CU > 0) {  // persistent grid: at most this many workgroups per CU
-        const uint64_t cap = (uint64_t)T::BLOCKS_PER_CU * (a.num_cus > 0 ? a.num_cus : 256);
-        if (blocks > cap) blocks = cap;
-    }
-    hipLaunchKernelGGL((gather_decode<D, KV, RAW, T::COPIES, T::BLOCK, CHUNK, HOT>), dim3((unsigned)blocks),
-                       dim3(T::BLOCK), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err,
+    hipLaunchKernelGGL((gather_decode<D, KV, RAW, kCopies, kBlock, CHUNK, HOT>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err,
                        a.by_offset, a.hot_index, a.host_off0, a.hot_off0);
     return hipGetLastError();
 }
@@ -242,7 +269,7 @@ static hipError_t launch_one(const LaunchArgs &a)
     switch (lookup_chunk_rows(a.n, a.num_cus)) {
     case 1: return launch_shape<D, KV, RAW, HOT, 1>(a);
     case 4: return launch_shape<D, KV, RAW, HOT, 4>(a);
-    default: return launch_shape<D, KV, RAW, HOT, Tune<D, KV>::CHUNK>(a);
+    default: return launch_shape<D, KV, RAW, HOT, kChunk>(a);
     }
 }
 
@@ -253,15 +280,15 @@ struct Entry {
     launch_fn scaled, raw, hot_scaled, hot_raw;
 };
 
-#define CPK_ENTRY(D, KV)                                                                                   \
+#define CP_ENTRY(D, KV)                                                                                   \
     {D, KV, &launch_one<D, KV, false, false>, &launch_one<D, KV, true, false>, &launch_one<D, KV, false, true>, \
      &launch_one<D, KV, true, true>}
 
 static const Entry kTable[] = {
-    CPK_ENTRY(64, 3),  CPK_ENTRY(64, 4),  CPK_ENTRY(64, 5),  CPK_ENTRY(64, 6),
-    CPK_ENTRY(128, 3), CPK_ENTRY(128, 4), CPK_ENTRY(128, 5), CPK_ENTRY(128, 6),
-    CPK_ENTRY(256, 3), CPK_ENTRY(256, 4), CPK_ENTRY(256, 5), CPK_ENTRY(256, 6),
-    CPK_ENTRY(512, 3), CPK_ENTRY(512, 4), CPK_ENTRY(512, 5), CPK_ENTRY(512, 6),
+    CP_ENTRY(64, 3),  CP_ENTRY(64, 4),  CP_ENTRY(64, 5),  CP_ENTRY(64, 6),
+    CP_ENTRY(128, 3), CP_ENTRY(128, 4), CP_ENTRY(128, 5), CP_ENTRY(128, 6),
+    CP_ENTRY(256, 3), CP_ENTRY(256, 4), CP_ENTRY(256, 5), CP_ENTRY(256, 6),
+    CP_ENTRY(512, 3), CP_ENTRY(512, 4), CP_ENTRY(512, 5), CP_ENTRY(512, 6),
 };
 
 static const Entry *find(uint32_t d, uint32_t kv)

@@ -371,7 +371,9 @@ __global__ __launch_bounds__(Tcq<KV>::NT) __attribute__((amdgpu_waves_per_eu(4))
         }
         __syncthreads();
         const double norm = sh.norm;
-        if (norm > 0.0) {
+        // alpha = ||e|| / ||f(c)|| needs a finite nonzero norm: a row of zeros,
+        // or one holding an inf or a NaN, keeps the all-zero code and alpha 0
+        if (norm > 0.0 && norm < __builtin_inf()) {
             const double sd = __builtin_sqrt((double)d);
             for (uint32_t i = tid; i < d; i += P::NT) sh.z[i] = sd * (double)er[i] / norm;
             __syncthreads();
@@ -421,8 +423,6 @@ __global__ __launch_bounds__(Tcq<KV>::NT) __attribute__((amdgpu_waves_per_eu(4))
                 sh.code[NB + 1] = (uint8_t)(ab >> 8);
             }
         }
-        // a zero row (or one whose norm is not finite and positive) keeps the
-        // all-zero code and alpha 0
         __syncthreads();
         for (uint32_t b = tid; b < NB + 2; b += P::NT) rec[b] = sh.code[b];
         __syncthreads();

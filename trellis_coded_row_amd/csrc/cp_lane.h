@@ -7,28 +7,14 @@
 
 #include "cp_internal.h"
 
-// Launch-shape knobs (overridable at build time for tuning).
-#ifndef CPK_COPIES
-#define CPK_COPIES 16
-#endif
-#ifndef CPK_BLOCK
-#define CPK_BLOCK 1024
-#endif
-#ifndef CPK_NT_STORE
-#define CPK_NT_STORE 1
-#endif
-#ifndef CPK_FMA_MIX
-#define CPK_FMA_MIX 1
-#endif
-#ifndef CPK_BLOCKS_PER_CU
-#define CPK_BLOCKS_PER_CU 0
-#endif
-#ifndef CPK_CHUNK
-#define CPK_CHUNK 16
-#endif
-
-
 namespace cpk {
+
+// Launch shape of the gather-decode kernels (measured on MI355X, d = 512
+// replay): 1024-thread workgroups, the codebook in LDS as 16 copies per sign,
+// wave chunks of up to 16 lookups.
+constexpr int kBlock = 1024;
+constexpr int kCopies = 16;
+constexpr int kChunk = 16;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -48,9 +34,11 @@ __device__ __forceinline__ uint32_t ld32(const uint8_t *p)
     return *reinterpret_cast<const uint32_t *>(p);
 }
 
-// alpha * (fp16 half of e) in one v_fma_mix_f32: the half is widened exactly,
-// the product of a bf16 and an fp16 is exact in fp32, and adding -0 leaves
-// every product (signed zeros included) unchanged.
+// alpha * (fp16 half of e) in one v_fma_mix_f32: the half is widened exactly
+// and the product is rounded once to fp32; adding -0 leaves every product
+// (signed zeros included) unchanged. The product of a bf16 and an fp16 has at
+// most 8 + 11 significant bits, so it is exact in fp32 whenever it is zero or
+// at least 2^-126 in magnitude (see scale_is_tiny for the other case).
 __device__ __forceinline__ float mix_lo(uint32_t e, float a, float negz)
 {
     float r;
@@ -81,33 +69,81 @@ __device__ __forceinline__ float mix_hi_s(uint32_t e, float a, float negz)
     return r;
 }
 
-// One output pair: e = LUT entry (fp16 lo = element 2t, hi = element 2t+1),
-// negmask = 0x80008000 when the window's bit 15 is set. Scaled: bf16 pair of
-// alpha * value, rounded to nearest even; that rounding is symmetric in sign,
-// so the sign flip can be applied to the packed result.
-template <bool RAW, bool SALPHA = false>
-__device__ __forceinline__ uint32_t emit_pair(uint32_t e, uint32_t negmask, float alpha)
+// What a decode writes: the raw f(c) (fp16), the scaled row (bf16, the fast
+// path), or the scaled row computed for a tiny scale (scale_pair_tiny).
+enum Emit { kRaw, kScaled, kTiny };
+
+// One scaled output pair: e = signed codebook pair (fp16 lo = element 2t, hi =
+// element 2t+1) -> the bf16 pair of alpha * value, each product formed in
+// fp32 (exact unless the scale is tiny) and rounded once to nearest even by
+// v_cvt_pk_bf16_f32.
+template <bool SALPHA>
+__device__ __forceinline__ uint32_t emit_scaled(uint32_t e, float alpha)
 {
-    if constexpr (RAW) {
-        return e ^ negmask;
+    const float negz = __builtin_bit_cast(float, 0x80000000u);
+    f32x2 v;
+    if constexpr (SALPHA) {
+        v.x = mix_lo_s(e, alpha, negz);
+        v.y = mix_hi_s(e, alpha, negz);
     } else {
-        f32x2 v;
-#if CPK_FMA_MIX
-        const float negz = __builtin_bit_cast(float, 0x80000000u);
-        if constexpr (SALPHA) {
-            v.x = mix_lo_s(e, alpha, negz);
-            v.y = mix_hi_s(e, alpha, negz);
-        } else {
-            v.x = mix_lo(e, alpha, negz);
-            v.y = mix_hi(e, alpha, negz);
-        }
-#else
-        v.x = alpha * (float)__builtin_bit_cast(_Float16, (uint16_t)(e & 0xFFFFu));
-        v.y = alpha * (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
-#endif
-        bf16x2 b = __builtin_convertvector(v, bf16x2);
-        return __builtin_bit_cast(uint32_t, b) ^ negmask;
+        v.x = mix_lo(e, alpha, negz);
+        v.y = mix_hi(e, alpha, negz);
     }
+    const bf16x2 b = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+// A scale below 2^-102 (fp32 bits of the bf16; zeros and bf16 subnormals
+// included): with it a product with a nonzero fp16 (>= 2^-24 in magnitude)
+// // can fall below 2^-126, where fp32 keeps fewer than the product's 19
+// significant bits and the fp32 product followed by the bf16 rounding would
+// round twice. The kernels decode such rows again with scale_pair_tiny in a
+// rarely taken pass after the chunk's main stores.
+__device__ __forceinline__ bool scale_is_tiny(uint32_t alpha_bits)
+{
+    return (alpha_bits & 0x7F800000u) < (25u << 23);
+}
+
+// bf16 bits of alpha * h, rounded once to nearest even, for a tiny scale
+// (|alpha| < 2^-102) and a finite fp16 h. Done on a copy scaled by 2^64, where
+// every operation is exact on normal floats, so the result does not depend on
+// the float denormal modes except for widening h:
+//   a2 = |alpha| * 2^64, built from the bits (exact; a bf16 subnormal alpha is
+//        its integer significand times 2^-85);
+//   p  = h * a2, exact (normal or zero: 2^-93 <= |p| < 2^-22);
+//   |alpha * h| = |p| * 2^-64 is a bf16 normal when |p| >= 2^-62: round |p| to
+//        bf16 and lower its exponent by 64; otherwise it lies below 2^-126,
+//        where bf16 steps are 2^-133: round |p| * 2^69 (< 2^7) to an integer
+//        with ties to even by adding and removing 2^23, and that integer is
+//        the bf16 pattern (128 is the smallest normal, 0x0080).
+__device__ __forceinline__ uint32_t scale_half_tiny(uint32_t h16, uint32_t alpha_bits)
+{
+    const uint32_t mag = alpha_bits & 0x7FFFFFFFu;
+    const float a2 = (mag >> 23) ? __builtin_bit_cast(float, mag + (64u << 23))
+                                 : (float)(mag & 0x7FFFFFu) * 0x1p-85f;
+    const float p = (float)__builtin_bit_cast(_Float16, (uint16_t)h16) * a2;
+    const uint32_t sign = ((__builtin_bit_cast(uint32_t, p) ^ alpha_bits) & 0x80000000u) >> 16;
+    const float ap = __builtin_fabsf(p);
+    uint32_t r;
+    if (ap >= 0x1p-62f) {
+        r = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ap) - (64u << 7);
+    } else {
+        r = __builtin_bit_cast(uint32_t, ap * 0x1p69f + 0x1p23f) - 0x4B000000u;
+    }
+    return sign | r;
+}
+
+__device__ __forceinline__ uint32_t scale_pair_tiny(uint32_t e, uint32_t alpha_bits)
+{
+    return scale_half_tiny(e & 0xFFFFu, alpha_bits) | (scale_half_tiny(e >> 16, alpha_bits) << 16);
+}
+
+template <Emit MODE, bool SALPHA>
+__device__ __forceinline__ uint32_t emit_pair(uint32_t e, float alpha, uint32_t alpha_bits)
+{
+    if constexpr (MODE == kRaw) return e;
+    else if constexpr (MODE == kScaled) return emit_scaled<SALPHA>(e, alpha);
+    else return scale_pair_tiny(e, alpha_bits);
 }
 
 // h = x*x + x (mod 2^32) on the low 24 bits of x. Bits 7..15 of h, the only
@@ -136,7 +172,7 @@ using field_t = typename std::conditional<(16 + 3 * KV <= 32), uint32_t, uint64_
 
 // Decodes one row's 8 outputs of this lane from `newbits` (the lane's 4kv
 // new code bits) and the row's scale, and returns them packed (4 dwords).
-template <int D, int KV, bool RAW, int COPIES, bool SALPHA>
+template <int D, int KV, Emit MODE, int COPIES, bool SALPHA>
 __device__ __forceinline__ u32x4 decode_lane(uint32_t newbits, uint32_t alpha_bits, uint32_t l, uint32_t g,
                                              const uint32_t *s_lut, uint32_t lds_off)
 {
@@ -171,7 +207,7 @@ __device__ __forceinline__ u32x4 decode_lane(uint32_t newbits, uint32_t alpha_bi
         // half (+64 bytes); the lane picks one of the 16 copies
         const uint32_t e = *reinterpret_cast<const uint32_t *>(
             reinterpret_cast<const char *>(s_lut) + and_or(h, 0xFF80u, and_or(x >> 9, 0x40u, lds_off)));
-        v[k] = emit_pair<RAW, SALPHA>(e, 0u, alpha);
+        v[k] = emit_pair<MODE, SALPHA>(e, alpha, alpha_bits);
     }
     return v;
 }
@@ -211,13 +247,11 @@ __device__ __forceinline__ uint32_t scale_bits(const uint8_t *__restrict__ tab, 
     return ((adw >> ((ao & 2) << 3)) & 0xFFFFu) << 16;
 }
 
+// Output rows are written once and not read back by the kernel: nontemporal
+// stores keep them from evicting hot records from the caches.
 __device__ __forceinline__ void store16(uint32_t *dst, u32x4 v)
 {
-#if CPK_NT_STORE
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
-#else
-    *reinterpret_cast<u32x4 *>(dst) = v;
-#endif
 }
 
 }  // namespace cpk

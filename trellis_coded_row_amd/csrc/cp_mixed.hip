@@ -34,7 +34,7 @@ namespace {
 // lane): the history bits come from the two previous lanes of the row (kv = 3
 // needs both; for kv >= 4 the second contributes nothing), the window field
 // is 64 bits wide and the shifts take the rate as an operand.
-template <int D, bool RAW, bool SALPHA>
+template <int D, Emit MODE, bool SALPHA>
 __device__ __forceinline__ u32x4 decode_any_rate(uint32_t newbits, uint32_t kv, uint32_t alpha_bits, uint32_t l,
                                                  uint32_t g, const uint32_t *s_lut, uint32_t lds_off)
 {
@@ -59,7 +59,7 @@ __device__ __forceinline__ u32x4 decode_any_rate(uint32_t newbits, uint32_t kv, 
         const uint32_t h = hash_mad(x);
         const uint32_t e = *reinterpret_cast<const uint32_t *>(
             reinterpret_cast<const char *>(s_lut) + and_or(h, 0xFF80u, and_or(x >> 9, 0x40u, lds_off)));
-        v[k] = emit_pair<RAW, SALPHA>(e, 0u, alpha);
+        v[k] = emit_pair<MODE, SALPHA>(e, alpha, alpha_bits);
     }
     return v;
 }
@@ -126,35 +126,54 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
         const uint64_t okmask = __ballot(ok);
         my_id = load_id(c + waves);
 
-        if constexpr (GROUPS == 1) {
+        // record offset and rate of the row that lane group g decodes i-th
+        auto row_offset = [&](uint32_t i) -> uint64_t {
+            if constexpr (GROUPS == 1) return readlane_u64(my_off, i);
+            else return __shfl(my_off, (int)(i * GROUPS + g), 64);
+        };
+        auto row_kv = [&](uint32_t i) -> uint32_t {
+            if constexpr (GROUPS == 1) return (uint32_t)__builtin_amdgcn_readlane((int)my_kv, (int)i);
+            else return (uint32_t)__shfl((int)my_kv, (int)(i * GROUPS + g), 64);
+        };
+        // smallest exponent field (in place) among the chunk's scales
+        uint32_t amin = 0x7F800000u;
+        {
             uint32_t nb[CI], ab[CI], kv[CI];
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
-                const uint64_t o = readlane_u64(my_off, (uint32_t)i);
-                kv[i] = (uint32_t)__builtin_amdgcn_readlane((int)my_kv, i);
-                nb[i] = lane_bits(tab, o, 4u * kv[i], l);
-                ab[i] = scale_bits(tab, o, kv[i] * (uint32_t)(D / 16));
-            }
-#pragma unroll
-            for (int i = 0; i < CI; ++i) {
-                const u32x4 v = decode_any_rate<D, RAW, true>(nb[i], kv[i], ab[i], l, g, s_lut, lds_off);
-                if ((uint32_t)i < cn) store16(out + row_of(c, i) * (D / 2) + 4u * l, v);
-            }
-        } else {
-            uint32_t nb[CI], ab[CI], kv[CI];
-#pragma unroll
-            for (int i = 0; i < CI; ++i) {
-                const int r = (int)(i * GROUPS + g);
-                const uint64_t o = __shfl(my_off, r, 64);
-                kv[i] = (uint32_t)__shfl((int)my_kv, r, 64);
+                const uint64_t o = row_offset((uint32_t)i);
+                kv[i] = row_kv((uint32_t)i);
                 nb[i] = lane_bits(tab, o, 4u * kv[i], l);
                 ab[i] = scale_bits(tab, o, kv[i] * (uint32_t)(D / 16));
             }
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
                 const uint32_t r = i * GROUPS + g;
-                const u32x4 v = decode_any_rate<D, RAW, false>(nb[i], kv[i], ab[i], l, g, s_lut, lds_off);
+                const u32x4 v = decode_any_rate<D, RAW ? kRaw : kScaled, (GROUPS == 1)>(nb[i], kv[i], ab[i], l, g,
+                                                                                          s_lut, lds_off);
                 if (r < cn) store16(out + row_of(c, r) * (D / 2) + 4u * l, v);
+                if constexpr (!RAW) {
+                    amin = __builtin_elementwise_min(amin, ab[i] & 0x7F800000u);
+                    // taken here, so the row's scale register is free afterwards
+                    if constexpr (GROUPS == 1) asm volatile("" : "+s"(amin));
+                    else asm volatile("" : "+v"(amin));
+                }
+            }
+        }
+        // rows with a tiny scale again, exactly (see the single-rate kernel)
+        if constexpr (!RAW) {
+            if (__builtin_expect(__ballot(scale_is_tiny(amin)) != 0, 0)) {
+                __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll 1
+                for (uint32_t i = 0; i < (uint32_t)CI; ++i) {
+                    const uint32_t r = i * GROUPS + g;
+                    const uint64_t o = row_offset(i);
+                    const uint32_t kv = row_kv(i);
+                    const uint32_t ab = scale_bits(tab, o, kv * (uint32_t)(D / 16));
+                    const u32x4 v = decode_any_rate<D, kTiny, (GROUPS == 1)>(lane_bits(tab, o, 4u * kv, l), kv, ab,
+                                                                              l, g, s_lut, lds_off);
+                    if (r < cn && scale_is_tiny(ab)) store16(out + row_of(c, r) * (D / 2) + 4u * l, v);
+                }
             }
         }
         // the next chunk's index entries load while this chunk's stores drain
@@ -176,7 +195,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
 template <int D, bool RAW, int CHUNK_ROWS>
 hipError_t launch_mixed_shape(const MixedLaunchArgs &a)
 {
-    constexpr int BLOCK = CPK_BLOCK;
+    constexpr int BLOCK = kBlock;
     constexpr int GROUPS = 64 / (D / 8);
     constexpr int CHUNK = (CHUNK_ROWS / GROUPS > 0 ? CHUNK_ROWS / GROUPS : 1) * GROUPS;
     const uint64_t nchunks = (a.n + CHUNK - 1) / CHUNK;
@@ -194,7 +213,7 @@ hipError_t launch_mixed_one(const MixedLaunchArgs &a)
     switch (lookup_chunk_rows(a.n, a.num_cus)) {
     case 1: return launch_mixed_shape<D, RAW, 1>(a);
     case 4: return launch_mixed_shape<D, RAW, 4>(a);
-    default: return launch_mixed_shape<D, RAW, CPK_CHUNK>(a);
+    default: return launch_mixed_shape<D, RAW, kChunk>(a);
     }
 }
 
