@@ -224,6 +224,27 @@ uint64_t cp_dedup_workspace_bytes(const cp_table *table, uint64_t n);
 cp_status cp_lookup_decode_dedup(const cp_table *table, const int64_t *ids, uint64_t n, uint16_t *out,
                                  void *workspace, uint64_t workspace_bytes, void *stream);
 
+/* Largest batch cp_lookup_decode_dedup_noalloc accepts. */
+#define CP_DEDUP_NOALLOC_MAX_IDS 65536u
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * result as cp_lookup_decode_dedup, with its scratch (hash table, staging
+ * area) in a fixed device array that the library holds on each device it
+ * runs on until the process ends (about 16.8 MB per device, enough for
+ * CP_DEDUP_NOALLOC_MAX_IDS lookups of any supported record size). The call
+ * allocates nothing: no hipMalloc, no hipFree, no memset; it launches kernels
+ * on `stream` only (the first call on a device also looks up the array's
+ * address once).
+ *   ids, out, stream - as in cp_lookup_decode; 1 <= n <= CP_DEDUP_NOALLOC_MAX_IDS.
+ * All calls on one device share that array, which keeps the last call's
+ * contents: calls that overlap on one device (concurrent streams or host
+ * threads) race and give undefined rows; serialise them.
+ * Errors: INVALID_ARGUMENT (as cp_lookup_decode_dedup, or n above
+ * CP_DEDUP_NOALLOC_MAX_IDS), UNSUPPORTED (a mixed-rate table), HIP. */
+cp_status cp_lookup_decode_dedup_noalloc(const cp_table *table, const int64_t *ids, uint64_t n, uint16_t *out,
+                                         void *stream);
+
 /* Copies records [first_row, first_row + nrows) of the table to host memory
  * `dst` (nrows * R bytes, packed records). Waits for all work on the table's
  * device first, so records written by cp_table_encode on any stream are

@@ -201,3 +201,10 @@ def test_create_rejects_a_codebook_entry_that_is_not_finite(bad):
     cls = (ctypes.c_uint8 * 8)(0, 1, 0, 1, 1, 1, 0, 0)
     st, h = cp.cp_table_create_mixed(_mdesc(), ctypes.addressof(lut), ctypes.addressof(cls))
     assert (st, h) == (cp.CP_ERR_INVALID_ARGUMENT, 0)
+
+
+def test_noalloc_limit_matches_the_header_and_null_table_is_refused():
+    text = open(HEADER).read()
+    m = re.search(r"#define CP_DEDUP_NOALLOC_MAX_IDS (\d+)u", text)
+    assert m and int(m.group(1)) == cp.CP_DEDUP_NOALLOC_MAX_IDS
+    assert cp.cp_lookup_decode_dedup_noalloc(0, 8, 1, 16, None) == cp.CP_ERR_INVALID_ARGUMENT

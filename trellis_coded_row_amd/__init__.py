@@ -28,6 +28,7 @@ __all__ = [
     "CPError", "Table", "load_library",
     "cp_record_bytes", "cp_supported", "cp_table_create", "cp_table_upload", "cp_lookup_decode",
     "cp_lookup_decode_raw", "cp_dedup_workspace_bytes", "cp_lookup_decode_dedup",
+    "cp_lookup_decode_dedup_noalloc", "CP_DEDUP_NOALLOC_MAX_IDS",
     "cp_table_download", "cp_encode_workspace_bytes", "cp_table_encode",
     "cp_table_set_hot_rows", "cp_table_hot_rows",
     "cp_table_create_mixed", "cp_table_record_range", "cp_table_describe_mixed", "cp_mixed_desc", "MixedTable",
@@ -47,6 +48,7 @@ CP_ERR_ID_OUT_OF_RANGE = 5
 CP_RESIDENCY_DEVICE = 0
 CP_RESIDENCY_HOST_MAPPED = 1
 CP_FLAG_HOST_NONCOHERENT = 1
+CP_DEDUP_NOALLOC_MAX_IDS = 65536
 
 
 class cp_table_desc(ctypes.Structure):
@@ -105,6 +107,7 @@ def load_library() -> ctypes.CDLL:
         "cp_lookup_decode_raw": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
         "cp_dedup_workspace_bytes": (ctypes.c_uint64, [vp, ctypes.c_uint64]),
         "cp_lookup_decode_dedup": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp]),
+        "cp_lookup_decode_dedup_noalloc": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
         "cp_table_download": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp]),
         "cp_encode_workspace_bytes": (ctypes.c_uint64, [vp, ctypes.c_uint64]),
         "cp_table_encode": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp]),
@@ -198,6 +201,10 @@ def cp_dedup_workspace_bytes(table: int, n: int) -> int:
 def cp_lookup_decode_dedup(table: int, ids_ptr: int, n: int, out_ptr: int, workspace_ptr: int,
                            workspace_bytes: int, stream: int | None) -> int:
     return _L.cp_lookup_decode_dedup(table, ids_ptr, n, out_ptr, workspace_ptr, workspace_bytes, stream)
+
+
+def cp_lookup_decode_dedup_noalloc(table: int, ids_ptr: int, n: int, out_ptr: int, stream: int | None) -> int:
+    return _L.cp_lookup_decode_dedup_noalloc(table, ids_ptr, n, out_ptr, stream)
 
 
 def cp_table_download(table: int, first_row: int, nrows: int, dst_ptr: int) -> int:
@@ -354,6 +361,19 @@ class Table:
             _keep_for_stream(workspace, stream)
         if own_out:
             _keep_for_stream(out, stream)
+        return out
+
+    def lookup_decode_dedup_noalloc(self, ids, out, stream=None):
+        """bf16[n, d] like lookup_decode_dedup, with the library's fixed
+        per-device scratch instead of a workspace (n <= CP_DEDUP_NOALLOC_MAX_IDS;
+        `out` must be given: nothing is allocated; calls must not overlap on
+        one device)."""
+        if out is None:
+            raise ValueError("out must be given (this call allocates nothing)")
+        n, out = self._check_io(ids, out, torch.bfloat16)
+        st = cp_lookup_decode_dedup_noalloc(self.handle, ids.data_ptr(), n, out.data_ptr(), _stream_handle(stream))
+        if st != CP_OK:
+            raise CPError(st, "cp_lookup_decode_dedup_noalloc")
         return out
 
     def download(self, first_row: int = 0, nrows: int | None = None) -> np.ndarray:

@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/cp.h"
 #include "cp_internal.h"
 
@@ -71,7 +73,7 @@ struct DeviceGuard {
 
 // Bytes after the last record that loads of the last record may touch
 // (aligned dwords straddling the record end); zeroed at creation.
-static const uint64_t kTailPad = 64;
+static constexpr uint64_t kTailPad = 64;
 
 extern "C" {
 
@@ -443,19 +445,13 @@ uint64_t cp_dedup_workspace_bytes(const cp_table *t, uint64_t n)
     return cpk::dedup_layout(n, t->record_bytes, kTailPad).total;
 }
 
-cp_status cp_lookup_decode_dedup(const cp_table *t, const int64_t *ids, uint64_t n, uint16_t *out,
-                                 void *workspace, uint64_t workspace_bytes, void *stream)
+// Shared body of the two dedup entry points: `ws` is device memory of at
+// least dedup_layout(n, R, kTailPad).total bytes, 256-byte aligned; the
+// caller has checked the arguments and made the table's device current.
+static cp_status dedup_lookup(const cp_table *t, const int64_t *ids, uint64_t n, uint16_t *out, uint8_t *ws,
+                              void *stream)
 {
-    if (!t) return CP_ERR_INVALID_ARGUMENT;
-    if (n == 0) return CP_OK;
-    if (!ids || !out || ((uintptr_t)out & 15u) || ((uintptr_t)ids & 7u)) return CP_ERR_INVALID_ARGUMENT;
-    if (n > 0x7FFFFFFFull) return CP_ERR_INVALID_ARGUMENT;  // staging indices are 32-bit
-    if (t->mixed) return CP_ERR_UNSUPPORTED;
     const cpk::DedupLayout L = cpk::dedup_layout(n, t->record_bytes, kTailPad);
-    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total) return CP_ERR_INVALID_ARGUMENT;
-    DeviceGuard guard(t->device);
-    if (guard.err != hipSuccess) return hip_fail(guard.err);
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
     cpk::DedupArgs d;
     d.records = t->records_dev;
     d.rows = t->desc.rows;
@@ -481,6 +477,82 @@ cp_status cp_lookup_decode_dedup(const cp_table *t, const int64_t *ids, uint64_t
     a.stream = (hipStream_t)stream;
     e = cpk::launch(t->desc.d, t->desc.bits_per_step, false, a);
     return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
+static cp_status dedup_check(const cp_table *t, const int64_t *ids, uint64_t n, const uint16_t *out)
+{
+    if (!ids || !out || ((uintptr_t)out & 15u) || ((uintptr_t)ids & 7u)) return CP_ERR_INVALID_ARGUMENT;
+    if (n > 0x7FFFFFFFull) return CP_ERR_INVALID_ARGUMENT;  // staging indices are 32-bit
+    if (t->mixed) return CP_ERR_UNSUPPORTED;
+    return CP_OK;
+}
+
+cp_status cp_lookup_decode_dedup(const cp_table *t, const int64_t *ids, uint64_t n, uint16_t *out,
+                                 void *workspace, uint64_t workspace_bytes, void *stream)
+{
+    if (!t) return CP_ERR_INVALID_ARGUMENT;
+    if (n == 0) return CP_OK;
+    const cp_status st = dedup_check(t, ids, n, out);
+    if (st != CP_OK) return st;
+    const cpk::DedupLayout L = cpk::dedup_layout(n, t->record_bytes, kTailPad);
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total) return CP_ERR_INVALID_ARGUMENT;
+    DeviceGuard guard(t->device);
+    if (guard.err != hipSuccess) return hip_fail(guard.err);
+    return dedup_lookup(t, ids, n, out, static_cast<uint8_t *>(workspace), stream);
+}
+
+}  // extern "C"
+
+// Scratch of cp_lookup_decode_dedup_noalloc: a file-scope device array sized
+// for the largest batch it accepts with the largest record any supported
+// shape has (d = 512 at 3 bits per element: 194 bytes), about 16.8 MB. The
+// runtime places one copy on every device the library's code runs on, at an
+// address of its own, and keeps it until the process ends. Host code never
+// uses the array's name as an address (on the host it names a stand-in, not
+// device memory): scratch_address() asks the runtime for this device's copy.
+static constexpr uint64_t kNoallocMaxRecordBytes = 194;
+static constexpr uint64_t kNoallocScratchBytes =
+    cpk::dedup_layout(CP_DEDUP_NOALLOC_MAX_IDS, kNoallocMaxRecordBytes, kTailPad).total;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+static constexpr int kMaxDevices = 256;
+static std::mutex g_scratch_mutex;
+static uint8_t *g_scratch_ptr[kMaxDevices];
+
+static hipError_t scratch_address(int device, uint8_t **ptr)
+{
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[device]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = static_cast<uint8_t *>(p);
+    }
+    *ptr = g_scratch_ptr[device];
+    return hipSuccess;
+}
+
+extern "C" {
+
+cp_status cp_lookup_decode_dedup_noalloc(const cp_table *t, const int64_t *ids, uint64_t n, uint16_t *out,
+                                         void *stream)
+{
+    if (!t) return CP_ERR_INVALID_ARGUMENT;
+    if (n == 0) return CP_OK;
+    const cp_status st = dedup_check(t, ids, n, out);
+    if (st != CP_OK) return st;
+    if (n > CP_DEDUP_NOALLOC_MAX_IDS) return CP_ERR_INVALID_ARGUMENT;
+    if (cpk::dedup_layout(n, t->record_bytes, kTailPad).total > kNoallocScratchBytes)
+        return CP_ERR_INVALID_ARGUMENT;  // not reached: every supported record fits
+    DeviceGuard guard(t->device);
+    if (guard.err != hipSuccess) return hip_fail(guard.err);
+    uint8_t *ws = nullptr;
+    const hipError_t e = scratch_address(t->device, &ws);
+    if (e != hipSuccess) return hip_fail(e);
+    return dedup_lookup(t, ids, n, out, ws, stream);
 }
 
 cp_status cp_table_download(const cp_table *t, uint64_t first_row, uint64_t nrows, void *dst)

@@ -210,34 +210,6 @@ __global__ __launch_bounds__(256) void dedup_resolve(const uint32_t *__restrict_
     }
 }
 
-// Workspace layout for n lookups: slots = next power of two >= 2n (load factor
-// <= 1/2), then keys[slots] (8 B), sidx[slots], slot_of[n] (4 B), uniq[n],
-// staged_off[n] (8 B), count (8 B), staging (n slots of slot_bytes + tail
-// pad), each region 256-byte aligned. A staging slot holds a record's 16-byte
-// aligned window: 16 * ceil((R + 15) / 16) bytes.
-static uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
-
-static uint32_t window_units(uint64_t record_bytes) { return (uint32_t)((record_bytes + 15 + 15) / 16); }
-
-DedupLayout dedup_layout(uint64_t n, uint64_t record_bytes, uint64_t tail_pad)
-{
-    DedupLayout L{};
-    uint64_t slots = 1;
-    while (slots < 2 * n) slots <<= 1;
-    L.slots = slots;
-    L.slot_bytes = 16ull * window_units(record_bytes);
-    uint64_t off = 0;
-    L.keys = off;       off = align256(off + 8 * slots);
-    L.sidx = off;       off = align256(off + 4 * slots);
-    L.slot_of = off;    off = align256(off + 4 * n);
-    L.uniq = off;       off = align256(off + 8 * n);
-    L.staged_ids = off; off = align256(off + 8 * n);
-    L.count = off;      off = align256(off + 8);
-    L.staging = off;    off = align256(off + n * L.slot_bytes + tail_pad);
-    L.total = off;
-    return L;
-}
-
 hipError_t dedup_prepare(const DedupArgs &a)
 {
     const DedupLayout &L = a.layout;
@@ -261,7 +233,7 @@ hipError_t dedup_prepare(const DedupArgs &a)
                        pad_bytes);
     hipLaunchKernelGGL(dedup_insert, dim3(grid(a.n, kTile)), dim3(256), 0, a.stream, a.ids, a.n, a.rows, keys,
                        sidx, L.slots - 1, slot_of, uniq, count);
-    const uint32_t units = window_units(a.record_bytes);
+    const uint32_t units = dedup_window_units(a.record_bytes);
     hipLaunchKernelGGL(dedup_gather, dim3(grid(a.n * units, 256)), dim3(256), 0, a.stream, a.records,
                        a.record_bytes, uniq, count, staging, a.n, units, L.slot_bytes);
     hipLaunchKernelGGL(dedup_resolve, dim3(grid(a.n, 256)), dim3(256), 0, a.stream, slot_of, a.n, sidx, uniq,

@@ -64,7 +64,40 @@ struct DedupArgs {
     hipStream_t stream;
 };
 
-DedupLayout dedup_layout(uint64_t n, uint64_t record_bytes, uint64_t tail_pad);
+// Workspace layout for n lookups: slots = next power of two >= 2n (load factor
+// <= 1/2), then keys[slots] (8 B), sidx[slots], slot_of[n] (4 B), uniq[n],
+// staged_off[n] (8 B), count (8 B), staging (n slots of slot_bytes + tail
+// pad), each region 256-byte aligned. A staging slot holds a record's 16-byte
+// aligned window: 16 * ceil((R + 15) / 16) bytes.
+constexpr uint64_t dedup_align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
+
+constexpr uint32_t dedup_window_units(uint64_t record_bytes) { return (uint32_t)((record_bytes + 15 + 15) / 16); }
+
+constexpr DedupLayout dedup_layout(uint64_t n, uint64_t record_bytes, uint64_t tail_pad)
+{
+    DedupLayout L{};
+    uint64_t slots = 1;
+    while (slots < 2 * n) slots <<= 1;
+    L.slots = slots;
+    L.slot_bytes = 16ull * dedup_window_units(record_bytes);
+    uint64_t off = 0;
+    L.keys = off;
+    off = dedup_align256(off + 8 * slots);
+    L.sidx = off;
+    off = dedup_align256(off + 4 * slots);
+    L.slot_of = off;
+    off = dedup_align256(off + 4 * n);
+    L.uniq = off;
+    off = dedup_align256(off + 8 * n);
+    L.staged_ids = off;
+    off = dedup_align256(off + 8 * n);
+    L.count = off;
+    off = dedup_align256(off + 8);
+    L.staging = off;
+    off = dedup_align256(off + n * L.slot_bytes + tail_pad);
+    L.total = off;
+    return L;
+}
 
 // Dedups ids into the workspace and stages each distinct record once; after
 // it, staged_ids[j] is the byte offset of lookup j's record in the staging
