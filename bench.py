@@ -49,8 +49,10 @@ def kernel_source_hash(kind: str = "single") -> str:
 
 
 def read_counter_summary(config: str, ids_kind: str, kind: str = "single") -> dict | None:
-    """HBM traffic per launch from a committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel sources."""
+    """Memory traffic per launch from a committed rocprofv3 --pmc summary, if
+    it was taken on the current kernel sources: HBM bytes (FETCH_SIZE and
+    WRITE_SIZE, scaled by what they read for a copy of known size) and, for a
+    table in host memory, the bytes read over PCIe."""
     path = os.path.join(PROFILES, f"counters_gather_decode_{config}_{ids_kind}.txt")
     if not os.path.exists(path):
         return None
@@ -68,7 +70,10 @@ def read_counter_summary(config: str, ids_kind: str, kind: str = "single") -> di
         write = float(vals["WRITE_SIZE_KiB_per_dispatch"]) * 1024 * float(vals["write_scale"])
     except (KeyError, ValueError):
         return None
-    return {"fetch_bytes": fetch, "write_bytes": write, "bytes": fetch + write, "file": os.path.basename(path)}
+    res = {"fetch_bytes": fetch, "write_bytes": write, "bytes": fetch + write, "file": os.path.basename(path)}
+    if "PCIE_READ_BYTES_per_dispatch" in vals:
+        res["pcie_bytes"] = float(vals["PCIE_READ_BYTES_per_dispatch"])
+    return res
 
 
 def host_cpu_model() -> str:
@@ -203,8 +208,12 @@ def probes(torch, mib: int = 1024) -> dict:
 
 
 def pcie_probe(torch, mib: int = 1024) -> dict:
-    """Host-to-device bandwidth from pinned host memory (torch copy of `mib`
-    MiB), the denominator for a table read over PCIe."""
+    """Host-to-device bandwidth from pinned host memory, two ways: a DMA copy
+    (torch copy of `mib` MiB, the denominator for a table read over PCIe) and
+    a kernel reading the same pinned buffer in place (zero-copy, as the
+    lookup reads a host-resident table: cpp_read_stream)."""
+    from trellis_coded_row_amd import probe as cpp
+
     n = mib * (1 << 20) // 4
     h = torch.empty(n, dtype=torch.int32, pin_memory=True)
     d = torch.empty(n, dtype=torch.int32, device="cuda")
@@ -212,9 +221,63 @@ def pcie_probe(torch, mib: int = 1024) -> dict:
     for _ in range(2):
         d.copy_(h, non_blocking=True)
     ms = time_region(lambda: d.copy_(h, non_blocking=True), 5, torch) / 5
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    zc = lambda: cpp.cpp_read_stream(h.data_ptr(), n * 4, sink.data_ptr(), stream)
+    for _ in range(2):
+        zc()
+    zc_ms = time_region(zc, 5, torch) / 5
     del h, d
     torch.cuda.empty_cache()
-    return {"h2d_GBps": n * 4 / ms / 1e6, "MiB": mib}
+    return {"h2d_GBps": n * 4 / ms / 1e6, "zero_copy_read_GBps": n * 4 / zc_ms / 1e6, "MiB": mib}
+
+
+def lookup_chunk(n: int, cus: int) -> int:
+    """Rows per wave chunk the lookup launch picks for n lookups (at least 8
+    waves per CU: 16 rows from 16 * 8 * cus lookups, 4 from 4 * 8 * cus)."""
+    waves = cus * 8
+    return 16 if n >= 16 * waves else (4 if n >= 4 * waves else 1)
+
+
+def floor_probes(torch, np, records, R: int, d: int, ids_np, host: bool, flush) -> dict:
+    """The lookup's two halves timed alone on the same workload: its output
+    stream (cpp_store_rows: the same rows, same placement, no loads) and its
+    record fetch (cpp_gather_records: the same ids and record reads from a
+    copy of the records in the same kind of memory, no decode, no stores),
+    each back to back (warm) and after an L2/MALL eviction (cold)."""
+    from trellis_coded_row_amd import probe as cpp
+
+    n = ids_np.shape[0]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream().cuda_stream
+    out = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+    ids = torch.from_numpy(ids_np).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flat = np.ascontiguousarray(records).reshape(-1)
+    if host:
+        rec = torch.empty(flat.size + 64, dtype=torch.uint8, pin_memory=True)
+        rec[: flat.size].numpy()[:] = flat
+    else:
+        rec = torch.empty(flat.size + 64, dtype=torch.uint8, device="cuda")
+        step = 1 << 30
+        for a in range(0, flat.size, step):
+            b = min(a + step, flat.size)
+            rec[a:b].copy_(torch.from_numpy(flat[a:b]))
+    rec[flat.size:].zero_()  # loads of the last record may touch a few bytes past it
+    store = lambda: cpp.cpp_store_rows(out.data_ptr(), n, d, lookup_chunk(n, cus), stream)
+    gather = lambda: cpp.cpp_gather_records(rec.data_ptr(), R, ids.data_ptr(), n, sink.data_ptr(), stream)
+    res = {}
+    for name, fn in (("store_only", store), ("gather_only", gather)):
+        for _ in range(10):
+            fn()
+        warm = time_region(fn, 50, torch) / 50
+        cold = time_each(fn, 20, torch, before=flush)
+        res[f"{name}_ms"] = warm
+        res[f"{name}_flushed_ms"] = sum(cold) / len(cold)
+    res["store_only_GBps"] = n * 2 * d / (res["store_only_ms"] / 1e3) / 1e9
+    del out, ids, rec, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 VALU_PEAK_TOPS = 39.3  # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: one 64-bit VALU op per lane-slot
@@ -402,13 +465,13 @@ def main() -> int:
     upload_s = time.time() - t_up
     hot_rows = 0
     hot_lookups = 0
+    hot_set_np = None
     if args.hot_share > 0:
         # the rows of the smallest Zipf ranks of the id stream (its most frequent rows)
         k = int(args.hot_share * cfg.rows)
-        hot_set = workload.keyed_permutation(np.arange(k, dtype=np.int64), cfg.rows, cfg.ids_seed)
-        hot_rows = table.set_hot_rows(hot_set)
-        hot_lookups = int(np.isin(ids_np, hot_set).sum())
-        del hot_set
+        hot_set_np = workload.keyed_permutation(np.arange(k, dtype=np.int64), cfg.rows, cfg.ids_seed)
+        hot_rows = table.set_hot_rows(hot_set_np)
+        hot_lookups = int(np.isin(ids_np, hot_set_np).sum())
 
     n = ids_np.shape[0]
     ids = torch.from_numpy(ids_np).cuda()
@@ -483,42 +546,65 @@ def main() -> int:
         "wall_s_timed_region": wall_s,
         "setup_s": {"generate": round(gen_s, 2), "upload": round(upload_s, 2)},
     }
+    counters = read_counter_summary(cfg.name, ids_kind, "mixed" if mixed else "single")
+    kernel_name = f"gather_decode_mixed<{cfg.d}>" if mixed else f"gather_decode<{cfg.d},{cfg.kv}>"
     if cfg.host_resident:
-        # the records cross PCIe: report that rate against a measured
-        # pinned host-to-device copy (the HBM roofline does not bound it)
-        # R: mean record bytes per lookup; lookups of rows with HBM copies do not cross PCIe
-        res["pcie_record_GBps"] = (n - hot_lookups) * R / (launch_ms / 1e3) / 1e9
-        if hot_rows:
-            res["lookups_served_from_hbm_copies"] = hot_lookups
+        # The records cross PCIe, so PCIe bounds the launch, not HBM. The
+        # bytes that must cross are each distinct record once (a repeat can
+        # be served from the GPU's caches; rows with HBM copies never cross);
+        # the denominator is a measured pinned host-to-device copy.
         probe = pcie_probe(torch)
         res["pcie_probe"] = probe
-        res["pcie_frac"] = res["pcie_record_GBps"] / probe["h2d_GBps"]
-    counters = read_counter_summary(cfg.name, ids_kind, "mixed" if mixed else "single")
-    res["roofline"] = {
-        "bound": "hbm",
-        "achieved": achieved,
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": achieved / HBM_PEAK_GBPS,
-        "traffic": counters["bytes"] if counters else None,
-        "algorithmic_bytes_per_launch": algo_bytes,
-        "kernel": f"gather_decode_mixed<{cfg.d}>" if mixed else f"gather_decode<{cfg.d},{cfg.kv}>",
-    }
+        uniq = np.unique(ids_np)
+        if hot_rows:
+            uniq = uniq[~np.isin(uniq, hot_set_np)]
+            res["lookups_served_from_hbm_copies"] = hot_lookups
+        pcie_bytes = int(uniq.size) * R
+        # granules of 64 bytes the distinct records touch: what the reads move
+        # if every distinct record is fetched once
+        first, last = uniq * R // 64, (uniq * R + R - 1) // 64
+        res["pcie_distinct_records"] = int(uniq.size)
+        res["pcie_distinct_64B_granule_bytes"] = int((last - first + 1).sum()) * 64
+        res["pcie_per_lookup_record_GBps"] = (n - hot_lookups) * R / (launch_ms / 1e3) / 1e9
+        pcie_achieved = pcie_bytes / (launch_ms / 1e3) / 1e9
+        res["roofline"] = {
+            "bound": "pcie",
+            "achieved": pcie_achieved,
+            "peak": probe["h2d_GBps"],
+            "unit": "GB/s",
+            "frac": pcie_achieved / probe["h2d_GBps"],
+            "traffic": counters.get("pcie_bytes") if counters else None,
+            "algorithmic_bytes_per_launch": pcie_bytes,
+            "kernel": kernel_name,
+            "hbm_effective_frac": achieved / HBM_PEAK_GBPS,
+        }
+    else:
+        res["roofline"] = {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": counters["bytes"] if counters else None,
+            "algorithmic_bytes_per_launch": algo_bytes,
+            "kernel": kernel_name,
+        }
 
     # per-launch distribution (each launch between its own pair of events)
     per = sorted(time_each(step, min(100, max(10, args.steps)), torch))
     q = lambda a, f: a[min(len(a) - 1, int(f * len(a)))]
     res["launch_ms_p10_p50_p90"] = [q(per, 0.1), q(per, 0.5), q(per, 0.9)]
+    # 512 MiB > L2 + MALL. A read of it leaves the caches holding clean lines
+    # of the flush buffer (cold records, nothing to write back); a write of it
+    # leaves dirty lines, whose write-back then competes with the lookup's own
+    # traffic (as after a layer that wrote its output).
+    flush = torch.empty(512 << 18, dtype=torch.int32, device="cuda")
+    flush.fill_(1)
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
+    clean_flush = lambda: torch.sum(flush, 0, dtype=torch.int64, out=sink)
     if not args.no_flushed:
-        # 512 MiB > L2 + MALL. A read of it leaves the caches holding clean
-        # lines of the flush buffer (cold records, nothing to write back); a
-        # write of it leaves dirty lines, whose write-back then competes with
-        # the lookup's own traffic (as after a layer that wrote its output).
-        flush = torch.empty(512 << 18, dtype=torch.int32, device="cuda")
-        flush.fill_(1)
-        sink = torch.empty((), dtype=torch.int64, device="cuda")
         reps = max(5, args.steps // 2)
-        per = time_each(step, reps, torch, before=lambda: torch.sum(flush, 0, dtype=torch.int64, out=sink))
+        per = time_each(step, reps, torch, before=clean_flush)
         flushed_ms = sum(per) / len(per)
         per.sort()
         res["flushed_launch_ms_p10_p50_p90"] = [q(per, 0.1), q(per, 0.5), q(per, 0.9)]
@@ -530,13 +616,18 @@ def main() -> int:
         res["flushed_dirty_launch_ms_mean"] = dirty_ms
         res["flushed_dirty_pct_hbm_peak"] = 100.0 * algo_bytes / (dirty_ms / 1e3) / 1e9 / HBM_PEAK_GBPS
         res["flush"] = "512 MiB read before each launch (clean eviction); dirty: 512 MiB written before each launch"
-        del flush, sink
-        torch.cuda.empty_cache()
     if not args.no_probes:
         # what plain HBM streams reach on this GPU: the lookup is mostly a
-        # write stream, so the fill is its closest measured ceiling
+        # write stream, so the fill is its closest measured ceiling; and the
+        # lookup's own output stream and record fetch timed alone
         res["probes"] = probes(torch)
         res["probes"]["effective_over_fill"] = res["effective_GBps"] / res["probes"]["fill_GBps"]
+        if not mixed:
+            fl = floor_probes(torch, np, records, R, cfg.d, ids_np, cfg.host_resident, clean_flush)
+            fl["lookup_over_store_only"] = launch_ms / fl["store_only_ms"]
+            res["probes"].update(fl)
+    del flush, sink
+    torch.cuda.empty_cache()
 
     if args.graph:
         res["graph"] = graph_timing(step, out, args.steps, torch)

@@ -33,6 +33,15 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, name), name
 
 
+def test_probe_library_exports_its_header():
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(cpbuild.ROOT, "include", "cp_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(cpp_\w+)\s*\(", text)))
+    assert names == ["cpp_gather_records", "cpp_read_stream", "cpp_store_rows"]
+    lib = ctypes.CDLL(cpbuild.PROBE_LIB)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
 def test_record_bytes_and_supported_shapes():
     for d in (64, 128, 256, 512):
         for kv in (3, 4, 5, 6):

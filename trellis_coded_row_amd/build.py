@@ -1,4 +1,6 @@
-"""Builds the HIP library (libcp.so) for gfx950 with hipcc, in-tree."""
+"""Builds the HIP libraries for gfx950 with hipcc, in-tree: libcp.so (the
+lookup library, include/cp.h) and libcp_probe.so (measurement probes,
+include/cp_probe.h)."""
 from __future__ import annotations
 
 import os
@@ -14,6 +16,8 @@ SOURCES = [os.path.join(CSRC, "cp_decode.hip"), os.path.join(CSRC, "cp_dedup.hip
 DEPS = SOURCES + [os.path.join(CSRC, "cp_internal.h"), os.path.join(CSRC, "cp_lane.h"),
                   os.path.join(ROOT, "include", "cp.h")]
 LIB = os.path.join(PKG, "libcp.so")
+PROBE_SOURCES = [os.path.join(CSRC, "cp_probe.hip")]
+PROBE_LIB = os.path.join(PKG, "libcp_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -38,18 +42,23 @@ def is_stale() -> bool:
     return any(os.path.getmtime(p) > t for p in DEPS)
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
-           *SOURCES, "-o", tmp]
+def _hipcc(sources: list[str], lib: str, verbose: bool, extra_flags: list[str] | None) -> str:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"), *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libcp.so")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"hipcc failed building {os.path.basename(lib)}")
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
+    """Builds both libraries; returns the path of libcp.so."""
+    _hipcc(PROBE_SOURCES, PROBE_LIB, verbose, extra_flags)
+    return _hipcc(SOURCES, LIB, verbose, extra_flags)
 
 
 if __name__ == "__main__":

@@ -49,13 +49,14 @@ namespace cpk {
 // rows, so hot row 32b + j is slot base + popcount(bits below j). Offsets are
 // then taken from `tab` = the lower of the two regions' addresses, the host
 // records starting at host_off0 and the cache at hot_off0.
-template <int D, int KV, bool RAW, int COPIES, int BLOCK, int CHUNK, bool HOT>
+template <int D, int KV, bool RAW, int COPIES, int BLOCK, int CHUNK, bool HOT, bool PREFETCH>
 __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict__ tab, const uint64_t rows,
                                                        const uint32_t *__restrict__ lut,
                                                        const int64_t *__restrict__ ids, const uint64_t n,
                                                        uint32_t *__restrict__ out, int *__restrict__ err,
                                                        const bool by_offset, const HotEntry *__restrict__ hot_index,
-                                                       const uint64_t host_off0, const uint64_t hot_off0)
+                                                       const uint64_t host_off0, const uint64_t hot_off0,
+                                                       const uint32_t gen)
 {
     constexpr int LANES = D / 8;        // lanes per row
     constexpr int GROUPS = 64 / LANES;  // rows decoded side by side in a wave
@@ -99,6 +100,48 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     // the first chunk's ids are requested before the codebook is staged, so
     // the two loads' latencies overlap (what a small batch waits for)
     int64_t my_id = load_id(wave);
+    // Workgroups of the first residency round (blockIdx < gen: one workgroup
+    // per CU) also read the ids, and touch the record lines, of the chunks
+    // that workgroups gen, 2 gen, ... later take with the same wave index (up
+    // to kPrefetchRounds rounds). Those run on the same XCD (workgroups are
+    // dealt to the XCDs in turn, and gen is a multiple of their count), so
+    // their id and record reads find the lines in the caches: uncached records
+    // come from HBM in one burst at the start, before the output stream is
+    // under way, instead of one round of misses after another while it is.
+    // The loaded words are only kept alive.
+    uint32_t touched = 0;
+    const bool pf_wave = PREFETCH && blockIdx.x < gen && gridDim.x > gen;
+    const uint64_t pf_step = (uint64_t)gen * WAVES;
+    int64_t pid[kPrefetchRounds];
+    if constexpr (PREFETCH) {
+        if (pf_wave) {
+#pragma unroll
+            for (int k = 0; k < kPrefetchRounds; ++k) pid[k] = load_id(wave + (uint64_t)(k + 1) * pf_step);
+        }
+    }
+    // The touches, issued right after this wave's own record loads: loads
+    // complete in order, so the wave's own decode never waits for them
+    // (issued before, they held up the first round's own work).
+    auto touch_later = [&]() {
+        if constexpr (PREFETCH) {
+            if (pf_wave) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int k = 0; k < kPrefetchRounds; ++k) {
+                    const uint64_t pc = wave + (uint64_t)(k + 1) * pf_step;
+                    if (pc >= nchunks) break;
+                    const uint64_t rid = (uint64_t)pid[k];
+                    const uint64_t off = by_offset ? ((int64_t)rid >= 0 ? rid : 0) : (rid < rows ? rid * R : 0);
+                    // lane l touches 64-byte segment l % 4 of the record of chunk row l / 4
+                    const uint64_t o = __shfl(off, (int)(lane >> 2), 64);
+                    const uint64_t seg = (o & ~(uint64_t)63) + 64u * (lane & 3u);
+                    if ((lane >> 2) < (uint32_t)CHUNK && seg < o + R) touched ^= ld32(tab + seg);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    bool first_chunk = true;
     stage_lut<BLOCK>(s_lut, lut);
     for (uint64_t c = wave; c < nchunks; c += waves) {
         // rows in this chunk
@@ -162,6 +205,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
                 nb[i] = row_bits(o);
                 ab[i] = row_scale(o);
             }
+            if (first_chunk) touch_later();
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
                 // every row is decoded (an invalid id reads record 0), so the
@@ -186,6 +230,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
                 nb[i] = row_bits(o);
                 ab[i] = row_scale(o);
             }
+            if (first_chunk) touch_later();
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
                 const uint32_t r = i * GROUPS + g;
@@ -219,6 +264,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
                 }
             }
         }
+        first_chunk = false;
         // Rows with an id outside the table were decoded from record 0 above;
         // overwrite them with zeros. Rare, so kept off the main path; the wait
         // orders the two stores to the same address.
@@ -234,6 +280,8 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
         }
     }
     if (bad) atomicOr(err, 1);
+    // the touched words count as used (no memory effect)
+    if constexpr (PREFETCH) asm volatile("" ::"v"(touched));
 }
 
 // ---------------------------------------------------------------------------
@@ -257,9 +305,11 @@ static hipError_t launch_shape(const LaunchArgs &a)
     const uint64_t nchunks = (a.n + CHUNK - 1) / CHUNK;
     uint64_t blocks = (nchunks + kBlock / 64 - 1) / (kBlock / 64);
     if (blocks > 0x7FFFFFFFull) blocks = 0x7FFFFFFFull;  // the chunk loop strides over any excess
-    hipLaunchKernelGGL((gather_decode<D, KV, RAW, kCopies, kBlock, CHUNK, HOT>), dim3((unsigned)blocks),
-                       dim3(kBlock), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err,
-                       a.by_offset, a.hot_index, a.host_off0, a.hot_off0);
+    // workgroups of one residency round: one per CU
+    const uint32_t gen = (uint32_t)(a.num_cus > 0 ? a.num_cus : 256);
+    hipLaunchKernelGGL((gather_decode<D, KV, RAW, kCopies, kBlock, CHUNK, HOT, !HOT>),
+                       dim3((unsigned)blocks), dim3(kBlock), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out,
+                       a.err, a.by_offset, a.hot_index, a.host_off0, a.hot_off0, gen);
     return hipGetLastError();
 }
 

@@ -15,6 +15,9 @@ namespace cpk {
 constexpr int kBlock = 1024;
 constexpr int kCopies = 16;
 constexpr int kChunk = 16;
+// Residency rounds ahead whose chunks the first round touches (the replay of
+// 393,216 lookups at d = 512 has 6 rounds on 256 CUs).
+constexpr int kPrefetchRounds = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
