@@ -451,18 +451,42 @@ def main() -> int:
 
     residency = cp.CP_RESIDENCY_HOST_MAPPED if cfg.host_resident else cp.CP_RESIDENCY_DEVICE
     flags = cp.CP_FLAG_HOST_NONCOHERENT if args.noncoherent else 0
+    encoded = (not mixed) and cfg.encoded_rows > 0
+
+    def fill(t) -> float | None:
+        """Uploads the records; for tables whose rows hold TCQ-encoded Gaussian
+        rows (the d64 and d256 tables all of them, the rate sweep rows
+        0..4095), the library's own encoder (cp_table_encode, bit-exact with
+        the oracle's: checked on a sample in the CPU-baseline leg) then writes
+        those rows over the random codes. Returns the encoding seconds."""
+        chunk = 1 << 22
+        if mixed:
+            for r0 in range(0, cfg.rows, chunk):
+                r1 = min(cfg.rows, r0 + chunk)
+                t.upload_bytes(records[int(offsets[r0]):int(offsets[r1])], r0, r1 - r0)
+        else:
+            for r0 in range(0, cfg.rows, chunk):
+                t.upload(records[r0:r0 + chunk], first_row=r0)
+        if not encoded:
+            return None
+        t_enc = time.time()
+        enc_ids = cfg.encoded_row_ids()
+        step = 1 << 16
+        ws = torch.empty(t.encode_workspace_bytes(step), dtype=torch.uint8, device="cuda")
+        for a in range(0, enc_ids.size, step):
+            b = min(a + step, enc_ids.size)
+            e = workload.table_rows(cfg.rows, cfg.d, cfg.rows_seed, enc_ids[a:b]).astype(np.float32)
+            t.encode(torch.from_numpy(e).cuda(), first_row=int(enc_ids[a]), workspace=ws)
+        torch.cuda.synchronize()
+        return time.time() - t_enc
+
     t_up = time.time()
-    chunk = 1 << 22
     if mixed:
         table = cp.MixedTable(cfg.d, kvs, classes, lut, residency=residency, flags=flags)
-        for r0 in range(0, cfg.rows, chunk):
-            r1 = min(cfg.rows, r0 + chunk)
-            table.upload_bytes(records[int(offsets[r0]):int(offsets[r1])], r0, r1 - r0)
     else:
         table = cp.Table(cfg.rows, cfg.d, cfg.kv, lut, residency=residency, flags=flags)
-        for r0 in range(0, cfg.rows, chunk):
-            table.upload(records[r0:r0 + chunk], first_row=r0)
-    upload_s = time.time() - t_up
+    enc_s = fill(table)
+    upload_s = time.time() - t_up - (enc_s or 0.0)
     hot_rows = 0
     hot_lookups = 0
     hot_set_np = None
@@ -544,8 +568,25 @@ def main() -> int:
         "pct_hbm_peak": 100.0 * algo_bytes * args.steps / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
         "launch_ms_mean": launch_ms,
         "wall_s_timed_region": wall_s,
-        "setup_s": {"generate": round(gen_s, 2), "upload": round(upload_s, 2)},
+        "setup_s": {"generate": round(gen_s, 2), "upload": round(upload_s, 2),
+                    "encode": round(enc_s, 2) if enc_s is not None else None},
     }
+    if encoded:
+        # reconstruction error of the encoded rows, from the lookup's own
+        # output: rows 0..4095 against the Gaussian rows they encode
+        mse_ids = np.arange(min(4096, cfg.encoded_rows), dtype=np.int64)
+        y = table.lookup_decode(torch.from_numpy(mse_ids).cuda()).float().cpu().numpy().astype(np.float64)
+        e = workload.table_rows(cfg.rows, cfg.d, cfg.rows_seed, mse_ids)
+        err2 = ((y - e) ** 2).sum(axis=1)
+        res["reconstruction"] = {
+            "rows": f"ids 0..{mse_ids.size - 1} (TCQ-encoded Gaussian rows)",
+            "mse_per_element": float(err2.sum() / e.size),
+            "relative_mse": float(err2.sum() / (e ** 2).sum()),
+            "mean_row_relative_error": float(np.mean(err2 / (e ** 2).sum(axis=1))),
+            "context": f"per-element MSE of the normalised row at {cfg.kv / 2:g} bits per element: Gaussian "
+                       f"rate-distortion bound {2.0 ** (-cfg.kv):.4f}",
+            "encoded_rows": int(cfg.encoded_rows), "encoded_by": "cp_table_encode (GPU)",
+        }
     counters = read_counter_summary(cfg.name, ids_kind, "mixed" if mixed else "single")
     kernel_name = f"gather_decode_mixed<{cfg.d}>" if mixed else f"gather_decode<{cfg.d},{cfg.kv}>"
     if cfg.host_resident:
@@ -616,6 +657,38 @@ def main() -> int:
         res["flushed_dirty_launch_ms_mean"] = dirty_ms
         res["flushed_dirty_pct_hbm_peak"] = 100.0 * algo_bytes / (dirty_ms / 1e3) / 1e9 / HBM_PEAK_GBPS
         res["flush"] = "512 MiB read before each launch (clean eviction); dirty: 512 MiB written before each launch"
+    if not args.no_flushed and not (mixed or cfg.host_resident or args.dedup or args.hot_share):
+        # The same lookups on a second table created with CP_FLAG_TOUCH_AHEAD
+        # (the first round of workgroups touches the later rounds' records):
+        # the choice for lookups that start with none of the table cached.
+        ta = cp.Table(cfg.rows, cfg.d, cfg.kv, lut, flags=cp.CP_FLAG_TOUCH_AHEAD)
+        fill(ta)
+        out_ta = torch.empty_like(out)
+        step_ta = lambda: ta.lookup_decode(ids, out_ta)
+        for _ in range(args.warmup):
+            step_ta()
+        ta_ms = time_region(step_ta, args.steps, torch) / args.steps
+        reps = max(5, args.steps // 2)
+        cold = time_each(step_ta, reps, torch, before=clean_flush)
+        dirty = time_each(step_ta, reps, torch, before=lambda: flush.fill_(0))
+        same = torch.equal(out_ta.view(torch.int16), out.view(torch.int16))
+        res["touch_ahead"] = {
+            "flag": "CP_FLAG_TOUCH_AHEAD",
+            "launch_ms_mean": ta_ms,
+            "pct_hbm_peak": 100.0 * algo_bytes / (ta_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+            "flushed_launch_ms_mean": sum(cold) / len(cold),
+            "flushed_pct_hbm_peak": 100.0 * algo_bytes / (sum(cold) / len(cold) / 1e3) / 1e9 / HBM_PEAK_GBPS,
+            "flushed_dirty_launch_ms_mean": sum(dirty) / len(dirty),
+            "flushed_dirty_pct_hbm_peak": 100.0 * algo_bytes / (sum(dirty) / len(dirty) / 1e3) / 1e9
+            / HBM_PEAK_GBPS,
+            "rows_identical_to_default_table": bool(same),
+        }
+        ta.close()
+        del out_ta
+        torch.cuda.empty_cache()
+        if not same:
+            print("the touch-ahead table's rows differ from the default table's", file=sys.stderr)
+            return 1
     if not args.no_probes:
         # what plain HBM streams reach on this GPU: the lookup is mostly a
         # write stream, so the fill is its closest measured ceiling; and the
@@ -659,6 +732,10 @@ def main() -> int:
         exp, _ = decode(ids_np[:sample])
         cpu_s = time.perf_counter() - t
         got = out[:sample].view(torch.int16).cpu().numpy().view(np.uint16)
+        # lookups of rows the GPU encoded are checked in encoder_check below
+        plain = np.ones(sample, dtype=bool)
+        if encoded:
+            plain = ids_np[:sample] >= cfg.encoded_rows if cfg.encoded == "first" else np.zeros(sample, dtype=bool)
         res["cpu_baseline"] = {
             "value": sample / cpu_s,
             "unit": "rows/s",
@@ -666,7 +743,8 @@ def main() -> int:
             "kind": "oracle",
             "sample": f"first {sample:,} of the {n:,} replay ids ({cpu_s:.1f} s, {threads} threads, "
                       f"plain C oracle, bit-by-bit trellis walk, fp64 scaling)",
-            "gpu_rows_matching_oracle": int((got == exp).all(axis=1).sum()),
+            "gpu_rows_matching_oracle": f"{int((got[plain] == exp[plain]).all(axis=1).sum())} of {int(plain.sum())}"
+                                        + (" (rows with random codes; encoded rows: encoder_check)" if encoded else ""),
         }
         # the same oracle on one thread, over a bounded slice of the replay
         one = min(n, 32768)
@@ -676,6 +754,34 @@ def main() -> int:
         res["cpu_baseline"]["single_thread"] = {"value": one / one_s, "unit": "rows/s",
                                                 "sample": f"first {one:,} replay ids ({one_s:.2f} s)"}
         res["cpu_baseline"]["host"] = {"cpus": os.cpu_count(), "model": host_cpu_model()}
+        if encoded:
+            # The GPU-encoded rows against the oracle's own encoding of the same
+            # Gaussian rows, and their lookup against the oracle decoding its
+            # own records (nothing the GPU produced goes into the oracle). The
+            # check ids: the first 4,096 replay ids when every row is encoded,
+            # else ids 0..4095; the replay sample above decodes the random-code
+            # records, which time the same as encoded ones.
+            chk_ids = ids_np[:4096] if cfg.encoded == "all" else np.arange(min(4096, cfg.encoded_rows),
+                                                                             dtype=np.int64)
+            chk_rows = np.unique(chk_ids)
+            t = time.perf_counter()
+            own, _ = oracle.encode_rows(workload.table_rows(cfg.rows, cfg.d, cfg.rows_seed, chk_rows), cfg.d,
+                                        cfg.kv, lut, mode=oracle.ENC_HEURISTIC, nthreads=threads)
+            enc_cpu_s = time.perf_counter() - t
+            lo, hi = int(chk_rows.min()), int(chk_rows.max()) + 1
+            gpu_recs = table.download(lo, hi - lo)[chk_rows - lo]
+            table_own = records.copy()
+            table_own[chk_rows] = own
+            exp_chk, _ = oracle.lookup_decode(lut, table_own, cfg.rows, cfg.d, cfg.kv, chk_ids, nthreads=threads)
+            got_chk = table.lookup_decode(torch.from_numpy(chk_ids).cuda()).view(torch.int16).cpu().numpy()
+            res["cpu_baseline"]["encoder_check"] = {
+                "rows": int(chk_rows.size),
+                "gpu_records_matching_oracle_encoding": int((gpu_recs == own).all(axis=1).sum()),
+                "gpu_rows_matching_oracle_decode": int((got_chk.view(np.uint16) == exp_chk).all(axis=1).sum()),
+                "lookups_checked": int(chk_ids.size),
+                "oracle_encode_rows_per_s": chk_rows.size / enc_cpu_s,
+            }
+            del table_own
     table.close()
     print(json.dumps(res), flush=True)
     return 0

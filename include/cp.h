@@ -86,7 +86,16 @@ typedef enum {
 enum {
     /* with CP_RESIDENCY_HOST_MAPPED: allocate the pinned memory non-coherent,
      * so the GPU may cache records it has read */
-    CP_FLAG_HOST_NONCOHERENT = 1u << 0
+    CP_FLAG_HOST_NONCOHERENT = 1u << 0,
+    /* with CP_RESIDENCY_DEVICE (single-rate tables): in lookups that take
+     * more than one round of workgroups, the first round also reads the ids
+     * and touches the record lines of the later rounds' lookups, so that
+     * records not in the caches come from HBM in one burst before the output
+     * stream is under way. Pays when a lookup starts with none of the table in
+     * the caches (after other kernels; the replay's launch drops from ~90 to
+     * ~80 us on MI355X), costs a few percent when lookups of the same rows run
+     * back to back. Results are the same either way. */
+    CP_FLAG_TOUCH_AHEAD = 1u << 1
 };
 
 typedef struct {
@@ -139,7 +148,8 @@ int cp_supported(uint32_t d, uint32_t bits_per_step);
  * (+ a small zeroed tail), pinned host memory the same for
  * CP_RESIDENCY_HOST_MAPPED.
  * Errors: INVALID_ARGUMENT (NULL pointers, struct_size, rows == 0, unknown
- * residency or flags, a codebook entry that is +-inf or NaN), UNSUPPORTED,
+ * residency or flags (CP_FLAG_TOUCH_AHEAD with host residency), a codebook
+ * entry that is +-inf or NaN), UNSUPPORTED,
  * OUT_OF_MEMORY (the records do not fit in device or pinned host memory; the
  * library stays usable), HIP. */
 cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, cp_table **out);

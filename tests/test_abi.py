@@ -74,7 +74,7 @@ def test_create_rejects_bad_descriptors_before_touching_the_device():
         (_desc(struct_size=8), cp.CP_ERR_INVALID_ARGUMENT),
         (_desc(rows=0), cp.CP_ERR_INVALID_ARGUMENT),
         (_desc(residency=7), cp.CP_ERR_INVALID_ARGUMENT),
-        (_desc(flags=2), cp.CP_ERR_INVALID_ARGUMENT),
+        (_desc(flags=4), cp.CP_ERR_INVALID_ARGUMENT),
         (_desc(reserved=1), cp.CP_ERR_INVALID_ARGUMENT),
         (_desc(d=10), cp.CP_ERR_INVALID_ARGUMENT),
         (_desc(d=96), cp.CP_ERR_UNSUPPORTED),
@@ -217,3 +217,14 @@ def test_noalloc_limit_matches_the_header_and_null_table_is_refused():
     m = re.search(r"#define CP_DEDUP_NOALLOC_MAX_IDS (\d+)u", text)
     assert m and int(m.group(1)) == cp.CP_DEDUP_NOALLOC_MAX_IDS
     assert cp.cp_lookup_decode_dedup_noalloc(0, 8, 1, 16, None) == cp.CP_ERR_INVALID_ARGUMENT
+
+
+def test_touch_ahead_is_for_single_rate_device_tables():
+    lut = (ctypes.c_uint16 * 1024)()
+    st, h = cp.cp_table_create(_desc(residency=cp.CP_RESIDENCY_HOST_MAPPED, flags=cp.CP_FLAG_TOUCH_AHEAD),
+                               ctypes.addressof(lut))
+    assert (st, h) == (cp.CP_ERR_INVALID_ARGUMENT, 0)
+    cls = (ctypes.c_uint8 * 8)(0, 1, 0, 1, 1, 1, 0, 0)
+    st, h = cp.cp_table_create_mixed(_mdesc(flags=cp.CP_FLAG_TOUCH_AHEAD), ctypes.addressof(lut),
+                                     ctypes.addressof(cls))
+    assert (st, h) == (cp.CP_ERR_INVALID_ARGUMENT, 0)

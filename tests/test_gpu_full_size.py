@@ -1,6 +1,12 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times: every output of each 393,216-lookup replay is compared with
-the CPU oracle (raw f(c) bit-exact, scaled rows within 1 bf16 ulp)."""
+the CPU oracle (raw f(c) and scaled rows bit-exact).
+
+Encoded rows are encoded by the oracle here: rows 0..4095 of each rate-sweep
+table, and the 16,384 most looked-up rows of the 1,048,576-row d256 table
+(84% of its replay's lookups; all of its rows would take the oracle about a
+quarter of an hour on 16 threads, so the benchmark encodes that table on the
+GPU and checks a sample against the oracle)."""
 from __future__ import annotations
 
 import numpy as np
@@ -28,15 +34,19 @@ def encoder(cfg):
     return lambda e: oracle.encode_rows(e, cfg.d, cfg.kv, LUT, oracle.ENC_HEURISTIC)[0]
 
 
+SMALL_ENCODED = 16384
+
+
 def test_small_d256_replay():
     cfg = workload.CONFIGS["small_d256"]
-    say("building the 1,048,576 x d256 table")
-    recs = workload.build_records(cfg, encode_fn=encoder(cfg))
+    say(f"building the 1,048,576 x d256 table ({SMALL_ENCODED} hottest rows encoded by the oracle)")
+    recs = workload.build_records(cfg, encode_fn=encoder(cfg), encode_limit=SMALL_ENCODED)
     t = make_table(LUT, recs, cfg.d, cfg.kv)
     try:
-        check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), "small_d256 zipf replay")
-        check_lookup(t, LUT, recs, cfg.d, cfg.kv, np.arange(cfg.encoded_rows, dtype=np.int64),
-                     "small_d256 encoded rows")
+        ids = cfg.ids()
+        assert np.isin(ids, cfg.encoded_row_ids(SMALL_ENCODED)).mean() > 0.8
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, ids, "small_d256 zipf replay")
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.encoded_row_ids(SMALL_ENCODED), "small_d256 encoded rows")
     finally:
         t.close()
 
@@ -49,8 +59,7 @@ def test_rate_sweep_replay(kv):
     t = make_table(LUT, recs, cfg.d, cfg.kv)
     try:
         check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), f"rate kv{kv} zipf replay")
-        check_lookup(t, LUT, recs, cfg.d, cfg.kv, np.arange(cfg.encoded_rows, dtype=np.int64),
-                     f"rate kv{kv} encoded rows")
+        check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.encoded_row_ids(), f"rate kv{kv} encoded rows (0..4095)")
     finally:
         t.close()
 

@@ -240,3 +240,25 @@ def test_dedup_rejects_a_small_workspace():
         assert (out.view(torch.int16).cpu().numpy().view(np.uint16) == exp).all()
     finally:
         t.close()
+
+
+@pytest.mark.parametrize("d,kv", [(512, 4), (512, 3), (512, 6), (256, 4), (64, 5)])
+def test_touch_ahead_tables(d, kv):
+    # CP_FLAG_TOUCH_AHEAD: the first round of workgroups also reads the later
+    # rounds' ids and touches their records; the rows must not change. Batch
+    # sizes with two and more rounds at 4- and 16-lookup chunks, ragged,
+    # with ids outside the table (whose touches read record 0)
+    rows = 200_003
+    recs = workload.random_records(rows, d, kv, seed=1700 + d + kv)
+    t = cp.Table(rows, d, kv, LUT, flags=cp.CP_FLAG_TOUCH_AHEAD)
+    try:
+        t.upload(recs)
+        rng = np.random.default_rng(d + 3 * kv)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        for n in (20 * cus * 4 + 17, 3 * cus * 16 * 16 + 5, 393_216):
+            ids = workload.zipf_ids(rows, n, seed=n + d)
+            ids[rng.integers(0, n, 5)] = rows + 7
+            ids[-1] = -1
+            check_lookup(t, LUT, recs, d, kv, ids, f"touch-ahead d{d} kv{kv} n{n}", expect_bad=int((ids >= rows).sum() + 1))
+    finally:
+        t.close()

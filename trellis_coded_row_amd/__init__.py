@@ -36,7 +36,7 @@ __all__ = [
     "cp_status_string", "cp_last_hip_error",
     "CP_OK", "CP_ERR_INVALID_ARGUMENT", "CP_ERR_UNSUPPORTED", "CP_ERR_OUT_OF_MEMORY", "CP_ERR_HIP",
     "CP_ERR_ID_OUT_OF_RANGE", "CP_RESIDENCY_DEVICE", "CP_RESIDENCY_HOST_MAPPED",
-    "CP_FLAG_HOST_NONCOHERENT",
+    "CP_FLAG_HOST_NONCOHERENT", "CP_FLAG_TOUCH_AHEAD",
 ]
 
 CP_OK = 0
@@ -48,6 +48,7 @@ CP_ERR_ID_OUT_OF_RANGE = 5
 CP_RESIDENCY_DEVICE = 0
 CP_RESIDENCY_HOST_MAPPED = 1
 CP_FLAG_HOST_NONCOHERENT = 1
+CP_FLAG_TOUCH_AHEAD = 2
 CP_DEDUP_NOALLOC_MAX_IDS = 65536
 
 

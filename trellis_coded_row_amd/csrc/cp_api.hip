@@ -173,7 +173,8 @@ static bool finite_codebook(const uint16_t *lut_fp16)
 static bool valid_residency(uint32_t residency, uint32_t flags)
 {
     if (residency != CP_RESIDENCY_DEVICE && residency != CP_RESIDENCY_HOST_MAPPED) return false;
-    return (flags & ~(uint32_t)CP_FLAG_HOST_NONCOHERENT) == 0;
+    if (residency == CP_RESIDENCY_HOST_MAPPED && (flags & CP_FLAG_TOUCH_AHEAD)) return false;
+    return (flags & ~(uint32_t)(CP_FLAG_HOST_NONCOHERENT | CP_FLAG_TOUCH_AHEAD)) == 0;
 }
 
 cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, cp_table **out)
@@ -211,6 +212,7 @@ cp_status cp_table_create_mixed(const cp_mixed_desc *desc, const uint16_t *lut_f
         return CP_ERR_INVALID_ARGUMENT;
     if (desc->nclass < 1 || desc->nclass > 4) return CP_ERR_INVALID_ARGUMENT;
     if (!valid_residency(desc->residency, desc->flags) || !finite_codebook(lut_fp16)) return CP_ERR_INVALID_ARGUMENT;
+    if (desc->flags & CP_FLAG_TOUCH_AHEAD) return CP_ERR_INVALID_ARGUMENT;  // single-rate tables only
     uint32_t R[4] = {0, 0, 0, 0};
     for (uint32_t c = 0; c < desc->nclass; ++c) {
         R[c] = (uint32_t)cp_record_bytes(desc->d, desc->bits_per_step[c]);
@@ -420,6 +422,7 @@ static cp_status lookup(const cp_table *t, const int64_t *ids, uint64_t n, uint1
     a.ids = ids;
     a.n = n;
     a.by_offset = false;
+    a.touch_ahead = (t->desc.flags & CP_FLAG_TOUCH_AHEAD) != 0;
     a.out = reinterpret_cast<uint32_t *>(out);
     a.err = t->err_dev;
     a.num_cus = t->num_cus;

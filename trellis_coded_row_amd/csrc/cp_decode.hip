@@ -49,7 +49,7 @@ namespace cpk {
 // rows, so hot row 32b + j is slot base + popcount(bits below j). Offsets are
 // then taken from `tab` = the lower of the two regions' addresses, the host
 // records starting at host_off0 and the cache at hot_off0.
-template <int D, int KV, bool RAW, int COPIES, int BLOCK, int CHUNK, bool HOT, bool PREFETCH>
+template <int D, int KV, bool RAW, int COPIES, int BLOCK, int CHUNK, bool HOT, bool AHEAD>
 __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict__ tab, const uint64_t rows,
                                                        const uint32_t *__restrict__ lut,
                                                        const int64_t *__restrict__ ids, const uint64_t n,
@@ -110,10 +110,10 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     // under way, instead of one round of misses after another while it is.
     // The loaded words are only kept alive.
     uint32_t touched = 0;
-    const bool pf_wave = PREFETCH && blockIdx.x < gen && gridDim.x > gen;
+    const bool pf_wave = AHEAD && blockIdx.x < gen && gridDim.x > gen;
     const uint64_t pf_step = (uint64_t)gen * WAVES;
     int64_t pid[kPrefetchRounds];
-    if constexpr (PREFETCH) {
+    if constexpr (AHEAD) {
         if (pf_wave) {
 #pragma unroll
             for (int k = 0; k < kPrefetchRounds; ++k) pid[k] = load_id(wave + (uint64_t)(k + 1) * pf_step);
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     // complete in order, so the wave's own decode never waits for them
     // (issued before, they held up the first round's own work).
     auto touch_later = [&]() {
-        if constexpr (PREFETCH) {
+        if constexpr (AHEAD) {
             if (pf_wave) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -175,8 +175,12 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
                 // lane l's 16 new bits are code half-word l (records are 2-byte aligned)
                 return *reinterpret_cast<const uint16_t *>(tab + o + 2u * l);
             } else {
-                const uint64_t bit = o * 8 + (uint64_t)NEWB * l;
-                const uint8_t *p = tab + ((bit >> 5) << 2);
+                // the two aligned dwords that hold lane l's bits: a base that
+                // is uniform when o is (d = 512) plus a small per-lane offset,
+                // so the loads take a scalar base and a 32-bit lane offset
+                const uint8_t *base = tab + (o & ~(uint64_t)3);
+                const uint32_t bit = (uint32_t)(o & 3u) * 8u + NEWB * l;
+                const uint8_t *p = base + ((bit >> 5) << 2);
                 const uint64_t both = ((uint64_t)ld32(p + 4) << 32) | ld32(p);
                 return (uint32_t)(both >> (bit & 31)) & ((1u << NEWB) - 1u);
             }
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     }
     if (bad) atomicOr(err, 1);
     // the touched words count as used (no memory effect)
-    if constexpr (PREFETCH) asm volatile("" ::"v"(touched));
+    if constexpr (AHEAD) asm volatile("" ::"v"(touched));
 }
 
 // ---------------------------------------------------------------------------
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
 // once depends on the instance's registers: the d = 512 kernels hold 16 rows'
 // record offsets and scales in SGPRs, which leaves room for one 1024-thread
 // workgroup per CU (16 waves), the next one starting as its waves retire.
-template <int D, int KV, bool RAW, bool HOT, int CHUNK_ROWS>
+template <int D, int KV, bool RAW, bool HOT, bool AHEAD, int CHUNK_ROWS>
 static hipError_t launch_shape(const LaunchArgs &a)
 {
     constexpr int GROUPS = 64 / (D / 8);
@@ -307,32 +311,40 @@ static hipError_t launch_shape(const LaunchArgs &a)
     if (blocks > 0x7FFFFFFFull) blocks = 0x7FFFFFFFull;  // the chunk loop strides over any excess
     // workgroups of one residency round: one per CU
     const uint32_t gen = (uint32_t)(a.num_cus > 0 ? a.num_cus : 256);
-    hipLaunchKernelGGL((gather_decode<D, KV, RAW, kCopies, kBlock, CHUNK, HOT, !HOT>),
-                       dim3((unsigned)blocks), dim3(kBlock), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out,
-                       a.err, a.by_offset, a.hot_index, a.host_off0, a.hot_off0, gen);
+    hipLaunchKernelGGL((gather_decode<D, KV, RAW, kCopies, kBlock, CHUNK, HOT, AHEAD>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err, a.by_offset,
+                       a.hot_index, a.host_off0, a.hot_off0, gen);
     return hipGetLastError();
 }
 
-template <int D, int KV, bool RAW, bool HOT>
-static hipError_t launch_one(const LaunchArgs &a)
+template <int D, int KV, bool RAW, bool HOT, bool AHEAD>
+static hipError_t launch_chunked(const LaunchArgs &a)
 {
     switch (lookup_chunk_rows(a.n, a.num_cus)) {
-    case 1: return launch_shape<D, KV, RAW, HOT, 1>(a);
-    case 4: return launch_shape<D, KV, RAW, HOT, 4>(a);
-    default: return launch_shape<D, KV, RAW, HOT, kChunk>(a);
+    case 1: return launch_shape<D, KV, RAW, HOT, AHEAD, 1>(a);
+    case 4: return launch_shape<D, KV, RAW, HOT, AHEAD, 4>(a);
+    default: return launch_shape<D, KV, RAW, HOT, AHEAD, kChunk>(a);
     }
+}
+
+// the table's residency and flags pick the variant: records partly in an HBM
+// copy (HOT, pinned-host tables), touch-ahead (device tables), or plain
+template <int D, int KV, bool RAW>
+static hipError_t launch_one(const LaunchArgs &a)
+{
+    if (a.hot_index) return launch_chunked<D, KV, RAW, true, false>(a);
+    if (a.touch_ahead) return launch_chunked<D, KV, RAW, false, true>(a);
+    return launch_chunked<D, KV, RAW, false, false>(a);
 }
 
 typedef hipError_t (*launch_fn)(const LaunchArgs &);
 
 struct Entry {
     uint32_t d, kv;
-    launch_fn scaled, raw, hot_scaled, hot_raw;
+    launch_fn scaled, raw;
 };
 
-#define CP_ENTRY(D, KV)                                                                                   \
-    {D, KV, &launch_one<D, KV, false, false>, &launch_one<D, KV, true, false>, &launch_one<D, KV, false, true>, \
-     &launch_one<D, KV, true, true>}
+#define CP_ENTRY(D, KV) {D, KV, &launch_one<D, KV, false>, &launch_one<D, KV, true>}
 
 static const Entry kTable[] = {
     CP_ENTRY(64, 3),  CP_ENTRY(64, 4),  CP_ENTRY(64, 5),  CP_ENTRY(64, 6),
@@ -354,7 +366,6 @@ hipError_t launch(uint32_t d, uint32_t kv, bool raw, const LaunchArgs &a)
 {
     const Entry *e = find(d, kv);
     if (!e) return hipErrorInvalidValue;
-    if (a.hot_index) return raw ? e->hot_raw(a) : e->hot_scaled(a);
     return raw ? e->raw(a) : e->scaled(a);
 }
 

@@ -36,6 +36,7 @@ struct LaunchArgs {
     const int64_t *ids;       // row ids, or (by_offset) record byte offsets, -1 = invalid
     uint64_t n;
     bool by_offset;           // ids hold byte offsets of records (a staging area)
+    bool touch_ahead = false; // the first round touches the later rounds' records
     uint32_t *out;            // n * d / 2 dwords (pairs of bf16 or fp16)
     int *err;                 // sticky out-of-range flag
     int num_cus;              // compute units of the device

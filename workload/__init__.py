@@ -51,6 +51,43 @@ def gaussian_rows(n: int, d: int, seed: int) -> np.ndarray:
     return g / np.linalg.norm(g, axis=1, keepdims=True) * rho[:, None]
 
 
+ROW_CHUNK = 1 << 16
+
+
+def table_rows(rows: int, d: int, seed: int, row_ids: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """The Gaussian rows (as gaussian_rows) of a table's rows `row_ids`, each
+    row fixed by (seed, row id) alone: chunk c of ROW_CHUNK rows is drawn from
+    default_rng([seed, c]), so any subset of the rows can be produced without
+    the others. float64[len(row_ids), d], in the order given."""
+    row_ids = np.asarray(row_ids, dtype=np.int64)
+    out = np.empty((row_ids.size, d), dtype=np.float64)
+    chunk_of = row_ids // ROW_CHUNK
+
+    def fill(c: int) -> None:
+        sel = np.nonzero(chunk_of == c)[0]
+        n = min(ROW_CHUNK, rows - c * ROW_CHUNK)
+        rng = np.random.default_rng([seed, int(c)])
+        g = rng.standard_normal((n, d))
+        rho = rng.lognormal(0.0, 0.5, size=n)
+        local = row_ids[sel] - c * ROW_CHUNK
+        gs = g[local]
+        out[sel] = gs / np.linalg.norm(gs, axis=1, keepdims=True) * rho[local][:, None]
+
+    chunks = np.unique(chunk_of)
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, [int(c) for c in chunks]))
+    return out
+
+
+def hottest_rows(rows: int, k: int, ids_seed: int) -> np.ndarray:
+    """The rows of the k smallest Zipf ranks of the id stream of `ids_seed`
+    (zipf_ids sends rank r to row keyed_permutation(r)): its most looked-up
+    rows, hottest first."""
+    return keyed_permutation(np.arange(min(k, rows), dtype=np.int64), rows, ids_seed)
+
+
 def _bf16_bits(x: np.ndarray) -> np.ndarray:
     """Nearest bf16 (ties to even) of each value's float32, as uint16."""
     b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
@@ -238,7 +275,8 @@ class TableConfig:
     ids_kind: str              # "uniform" or "zipf"
     n_ids: int
     ids_seed: int
-    encoded_rows: int          # rows 0..encoded_rows-1 are oracle-encoded Gaussian rows
+    encoded_rows: int          # how many rows hold TCQ-encoded Gaussian rows (see encoded_row_ids)
+    encoded: str = "first"     # which: "first" (rows 0..encoded_rows-1) or "all"
     host_resident: bool = False
     uniform_seed: int | None = None
     description: str = ""
@@ -261,14 +299,32 @@ class TableConfig:
         assert self.uniform_seed is not None
         return uniform_ids(self.rows, self.n_ids, self.uniform_seed)
 
+    @property
+    def rows_seed(self) -> int:
+        """Seed of the table's Gaussian rows (table_rows)."""
+        return self.table_seed + 1000
+
+    def encoded_row_ids(self, limit: int | None = None) -> np.ndarray:
+        """The rows that hold encoded Gaussian rows (the others hold random
+        codes). With `limit` below that count (a test that encodes on the
+        CPU), the `limit` most looked-up rows of the config's id stream
+        among them instead: where most lookups go."""
+        if self.encoded == "all":
+            if limit is None or limit >= self.rows:
+                return np.arange(self.rows, dtype=np.int64)
+            return hottest_rows(self.rows, limit, self.ids_seed)
+        k = self.encoded_rows if limit is None else min(limit, self.encoded_rows)
+        return np.arange(k, dtype=np.int64)
+
 
 CONFIGS = {
     "tiny_d64": TableConfig(
         "tiny_d64", 4096, 64, 4, 100, "uniform", 1024, 300, encoded_rows=4096,
         description="4,096 x d64 table, every row TCQ-encoded; 1,024 uniform ids"),
     "small_d256": TableConfig(
-        "small_d256", 1 << 20, 256, 4, 101, "zipf", REPLAY_IDS, 201, encoded_rows=1024,
-        description="1,048,576 x d256 table (66-byte records); 393,216-id Zipf(1.1) replay"),
+        "small_d256", 1 << 20, 256, 4, 101, "zipf", REPLAY_IDS, 201, encoded_rows=1 << 20, encoded="all",
+        description="1,048,576 x d256 table (66-byte records), every row TCQ-encoded; 393,216-id Zipf(1.1) "
+                    "replay"),
     "gpu_d512": TableConfig(
         "gpu_d512", 97_690_000, 512, 4, 102, "zipf", REPLAY_IDS, 202, encoded_rows=0,
         uniform_seed=302,
@@ -287,22 +343,18 @@ CONFIGS["mixed_d512"] = TableConfig(
 for _kv in (3, 4, 5, 6):
     CONFIGS[f"rate_d512_kv{_kv}"] = TableConfig(
         f"rate_d512_kv{_kv}", 1 << 22, 512, _kv, 103, "zipf", REPLAY_IDS, 203,
-        encoded_rows=256,
+        encoded_rows=4096,
         description=f"4,194,304 x d512 table at {_kv} bits per step "
-                    f"({_kv / 2:g} bits per element)")
+                    f"({_kv / 2:g} bits per element), rows 0..4095 TCQ-encoded")
 
 
-def build_records(cfg: TableConfig, encode_fn=None, first: int = 0,
-                  count: int | None = None) -> np.ndarray:
-    """Records [first, first+count) of a config's table. Rows below
-    cfg.encoded_rows are produced by encode_fn(e[n, d]) -> uint8[n, R] (the
-    oracle's encoder, passed in by the caller); all other rows are random
-    codes. With encode_fn None, every row is a random code."""
-    if count is None:
-        count = cfg.rows - first
-    out = random_records(cfg.rows, cfg.d, cfg.kv, cfg.table_seed, first, count)
-    enc_hi = min(cfg.encoded_rows, first + count)
-    if encode_fn is not None and first < enc_hi:
-        e = gaussian_rows(cfg.encoded_rows, cfg.d, cfg.table_seed + 1000)
-        out[: enc_hi - first] = encode_fn(e[first:enc_hi])
+def build_records(cfg: TableConfig, encode_fn=None, encode_limit: int | None = None) -> np.ndarray:
+    """All records of a config's table: random codes, with the rows
+    cfg.encoded_row_ids(encode_limit) replaced by encode_fn(e[n, d]) ->
+    uint8[n, R] of their Gaussian rows (the caller passes the encoder, e.g.
+    the oracle's). With encode_fn None, every row is a random code."""
+    out = random_records(cfg.rows, cfg.d, cfg.kv, cfg.table_seed)
+    if encode_fn is not None and cfg.encoded_rows:
+        sel = cfg.encoded_row_ids(encode_limit)
+        out[sel] = encode_fn(table_rows(cfg.rows, cfg.d, cfg.rows_seed, sel))
     return out
