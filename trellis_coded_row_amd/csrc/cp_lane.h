@@ -236,8 +236,10 @@ __device__ __forceinline__ void stage_lut(uint32_t *s_lut, const uint32_t *__res
 __device__ __forceinline__ uint32_t lane_bits(const uint8_t *__restrict__ tab, uint64_t o, uint32_t newb,
                                               uint32_t l)
 {
-    const uint64_t bit = o * 8 + (uint64_t)newb * l;
-    const uint8_t *p = tab + ((bit >> 5) << 2);
+    // a base that is uniform when o is (d = 512) plus a small lane offset
+    const uint8_t *base = tab + (o & ~(uint64_t)3);
+    const uint32_t bit = (uint32_t)(o & 3u) * 8u + newb * l;
+    const uint8_t *p = base + ((bit >> 5) << 2);
     const uint64_t both = ((uint64_t)ld32(p + 4) << 32) | ld32(p);
     return (uint32_t)(both >> (bit & 31)) & ((1u << newb) - 1u);
 }
