@@ -36,7 +36,7 @@ CSRC = os.path.join(ROOT, "trellis_coded_row_amd", "csrc")
 KERNEL_SOURCES = {
     "single": ("cp_decode.hip", "cp_lane.h"),
     "mixed": ("cp_mixed.hip", "cp_lane.h"),
-    "encode": ("cp_encode.hip",),
+    "encode": ("cp_encode.hip", "cp_encode_copies.h"),
 }
 PROFILES = os.path.join(ROOT, "profiles")
 

@@ -20,10 +20,10 @@ pytestmark = pytest.mark.gpu
 LUT = workload.lut_fp16()
 
 
-def gpu_encode(e32: np.ndarray, d: int, kv: int, table_rows: int | None = None, first_row: int = 0):
+def gpu_encode(e32: np.ndarray, d: int, kv: int, table_rows: int | None = None, first_row: int = 0, lut=LUT):
     n = e32.shape[0]
     rows = table_rows if table_rows is not None else max(n, 1)
-    t = cp.Table(rows, d, kv, LUT)
+    t = cp.Table(rows, d, kv, lut)
     if first_row or rows != n:
         t.upload(np.zeros((rows, t.record_bytes), dtype=np.uint8))
     dev = torch.from_numpy(np.ascontiguousarray(e32, dtype=np.float32)).cuda()
@@ -32,8 +32,8 @@ def gpu_encode(e32: np.ndarray, d: int, kv: int, table_rows: int | None = None, 
     return t, t.download()
 
 
-def oracle_encode(e32: np.ndarray, d: int, kv: int) -> np.ndarray:
-    recs, _ = oracle.encode_rows(e32.astype(np.float64), d, kv, LUT, mode=oracle.ENC_HEURISTIC)
+def oracle_encode(e32: np.ndarray, d: int, kv: int, lut=LUT) -> np.ndarray:
+    recs, _ = oracle.encode_rows(e32.astype(np.float64), d, kv, lut, mode=oracle.ENC_HEURISTIC)
     return recs
 
 
@@ -78,6 +78,28 @@ def test_encode_matches_oracle(d, kv, n):
     check_lookup(t, LUT, exp, d, kv, ids, f"decode of encoded d{d} kv{kv}")
     t.close()
     say(f"encode d={d} kv={kv} n={n}: ok")
+
+
+@pytest.mark.parametrize("kind", ["paired", "constant", "two-valued"])
+@pytest.mark.parametrize("kv", [3, 4, 5, 6])
+def test_encode_tie_codebooks(kv, kind):
+    """Codebooks under which many paths and many branch metrics are equal
+    (the same ones whose tie rule the CPU tests pin by brute force): the
+    GPU's add-compare-select must keep the same predecessor and end memory
+    as the oracle on every tie."""
+    from test_oracle import _tie_lut
+
+    d = 64
+    lut = _tie_lut(kind)
+    rng = np.random.default_rng(900 + kv)
+    rows = [np.full(d, 0.5), np.eye(d)[0] - np.eye(d)[d // 2], np.tile([2.0, 0, 0, 0.75, -1.0, 0, 0.25, 0.5], d // 8),
+            np.round(rng.standard_normal(d) * 2) / 2, rng.standard_normal(d)]
+    e = np.stack(rows).astype(np.float32)
+    say(f"encode tie codebook {kind} kv={kv}")
+    exp = oracle_encode(e, d, kv, lut)
+    t, got = gpu_encode(e, d, kv, lut=lut)
+    check_records(got, exp, f"tie codebook {kind} kv{kv}")
+    t.close()
 
 
 @pytest.mark.parametrize("d", [64, 512])

@@ -14,6 +14,7 @@ SOURCES = [os.path.join(CSRC, "cp_decode.hip"), os.path.join(CSRC, "cp_dedup.hip
            os.path.join(CSRC, "cp_encode.hip"), os.path.join(CSRC, "cp_mixed.hip"),
            os.path.join(CSRC, "cp_api.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, "cp_internal.h"), os.path.join(CSRC, "cp_lane.h"),
+                  os.path.join(CSRC, "cp_encode_copies.h"),
                   os.path.join(ROOT, "include", "cp.h")]
 LIB = os.path.join(PKG, "libcp.so")
 PROBE_SOURCES = [os.path.join(CSRC, "cp_probe.hip")]

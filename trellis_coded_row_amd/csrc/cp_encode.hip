@@ -29,7 +29,10 @@
 // back-pointers (one byte per memory per step) in a caller workspace.
 #pragma clang fp contract(off)
 
+#include "cp_encode_copies.h"
 #include "cp_internal.h"
+
+#include <type_traits>
 
 namespace cpk {
 
@@ -56,11 +59,6 @@ __device__ __forceinline__ uint16_t bf16_rne(double x)
     return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
-// Path-metric storage: 16 bytes of padding after every 256 bytes, so that the
-// predecessor metrics read by consecutive lanes (consecutive groups) fall on
-// different LDS banks.
-__device__ __forceinline__ uint32_t pad(uint32_t m) { return m + ((m >> 5) << 1); }
-
 template <int KV>
 struct Tcq {
     static constexpr uint32_t M = 16 - KV;             // memory bits
@@ -77,14 +75,53 @@ struct Tcq {
     static constexpr uint32_t NT = KV >= 5 ? 512 : kMaxThreads;
     static constexpr uint32_t IPT = S / NT;            // next memories per thread
     static constexpr uint32_t TPG = BR / IPT;          // threads per group
-    static constexpr uint32_t SP = S + (S >> 4);       // padded metric array length
-    // copies of each branch cost, lane l reading copy l mod CC: lanes reading
-    // different copies never meet on an LDS bank. Measured with paired loads
-    // and 1,024 threads on the d512 batch (ms for 4,096 rows with 1 / 2 / 4
-    // copies): kv 4: 32.5 / 31.3 / 31.4; kv 5: 33.3 / 30.7 / 33.3; before
-    // pairing, kv 6: 37.1 / 37.5 / 55.7; kv 3 has no LDS left for a second
-    // copy.
+    // Path-metric storage. A thread reads the BR metrics (L << kv) | r of
+    // its group L, consecutive lanes taking consecutive groups. At kv >= 4
+    // each run of BR metrics is followed by two doubles of padding: a lane's
+    // run then starts BR/2 + 1 (odd) 16-byte units after its neighbour's, so
+    // 16 lanes' 16-byte loads of metric pairs fall on 16 different bank
+    // groups. At kv 3 the LDS has room for one double per 16 metrics only.
+    static constexpr uint32_t PAD_SHIFT = KV == 3 ? 4 : KV;
+    static constexpr uint32_t PAD_UNITS = KV == 3 ? 1 : 2;
+    static constexpr uint32_t SP = S + (S >> PAD_SHIFT) * PAD_UNITS;  // padded metric array length
+    static __device__ __forceinline__ uint32_t pad(uint32_t m) { return m + (m >> PAD_SHIFT) * PAD_UNITS; }
+    // When the padding period divides 2^(M - kv), the padded position of
+    // next memory L | u << (M - kv) is pad(L) + u * USTRIDE: one register
+    // per thread and a constant per successor.
+    static constexpr bool LINEAR_NEXT = PAD_SHIFT <= M - KV;
+    // Steps unrolled by two: at kv 6 the 64 gather addresses that this
+    // hoists out of the step loop do not fit in the registers.
+    static constexpr bool PARITY_UNROLL = KV <= 5;
+    // The running best as a min (one instruction instead of two selects);
+    // at kv 6 the compiler then runs out of registers.
+    static constexpr bool MIN_SELECT = KV <= 5;
+    static constexpr uint32_t USTRIDE = LINEAR_NEXT ? (1u << (M - KV)) + (1u << (M - KV - PAD_SHIFT)) * PAD_UNITS : 0;
+    // Copies of each branch cost. Copy c of the pair with key k sits at the
+    // 16-byte unit unit(k, c), in bank group unit mod 16 (64 banks of 4
+    // bytes). The LDS serves a wave's 16-byte loads in four cycles of 16
+    // lanes (lanes sharing l >> 5 and the parity of bits 2..4 of l), one
+    // more cycle for every further unit in a bank group. Each thread reads,
+    // for each of its gathers, the copy that a fixed table (kEncodeCopies4
+    // and 5, generated offline by a bipartite matching per 16 such lanes:
+    // the keys a thread gathers depend only on the thread) assigns it: 1.19
+    // cycles per 16 lanes at kv 4 where one fixed copy per lane (copy = lane
+    // mod CC, copies side by side) takes 1.88; 1.75 where 1.88 at kv 5. kv 3
+    // has no LDS left for a second copy, kv 6 no registers.
     static constexpr uint32_t CC = KV == 4 ? 4 : KV == 5 ? 2 : 1;
+    static constexpr uint32_t CBITS = CC == 4 ? 2 : CC == 2 ? 1 : 0;  // bits per table entry
+    static __device__ __forceinline__ uint32_t unit(uint32_t k, uint32_t c)
+    {
+        // four copies in the bank groups k .. k + 3; else side by side
+        if constexpr (CC == 4) return 16u * (CC * (k >> 4) + c) + ((k + c) & 15u);
+        else return CC * k + c;
+    }
+    // this thread's copy choices, CBITS bits per gather q = r * H + j
+    static __device__ __forceinline__ uint64_t copies(uint32_t tid)
+    {
+        if constexpr (KV == 4) return kEncodeCopies4[tid];
+        else if constexpr (KV == 5) return kEncodeCopies5[tid];
+        else return 0;
+    }
     // The windows s and s ^ 0x8000 hash to idx and idx ^ 256 (adding 2^15 to
     // s flips bit 15 of s*s + s and changes only higher bits otherwise) and
     // carry opposite signs, so both branch costs share the key
@@ -103,10 +140,12 @@ struct Tcq {
 
 template <int KV>
 struct Shared {
-    double D[2][Tcq<KV>::SP];
-    // branch costs of one step, entry ((idx ^ negated << 8) * CC + copy) * 2
-    // + negated
+    // branch costs of one step: copy c of the pair with key
+    // k = idx ^ negated << 8 at doubles 2 unit(k, c) + negated. First in LDS: the gathers address both buffers from one
+    // per-thread register, with the buffer's offset (below 64 KB) in the
+    // instruction.
     alignas(16) double cost[2][1024 * Tcq<KV>::CC];
+    alignas(16) double D[2][Tcq<KV>::SP];
     double z[512];
     uint32_t lut[512];
     uint8_t code[6 * 512 / 16 + 2];
@@ -117,8 +156,8 @@ struct Shared {
 };
 
 // cost of the pair g = +-LUT[idx]: (z0 - g0)^2 + (z1 - g1)^2, for every copy
-// c, at ((idx ^ neg << 8) * CC + c) * 2 + neg; i = 2 idx + neg.
-template <uint32_t CC>
+// c, at 2 unit(idx ^ neg << 8, c) + neg; i = 2 idx + neg.
+template <int KV>
 __device__ __forceinline__ void fill_cost(double *cost, const uint32_t *lut, double z0, double z1, uint32_t i)
 {
     const uint32_t e = lut[i >> 1];
@@ -131,15 +170,19 @@ __device__ __forceinline__ void fill_cost(double *cost, const uint32_t *lut, dou
     const double c = e0 * e0 + e1 * e1;
     const uint32_t key = (i >> 1) ^ ((i & 1u) << 8);
 #pragma unroll
-    for (uint32_t k = 0; k < CC; ++k) cost[(key * CC + k) * 2 + (i & 1u)] = c;
+    for (uint32_t k = 0; k < Tcq<KV>::CC; ++k) cost[Tcq<KV>::unit(key, k) * 2 + (i & 1u)] = c;
 }
 
-template <uint32_t CC, uint32_t NT>
+template <int KV>
 __device__ __forceinline__ void fill_costs(double *cost, const uint32_t *lut, double z0, double z1)
 {
+    // at kv 5 the entry addresses are recomputed every step (a few integer
+    // operations): kept in registers across the step loop they spill
+    uint32_t i0 = threadIdx.x;
+    if constexpr (KV == 5) asm volatile("" : "+v"(i0));
 #pragma unroll
-    for (uint32_t i = threadIdx.x; i < 1024; i += NT)
-        fill_cost<CC>(cost, lut, z0, z1, i);
+    for (uint32_t i = i0; i < 1024; i += Tcq<KV>::NT)
+        fill_cost<KV>(cost, lut, z0, z1, i);
 }
 
 // One store of a thread's IPT back-pointers (consecutive bytes).
@@ -184,7 +227,7 @@ typedef double dbl2 __attribute__((ext_vector_type(2)));
 // group L, into cv[i] for successor succ(tq, i).
 template <int KV>
 __device__ __forceinline__ void load_costs(double *cv, const double *cst, uint32_t L, uint32_t tq, uint32_t r,
-                                           uint32_t cpy)
+                                           uint64_t copies)
 {
     using P = Tcq<KV>;
     const dbl2 *c2 = reinterpret_cast<const dbl2 *>(cst);
@@ -193,7 +236,9 @@ __device__ __forceinline__ void load_costs(double *cv, const double *cst, uint32
         const uint32_t u = P::succ(tq, j);  // below BR/2: sign bit clear
         const uint32_t s = (L << KV) | (u << P::M) | r;
         const uint32_t h = s * s + s;
-        const dbl2 c = c2[((h >> 7) & 511u) * P::CC + cpy];
+        const uint32_t q = r * P::H + j;
+        const uint32_t cp = (uint32_t)(copies >> (P::CBITS * q)) & (P::CC - 1);
+        const dbl2 c = c2[P::unit((h >> 7) & 511u, cp)];
         cv[j] = c.x;
         cv[j + P::H] = c.y;
     }
@@ -208,16 +253,23 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
     using P = Tcq<KV>;
     const uint32_t tid = threadIdx.x;
     const uint32_t L = tid % P::G, tq = tid / P::G;
-    const uint32_t cpy = tid & (P::CC - 1);
+    const uint64_t cpy = P::copies(tid);
     for (uint32_t m = tid; m < P::S; m += P::NT)
-        sh.D[0][pad(m)] = (start < 0 || (int32_t)m == start) ? 0.0 : __builtin_inf();
-    fill_costs<P::CC, P::NT>(sh.cost[0], sh.lut, sh.z[2 * (rot % T)], sh.z[2 * (rot % T) + 1]);
+        sh.D[0][P::pad(m)] = (start < 0 || (int32_t)m == start) ? 0.0 : __builtin_inf();
+    fill_costs<KV>(sh.cost[0], sh.lut, sh.z[2 * (rot % T)], sh.z[2 * (rot % T) + 1]);
     __syncthreads();
-    int cur = 0;
-    for (uint32_t k = 0; k < T; ++k) {
-        const double *Dc = sh.D[cur];
-        double *Dn = sh.D[cur ^ 1];
-        const double *cst = sh.cost[k & 1];
+    // this thread's first metric read and first metric write (next memory
+    // L | succ(tq, 0) << (M - kv), the others at constant distances)
+    const double *rp = &sh.D[0][P::pad(L << KV)];
+    double *wp = &sh.D[0][P::LINEAR_NEXT ? P::pad(L) + tq * P::H * P::USTRIDE : 0u];
+    // One step. Step k reads metric and cost buffer k & 1 and writes buffer
+    // (k & 1) ^ 1. Unrolled by two (the parity a constant), every LDS address
+    // is a per-thread register plus an immediate offset.
+    auto step = [&](uint32_t k, auto parity) {
+        const int B = (int)parity;
+        const double *Dc = sh.D[B];
+        double *Dn = sh.D[B ^ 1];
+        const double *cst = sh.cost[B];
         double best[P::IPT];
         uint32_t br[P::IPT];
 #pragma unroll
@@ -226,38 +278,66 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
             br[i] = 0;
         }
         // software-pipelined: the branch costs of predecessor r + 1 are
-        // requested before the add-compare-selects of predecessor r
+        // requested before the add-compare-selects of predecessor r. The
+        // back-pointer moves to r only on a strictly smaller candidate, so
+        // ties keep the smallest r; the metric is the same either way.
         double cv[2][P::IPT];
+        const double *dr = rp + B * P::SP;
+        dbl2 dv2 = {0.0, 0.0};
         load_costs<KV>(cv[0], cst, L, tq, 0, cpy);
 #pragma unroll
         for (uint32_t r = 0; r < P::BR; ++r) {
             if (r + 1 < P::BR) load_costs<KV>(cv[(r + 1) & 1], cst, L, tq, r + 1, cpy);
-            const double dv = Dc[pad((L << KV) | r)];
+            double dv;
+            if constexpr (KV >= 4) {
+                // the run of BR metrics is contiguous and 16-byte aligned
+                if (r % 2 == 0) dv2 = reinterpret_cast<const dbl2 *>(dr)[r / 2];
+                dv = (r & 1u) ? dv2.y : dv2.x;
+            } else {
+                dv = dr[r];
+            }
 #pragma unroll
             for (uint32_t i = 0; i < P::IPT; ++i) {
                 const double v = dv + cv[r & 1][i];
-                if (v < best[i]) {
+                if constexpr (P::MIN_SELECT) {
+                    br[i] = v < best[i] ? r : br[i];
+                    best[i] = __builtin_fmin(best[i], v);
+                } else if (v < best[i]) {
                     best[i] = v;
                     br[i] = r;
                 }
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, P::H + 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6 * P::IPT, 0);
+            if (KV < 4 || r % 2 == 0)
+                __builtin_amdgcn_sched_group_barrier(0x100, P::H + 1, 0);
+            else
+                __builtin_amdgcn_sched_group_barrier(0x100, P::H, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4 * P::IPT, 0);
         }
 #pragma unroll
         for (uint32_t i = 0; i < P::IPT; ++i) {
-            const uint32_t u = P::succ(tq, i);
-            Dn[pad(L | (u << (P::M - KV)))] = best[i];
+            if constexpr (P::LINEAR_NEXT) {
+                wp[(B ^ 1) * P::SP + P::succ(0, i) * P::USTRIDE] = best[i];
+            } else {
+                const uint32_t u = P::succ(tq, i);
+                Dn[P::pad(L | (u << (P::M - KV)))] = best[i];
+            }
         }
         store_bp<P::IPT>(bp + (uint64_t)k * P::S + tid * P::IPT, br);
         if (k + 1 < T) {
             const uint32_t t1 = (k + 1 + rot) % T;
-            fill_costs<P::CC, P::NT>(sh.cost[(k + 1) & 1], sh.lut, sh.z[2 * t1], sh.z[2 * t1 + 1]);
+            fill_costs<KV>(sh.cost[B ^ 1], sh.lut, sh.z[2 * t1], sh.z[2 * t1 + 1]);
         }
         __syncthreads();
-        cur ^= 1;
+    };
+    if constexpr (P::PARITY_UNROLL) {
+        for (uint32_t k = 0; k < T; k += 2) {
+            step(k, std::integral_constant<int, 0>{});
+            if (k + 1 < T) step(k + 1, std::integral_constant<int, 1>{});
+        }
+    } else {
+        for (uint32_t k = 0; k < T; ++k) step(k, (int)(k & 1u));
     }
-    return cur;
+    return (int)(T & 1u);
 }
 
 // Smallest metric over all memories, the smallest memory on ties.
@@ -269,7 +349,7 @@ __device__ __forceinline__ uint32_t argmin_memory(Shared<KV> &sh, const double *
     double bv = __builtin_inf();
     uint32_t bi = 0xFFFFFFFFu;
     for (uint32_t m = tid; m < P::S; m += P::NT) {
-        const double v = D[pad(m)];
+        const double v = D[P::pad(m)];
         if (v < bv || (v == bv && m < bi)) {
             bv = v;
             bi = m;
