@@ -47,6 +47,18 @@ int cpp_store_rows(uint16_t *out, uint64_t n, uint32_t d, uint32_t chunk, void *
 int cpp_gather_records(const void *records, uint64_t record_bytes, const int64_t *ids, uint64_t n,
                        uint32_t *sink, void *stream);
 
+/* Which lanes of a wave the LDS serves in the same cycle: one workgroup of
+ * one wave in which only lanes `lane_a` and `lane_b` (0..63, distinct) access
+ * LDS, `iters` times each, at addresses 256 bytes apart (the same banks of a
+ * 64-bank LDS); `width` bytes per access (4, 8 or 16), loads when `write` is
+ * 0, stores otherwise. Under rocprofv3 the dispatch counts bank-conflict
+ * cycles (SQ_LDS_BANK_CONFLICT) exactly when the two lanes share a cycle.
+ * The encoder's choice of branch-cost copies rests on this grouping for
+ * 16-byte loads. `sink`: 4 bytes of device memory, written only in the
+ * unlikely case that the data's XOR takes one fixed value. */
+int cpp_lds_pair(uint32_t width, uint32_t write, uint32_t lane_a, uint32_t lane_b, uint32_t iters, uint32_t *sink,
+                 void *stream);
+
 #ifdef __cplusplus
 }
 #endif

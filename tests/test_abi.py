@@ -36,10 +36,18 @@ def test_every_declared_symbol_is_exported():
 def test_probe_library_exports_its_header():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(cpbuild.ROOT, "include", "cp_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(cpp_\w+)\s*\(", text)))
-    assert names == ["cpp_gather_records", "cpp_read_stream", "cpp_store_rows"]
+    assert names == ["cpp_gather_records", "cpp_lds_pair", "cpp_read_stream", "cpp_store_rows"]
     lib = ctypes.CDLL(cpbuild.PROBE_LIB)
     for name in names:
         assert hasattr(lib, name), name
+    # argument checks come before any HIP call: hipErrorInvalidValue (1)
+    f = lib.cpp_lds_pair
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_uint32] * 5 + [ctypes.c_void_p] * 2
+    sink = ctypes.c_uint32(0)
+    assert f(16, 0, 3, 3, 1, ctypes.addressof(sink), None) == 1   # the same lane twice
+    assert f(16, 0, 3, 64, 1, ctypes.addressof(sink), None) == 1  # lane 64 of a 64-lane wave
+    assert f(16, 0, 3, 4, 1, None, None) == 1                     # no sink
 
 
 def test_record_bytes_and_supported_shapes():

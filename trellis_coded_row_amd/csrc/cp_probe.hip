@@ -1,7 +1,8 @@
 // cp_probe.hip - measurement probes (include/cp_probe.h): a streaming read,
-// the lookup's output stream alone, the lookup's record fetch alone. They
-// give the floors the gather-decode kernel is compared against; none is on
-// the lookup path.
+// the lookup's output stream alone, the lookup's record fetch alone, and a
+// two-lane LDS access that shows which lanes the LDS serves together. They
+// give the floors and the hardware facts the kernels are designed against;
+// none is on the lookup path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -103,9 +104,64 @@ hipError_t launch_store(uint16_t *out, uint64_t n, uint32_t chunk, hipStream_t s
     return hipGetLastError();
 }
 
+// Two lanes of one wave touch LDS addresses 256 bytes apart (the same banks
+// on a 64-bank LDS) `iters` times, every other lane idle: the accesses
+// collide, and so count bank-conflict cycles, only if the LDS serves the
+// two lanes in the same cycle. W: bytes per access (4, 8, 16).
+template <int W, bool WRITE>
+__global__ __launch_bounds__(64) void lds_pair(uint32_t a, uint32_t b, uint32_t iters, uint32_t *__restrict__ sink)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t lds[256];
+    for (uint32_t i = threadIdx.x; i < 256; i += 64) lds[i] = i;
+    __syncthreads();
+    const uint32_t l = threadIdx.x;
+    uint32_t acc = 0;
+    if (l == a || l == b) {
+        uint32_t off = l == a ? 0u : 64u;  // dwords
+        for (uint32_t it = 0; it < iters; ++it) {
+            uint32_t *p = lds + (off & 127u);
+            if constexpr (WRITE) {
+                if constexpr (W == 4) *p = it;
+                else if constexpr (W == 8) *reinterpret_cast<uint64_t *>(p) = it;
+                else *reinterpret_cast<u32x4 *>(p) = (u32x4){it, l, it, l};
+            } else {
+                if constexpr (W == 4) acc ^= *p;
+                else if constexpr (W == 8) acc ^= (uint32_t)*reinterpret_cast<const uint64_t *>(p);
+                else { const u32x4 v = *reinterpret_cast<const u32x4 *>(p); acc ^= v.x ^ v.w; }
+            }
+            asm volatile("" : "+v"(off));
+        }
+    }
+    // what the stores left is read back, so they are not dropped
+    __syncthreads();
+    acc ^= lds[l];  // one bank per lane: no conflict of its own
+    if (acc == kSinkMagic) *sink = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+int cpp_lds_pair(uint32_t width, uint32_t write, uint32_t lane_a, uint32_t lane_b, uint32_t iters, uint32_t *sink,
+                 void *stream)
+{
+    if (!sink || lane_a >= 64 || lane_b >= 64 || lane_a == lane_b) return (int)hipErrorInvalidValue;
+    (void)hipGetLastError();
+    const hipStream_t s = (hipStream_t)stream;
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(1), dim3(64), 0, s, lane_a, lane_b, iters, sink);
+        return (int)hipGetLastError();
+    };
+    switch (width * 2 + (write ? 1 : 0)) {
+    case 8: return go(lds_pair<4, false>);
+    case 9: return go(lds_pair<4, true>);
+    case 16: return go(lds_pair<8, false>);
+    case 17: return go(lds_pair<8, true>);
+    case 32: return go(lds_pair<16, false>);
+    case 33: return go(lds_pair<16, true>);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
 
 int cpp_read_stream(const void *src, uint64_t bytes, uint32_t *sink, void *stream)
 {
