@@ -95,6 +95,12 @@ struct Tcq {
     // The running best as a min (one instruction instead of two selects);
     // at kv 6 the compiler then runs out of registers.
     static constexpr bool MIN_SELECT = KV <= 5;
+    // VALU instructions the scheduler places after each predecessor's cost
+    // loads (a branch is four); measured on 4,096 rows of d = 512, ms with
+    // 4 / 5 / 6 / 8 / 12 x IPT: kv 3: 30.9 / 31.1 / 31.1 / 31.3 / 31.2;
+    // kv 4: 24.2 / 23.2 / 22.4 / 23.2 / 23.1; kv 5: 21.5 / 21.3 / 21.3 /
+    // 21.5 / 21.5; kv 6: 26.5 / 26.6 / 26.8 / 26.6 / 26.1.
+    static constexpr uint32_t SCHED_VALU = (KV == 4 || KV == 5 ? 6 : KV == 6 ? 12 : 4) * IPT;
     static constexpr uint32_t USTRIDE = LINEAR_NEXT ? (1u << (M - KV)) + (1u << (M - KV - PAD_SHIFT)) * PAD_UNITS : 0;
     // Copies of each branch cost. Copy c of the pair with key k sits at the
     // 16-byte unit unit(k, c), in bank group unit mod 16 (64 banks of 4
@@ -267,8 +273,7 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
     // is a per-thread register plus an immediate offset.
     auto step = [&](uint32_t k, auto parity) {
         const int B = (int)parity;
-        const double *Dc = sh.D[B];
-        double *Dn = sh.D[B ^ 1];
+        double *Dn = sh.D[B ^ 1];  // the next metrics when their positions are not linear (kv 6)
         const double *cst = sh.cost[B];
         double best[P::IPT];
         uint32_t br[P::IPT];
@@ -311,7 +316,7 @@ __device__ __forceinline__ int viterbi_pass(Shared<KV> &sh, uint32_t T, int32_t 
                 __builtin_amdgcn_sched_group_barrier(0x100, P::H + 1, 0);
             else
                 __builtin_amdgcn_sched_group_barrier(0x100, P::H, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4 * P::IPT, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, P::SCHED_VALU, 0);
         }
 #pragma unroll
         for (uint32_t i = 0; i < P::IPT; ++i) {
