@@ -759,11 +759,16 @@ def main() -> int:
             # The GPU-encoded rows against the oracle's own encoding of the same
             # Gaussian rows, and their lookup against the oracle decoding its
             # own records (nothing the GPU produced goes into the oracle). The
-            # check ids: the first 4,096 replay ids when every row is encoded,
-            # else ids 0..4095; the replay sample above decodes the random-code
-            # records, which time the same as encoded ones.
-            chk_ids = ids_np[:4096] if cfg.encoded == "all" else np.arange(min(4096, cfg.encoded_rows),
-                                                                             dtype=np.int64)
+            # check ids: when every row is encoded, the first 4,096 replay ids
+            # (the hot rows) and 4,096 rows drawn uniformly over the table with
+            # a fixed seed; else ids 0..4095. The replay sample above decodes
+            # the random-code records, which time the same as encoded ones.
+            if cfg.encoded == "all":
+                spread = np.random.default_rng(cfg.rows_seed + 1).choice(cfg.rows, size=min(4096, cfg.rows),
+                                                                          replace=False).astype(np.int64)
+                chk_ids = np.concatenate([ids_np[:4096], spread])
+            else:
+                chk_ids = np.arange(min(4096, cfg.encoded_rows), dtype=np.int64)
             chk_rows = np.unique(chk_ids)
             t = time.perf_counter()
             own, _ = oracle.encode_rows(workload.table_rows(cfg.rows, cfg.d, cfg.rows_seed, chk_rows), cfg.d,
@@ -777,6 +782,8 @@ def main() -> int:
             got_chk = table.lookup_decode(torch.from_numpy(chk_ids).cuda()).view(torch.int16).cpu().numpy()
             res["cpu_baseline"]["encoder_check"] = {
                 "rows": int(chk_rows.size),
+                "sample": ("the first 4,096 replay ids' rows and 4,096 rows drawn uniformly (seeded)"
+                           if cfg.encoded == "all" else f"rows 0..{chk_ids.size - 1}"),
                 "gpu_records_matching_oracle_encoding": int((gpu_recs == own).all(axis=1).sum()),
                 "gpu_rows_matching_oracle_decode": int((got_chk.view(np.uint16) == exp_chk).all(axis=1).sum()),
                 "lookups_checked": int(chk_ids.size),
