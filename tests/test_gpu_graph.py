@@ -79,6 +79,25 @@ def test_lookup_replayed_from_a_graph(d, kv):
         t.close()
 
 
+def test_touch_ahead_lookup_replayed_from_a_graph():
+    # a batch large enough for several residency rounds, so that the first
+    # round touches the later rounds' records on every replay
+    d, kv, rows = 512, 4, 50_021
+    recs = workload.random_records(rows, d, kv, seed=1250)
+    t = make_table(LUT, recs, d, kv, flags=cp.CP_FLAG_TOUCH_AHEAD)
+    try:
+        n = shape_change_sizes()[5] * 3 + 11
+        ids_np = workload.zipf_ids(rows, n, seed=1251)
+        ids = torch.from_numpy(ids_np).cuda()
+        exp, bad = oracle.lookup_decode(LUT, recs, rows, d, kv, ids_np)
+        assert bad == 0
+        out = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+        replay_and_compare(lambda: t.lookup_decode(ids, out), out, exp, f"touch-ahead n{n}")
+        assert t.check()
+    finally:
+        t.close()
+
+
 def test_bad_ids_in_a_graph_raise_the_flag_on_every_replay():
     d, kv, rows = 512, 4, 300
     recs = workload.random_records(rows, d, kv, seed=1300)

@@ -1,7 +1,7 @@
 """Seeded random sweep of the HIP lookup against the CPU oracle: table shape
 (d, kv), table size, batch size (every launch shape), id distribution with
-out-of-range ids sprinkled in, residency, and entry point (raw, scaled,
-dedup), plus mixed-rate tables. Each case runs twice, so a result that
+out-of-range ids sprinkled in, residency, touch-ahead tables, and entry
+point (raw, scaled, dedup), plus mixed-rate tables. Each case runs twice, so a result that
 changed from one launch to the next would fail as well as a wrong one."""
 from __future__ import annotations
 
@@ -57,9 +57,13 @@ def test_random_single_rate(case):
     host = bool(rng.random() < 0.25)
     recs = workload.random_records(rows, d, kv, seed=int(rng.integers(1 << 30)))
     ids = draw_ids(rng, rows, n)
-    label = f"case {case}: d{d} kv{kv} rows {rows} n {n} {'host' if host else 'hbm'}"
+    # every third device table touches ahead (CP_FLAG_TOUCH_AHEAD); decided by
+    # the case number, so the drawn parameters stay as they were
+    ahead = not host and case % 3 == 1
+    label = f"case {case}: d{d} kv{kv} rows {rows} n {n} {'host' if host else 'hbm'}{' touch-ahead' if ahead else ''}"
     say(label)
-    t = make_table(LUT, recs, d, kv, residency=cp.CP_RESIDENCY_HOST_MAPPED if host else cp.CP_RESIDENCY_DEVICE)
+    t = make_table(LUT, recs, d, kv, residency=cp.CP_RESIDENCY_HOST_MAPPED if host else cp.CP_RESIDENCY_DEVICE,
+                   flags=cp.CP_FLAG_TOUCH_AHEAD if ahead else 0)
     try:
         exp_raw, nbad = oracle.lookup_decode(LUT, recs, rows, d, kv, ids, raw=True)
         exp, _ = oracle.lookup_decode(LUT, recs, rows, d, kv, ids)
