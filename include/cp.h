@@ -265,8 +265,9 @@ cp_status cp_table_download(const cp_table *table, uint64_t first_row, uint64_t 
 /* Device workspace bytes that cp_table_encode needs for nrows rows on this
  * table (0 for a NULL table or nrows == 0): one byte per trellis memory and
  * step, (d / 2) * 2^(16 - kv) bytes, for each row encoded concurrently (at
- * most one per resident 1024-thread workgroup), 1 MB per concurrent row at
- * d = 512, kv = 4; for a mixed-rate table the largest such need of its
+ * most one per resident workgroup: one per compute unit at kv 3 and 4, two
+ * at kv 5 and 6), 1 MB per concurrent row at d = 512, kv = 4; for a
+ * mixed-rate table the largest such need of its
  * rates plus, per row, 12 bytes of row lists, a staged copy of the input row
  * (4d bytes) and a staged record. */
 uint64_t cp_encode_workspace_bytes(const cp_table *table, uint64_t nrows);
