@@ -729,8 +729,15 @@ def main() -> int:
         decode(ids_np[:cal])
         per_row = (time.perf_counter() - t) / cal
         sample = int(min(n, max(cal, args.cpu_seconds / max(per_row, 1e-9))))
+        # when the whole replay takes less than the target time, it is decoded
+        # again (the same work each pass) until the target is reached, so the
+        # rate rests on seconds of CPU work rather than a fraction of one
         t = time.perf_counter()
         exp, _ = decode(ids_np[:sample])
+        passes = 1
+        while sample == n and time.perf_counter() - t < args.cpu_seconds and passes < 1000:
+            decode(ids_np)
+            passes += 1
         cpu_s = time.perf_counter() - t
         got = out[:sample].view(torch.int16).cpu().numpy().view(np.uint16)
         # lookups of rows the GPU encoded are checked in encoder_check below
@@ -738,12 +745,12 @@ def main() -> int:
         if encoded:
             plain = ids_np[:sample] >= cfg.encoded_rows if cfg.encoded == "first" else np.zeros(sample, dtype=bool)
         res["cpu_baseline"] = {
-            "value": sample / cpu_s,
+            "value": sample * passes / cpu_s,
             "unit": "rows/s",
             "cores": threads,
             "kind": "oracle",
-            "sample": f"first {sample:,} of the {n:,} replay ids ({cpu_s:.1f} s, {threads} threads, "
-                      f"plain C oracle, bit-by-bit trellis walk, fp64 scaling)",
+            "sample": (f"first {sample:,} of the {n:,} replay ids" + (f", decoded {passes} times" if passes > 1 else "")
+                       + f" ({cpu_s:.1f} s, {threads} threads, plain C oracle, bit-by-bit trellis walk, fp64 scaling)"),
             "gpu_rows_matching_oracle": f"{int((got[plain] == exp[plain]).all(axis=1).sum())} of {int(plain.sum())}"
                                         + (" (rows with random codes; encoded rows: encoder_check)" if encoded else ""),
         }
