@@ -155,6 +155,27 @@ def graph_timing(step, out, steps: int, torch, per_graph: int = 16) -> dict:
             "replays_matching_eager": f"{same}/{checks}"}
 
 
+def graph_call_ms(fn, steps: int, torch, per_graph: int = 16) -> float:
+    """ms per call of fn() when `per_graph` calls are captured in one HIP
+    graph and the graph is replayed."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    reps = max(2, steps // per_graph)
+    for _ in range(2):
+        g.replay()
+    ms = time_region(g.replay, reps, torch)
+    del g
+    return ms / (reps * per_graph)
+
+
 def batch_scan(table, ids_np, d: int, bytes_per_lookup: float, torch, np) -> dict:
     """ms per launch for batches of growing size (the replay's ids tiled),
     launched one by one and replayed from a captured graph (device time
@@ -366,6 +387,159 @@ def bench_encode(args, np, torch, cp, workload) -> int:
     return 0
 
 
+def bench_sharded(args, np, torch, cp, workload) -> int:
+    """One GPU's share of a lookup into a table split by rows over G GPUs
+    (--sharded G): this GPU holds the 12.7 GB d512 table as shard 0 of G x
+    97,690,000 rows and runs, for the 393,216-lookup replay drawn over the
+    whole sharded table, the three steps that are its own: the plan
+    (cp_shard_plan), the owner's record gather (cp_table_gather_records) and
+    the decode of the received records (cp_lookup_decode_staged). With the
+    ids spread evenly over the shards, an owner serves as many lookups as a
+    requester makes, so the gather here copies the records of all the
+    replay's local ids from this GPU's table, standing in for the requests
+    of all G requesters. The two exchanges between them are not timed (one
+    GPU); their bytes are reported."""
+    G = args.sharded
+    cfg = workload.CONFIGS["gpu_d512"]
+    lut = workload.lut_fp16(0)
+    rps, d, kv, R = cfg.rows, cfg.d, cfg.kv, cfg.R
+    t_gen = time.time()
+    records = workload.random_records(rps, d, kv, cfg.table_seed)
+    ids_np = workload.zipf_ids(G * rps, cfg.n_ids, cfg.ids_seed)
+    gen_s = time.time() - t_gen
+    table = cp.Table(rps, d, kv, lut)
+    for r0 in range(0, rps, 1 << 22):
+        table.upload(records[r0:r0 + (1 << 22)], first_row=r0)
+    n = ids_np.size
+    ids = torch.from_numpy(ids_np).cuda()
+    local_ids = torch.empty(n, dtype=torch.int64, device="cuda")
+    positions = torch.empty(n, dtype=torch.int64, device="cuda")
+    counts = torch.empty(G, dtype=torch.int64, device="cuda")
+    ws_bytes = cp.cp_shard_plan_workspace_bytes(n, G)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    recv = torch.zeros(n * R + 64, dtype=torch.uint8, device="cuda")
+    out = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+
+    def plan():
+        st = cp.cp_shard_plan(ids.data_ptr(), n, rps, G, local_ids.data_ptr(), positions.data_ptr(),
+                              counts.data_ptr(), ws.data_ptr(), ws_bytes, torch.cuda.current_stream().cuda_stream)
+        if st != cp.CP_OK:
+            raise cp.CPError(st, "cp_shard_plan")
+
+    def gather():
+        st = cp.cp_table_gather_records(table.handle, local_ids.data_ptr(), n, recv.data_ptr(),
+                                        torch.cuda.current_stream().cuda_stream)
+        if st != cp.CP_OK:
+            raise cp.CPError(st, "cp_table_gather_records")
+
+    def decode():
+        st = cp.cp_lookup_decode_staged(table.handle, recv.data_ptr(), n, positions.data_ptr(), n, out.data_ptr(),
+                                        torch.cuda.current_stream().cuda_stream)
+        if st != cp.CP_OK:
+            raise cp.CPError(st, "cp_lookup_decode_staged")
+
+    def step():
+        plan()
+        gather()
+        decode()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    per_shard = counts.cpu().numpy()
+    if int(per_shard.sum()) != n or not table.check():
+        print("an id was owned by no shard", file=sys.stderr)
+        return 1
+    # the staged rows against the direct lookup of the same records on this
+    # GPU's table (id - owner * rows_per_shard)
+    direct = table.lookup_decode(torch.from_numpy(ids_np % rps).cuda())
+    torch.cuda.synchronize()
+    same_as_direct = torch.equal(direct.view(torch.int16), out.view(torch.int16))
+    wall0 = time.perf_counter()
+    total_ms = time_region(step, args.steps, torch)
+    wall_s = time.perf_counter() - wall0
+    ms = total_ms / args.steps
+    stages = (("plan", plan), ("gather", gather), ("decode", decode))
+    stage_eager_ms = {name: time_region(fn, args.steps, torch) / args.steps for name, fn in stages}
+    # device time per call without the host's launch cost: 16 calls captured
+    # in one graph, the graph replayed
+    stage_ms = {name: graph_call_ms(fn, args.steps, torch) for name, fn in stages}
+    step_graph_ms = graph_call_ms(step, args.steps, torch)
+    torch.cuda.synchronize()
+    same_as_direct = same_as_direct and torch.equal(direct.view(torch.int16), out.view(torch.int16))
+    del direct
+    # algorithmic bytes of each step: plan reads the ids twice (count, then
+    # place) and writes local ids and positions; the gather reads local ids
+    # and records and writes records; the decode reads positions and records
+    # and writes the rows
+    algo = {"plan": 8 * n * 2 + 16 * n, "gather": 8 * n + 2 * R * n, "decode": 8 * n + R * n + 2 * d * n}
+    gbps = {k: algo[k] / (stage_ms[k] / 1e3) / 1e9 for k in algo}
+    remote = n * (G - 1) / G
+    res = {
+        "metric": "decoded rows/s per GPU, row-sharded table (this GPU's plan, owner gather and staged decode)",
+        "value": n / (ms / 1e3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"sharded_d512_g{G}: {n:,} lookups (zipf ids) into a {G} x {rps:,}-row d512 table split "
+                         f"by rows; this GPU holds one {cfg.table_bytes / 1e9:.2f} GB shard ({R}-byte records) "
+                         "and runs the plan, the owner's record gather and the staged decode"),
+            "shards": G, "rows_per_shard": rps, "d": d, "bits_per_step": kv, "record_bytes": R, "lookups": n,
+            "ids_sha256_16": workload.ids_digest(ids_np),
+            "entry_points": ["cp_shard_plan", "cp_table_gather_records", "cp_lookup_decode_staged"],
+        },
+        "stage_ms": stage_ms,
+        "stage_ms_note": "device time per call: 16 calls captured in a HIP graph, the graph replayed",
+        "stage_ms_eager": stage_eager_ms,
+        "step_ms_graph": step_graph_ms,
+        "stage_effective_GBps": gbps,
+        "lookups_per_shard": [int(c) for c in per_shard],
+        "rows_identical_to_direct_lookup": bool(same_as_direct),
+        "rows_identical_note": "after the eager steps and again after the graph replays, every row equal to "
+                               "cp_lookup_decode of id - owner * rows_per_shard on this GPU's table",
+        "exchange_bytes_per_gpu_not_timed": {
+            "ids_sent": int(8 * remote), "records_received": int(R * remote),
+            "decoded_rows_instead": int(2 * d * remote),
+            "note": "per step with the ids spread evenly over the shards: ids to their owners and records back "
+                    "(an all-to-all each way); shipping decoded rows would move 2d bytes per lookup instead of R",
+        },
+        "wall_s_timed_region": wall_s,
+        "setup_s": {"generate": round(gen_s, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbps["decode"],
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gbps["decode"] / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": algo["decode"],
+            "kernel": f"gather_decode<{d},{kv}> (staged)",
+            "step_effective_GBps": sum(algo.values()) / (ms / 1e3) / 1e9,
+        },
+    }
+    if not same_as_direct:
+        print("the staged rows differ from the direct lookup's", file=sys.stderr)
+        return 1
+    if not args.no_cpu_baseline:
+        import oracle  # CPU check of a sample only
+
+        k = min(n, 4096)
+        exp, _ = oracle.lookup_decode(lut, records, rps, d, kv, ids_np[:k] % rps)
+        got = out[:k].view(torch.int16).cpu().numpy().view(np.uint16)
+        res["oracle_check"] = f"{int((got == exp).all(axis=1).sum())} of the first {k} lookups' rows equal the oracle's"
+    table.close()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -398,6 +572,9 @@ def main() -> int:
                     help="also time lookups replayed from a captured HIP graph (no host launch cost per lookup)")
     ap.add_argument("--batch-scan", action="store_true",
                     help="also time batches of 96 .. 1,572,864 ids (the replay tiled) and report the marginal rate")
+    ap.add_argument("--sharded", type=int, default=0, metavar="G",
+                    help="time this GPU's steps of a lookup into the d512 table split by rows over G GPUs "
+                         "(plan, owner record gather, staged decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     args = ap.parse_args()
@@ -420,6 +597,11 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.encode:
         return bench_encode(args, np, torch, cp, workload)
+    if args.sharded:
+        if not 2 <= args.sharded <= cp.CP_MAX_SHARDS:
+            print(f"--sharded takes 2 .. {cp.CP_MAX_SHARDS} shards", file=sys.stderr)
+            return 2
+        return bench_sharded(args, np, torch, cp, workload)
     cfg = workload.CONFIGS[args.config]
     ids_kind = args.ids or cfg.ids_kind
     lut = workload.lut_fp16(0)

@@ -320,6 +320,83 @@ cp_status cp_table_set_hot_rows(cp_table *table, const int64_t *rows, uint64_t c
 /* Number of distinct rows with a device copy (0 for NULL or none). */
 uint64_t cp_table_hot_rows(const cp_table *table);
 
+/* ---------------------------------------------------------------------
+ * A table sharded by rows over several GPUs: the steps each GPU runs.
+ *
+ * The pages run CP with the table split over 4 (or 8) GPUs of one node,
+ * 12.7 GB on each ("2비트 코드와 공유 트렐리스로 n-gram 룩업 테이블을 4~8배
+ * 압축한다", onedev.kr, section "Assumptions and limits"). Records are
+ * independently addressable and only requested rows are decoded (same page,
+ * "How it differs"), so a lookup moves records rather than decoded rows:
+ *   1. the requester plans: cp_shard_plan groups its ids by owning shard;
+ *   2. (the caller sends shard s the ids local_ids[start_s, start_s +
+ *      counts[s]), start_s = counts[0] + ... + counts[s - 1]: an all-to-all)
+ *   3. each owner copies the requested records: cp_table_gather_records;
+ *   4. (the records come back in the same order: a second all-to-all, R
+ *      bytes per lookup where a decoded row is 2 d)
+ *   5. the requester decodes: cp_lookup_decode_staged on the received
+ *      buffer, with the plan's positions, writes its rows in its original
+ *      lookup order.
+ * Steps 2 and 4 are the caller's (RCCL, or a copy when owners share a GPU).
+ * The shards are tables of rows_per_shard rows (the last may be shorter)
+ * with the same codebook and shape; shard s holds global rows
+ * [s * rows_per_shard, (s + 1) * rows_per_shard).
+ * --------------------------------------------------------------------- */
+
+/* Largest number of shards cp_shard_plan takes. */
+#define CP_MAX_SHARDS 64u
+
+/* Device workspace bytes cp_shard_plan needs for n ids over `shards` shards
+ * (0 when n == 0 or shards is 0 or above CP_MAX_SHARDS). */
+uint64_t cp_shard_plan_workspace_bytes(uint64_t n, uint32_t shards);
+
+/* Groups a batch of global row ids by owning shard, keeping batch order
+ * within each shard (a stable counting sort), on the current device.
+ *   ids       - device int64[n], 8-byte aligned; global row ids.
+ *   n         - 0 <= n <= 2^31 - 1.
+ *   rows_per_shard, shards - the owner of id i is i / rows_per_shard when
+ *               0 <= i < shards * rows_per_shard; other ids belong to no
+ *               shard. 1 <= shards <= CP_MAX_SHARDS.
+ *   local_ids - device int64[n] (written: the first counts[0] + ... +
+ *               counts[shards - 1] entries): the valid ids grouped by
+ *               shard, shard 0 first, each as its row within its shard.
+ *   positions - device int64[n]: positions[j] = the index in local_ids of
+ *               lookup j's entry (= where its record will sit in the
+ *               received buffer), or -1 for an id no shard owns.
+ *   counts    - device uint64[shards]: valid ids per shard.
+ *   workspace - device, 256-byte aligned, >= cp_shard_plan_workspace_bytes.
+ * Asynchronous on `stream`; allocates nothing. The result does not depend on
+ * how the GPU schedules the work (stable order).
+ * Errors: INVALID_ARGUMENT (NULL or misaligned pointers, n too large,
+ * shards out of range, rows_per_shard == 0 or shards * rows_per_shard
+ * above 2^64 - 1, workspace too small), HIP. */
+cp_status cp_shard_plan(const int64_t *ids, uint64_t n, uint64_t rows_per_shard, uint32_t shards, int64_t *local_ids,
+                        int64_t *positions, uint64_t *counts, void *workspace, uint64_t workspace_bytes,
+                        void *stream);
+
+/* The owner's step: copies the records of rows ids[0..n) of the table into
+ * `dst` (device, 2-byte aligned), packed: record k at bytes [k R, k R + R).
+ * An id outside [0, rows) writes a zero record and raises the table's flag
+ * (cp_table_check). Rows of a pinned-host table are read over PCIe (its
+ * device copies of hot rows hold the same bytes). Asynchronous on `stream`.
+ * Errors: INVALID_ARGUMENT (NULL table, NULL or misaligned ids / dst),
+ * UNSUPPORTED (a mixed-rate table), HIP. */
+cp_status cp_table_gather_records(cp_table *table, const int64_t *ids, uint64_t n, void *dst, void *stream);
+
+/* The requester's step: decodes received records. `records` (device,
+ * 16-byte aligned) holds nrecords packed records of this table's shape (R
+ * bytes each) followed by at least 64 readable bytes (loads of the last
+ * record may touch up to 7 bytes past it; their values do not matter).
+ * Row j of `out` (bf16 [n][d], 16-byte aligned) becomes alpha * f(c) of
+ * record positions[j] (device int64[n], 8-byte aligned), decoded with this
+ * table's codebook exactly as cp_lookup_decode decodes a row; a position
+ * outside [0, nrecords) gives a zero row and raises the table's flag.
+ * Asynchronous on `stream`; allocates nothing.
+ * Errors: INVALID_ARGUMENT (NULL table, NULL or misaligned pointers),
+ * UNSUPPORTED (a mixed-rate table), HIP. */
+cp_status cp_lookup_decode_staged(const cp_table *table, const void *records, uint64_t nrecords,
+                                  const int64_t *positions, uint64_t n, uint16_t *out, void *stream);
+
 /* Synchronises `stream`, then returns CP_ERR_ID_OUT_OF_RANGE and clears the
  * table's flag if any lookup since the last check saw an id outside
  * [0, rows); otherwise CP_OK. Errors: INVALID_ARGUMENT, HIP. */

@@ -236,6 +236,37 @@ def mixed_offsets(d: int, kv_of_class, row_class) -> np.ndarray:
     return off
 
 
+def shard_plan(ids, rows_per_shard: int, shards: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """A lookup batch into a table split by rows over `shards` GPUs, 12.7 GB
+    each in the pages' 4-GPU setup ("2비트 코드와 공유 트렐리스로 n-gram 룩업
+    테이블을 4~8배 압축한다", onedev.kr, "Assumptions and limits"): the owner of
+    global row i is i // rows_per_shard (for 0 <= i < shards * rows_per_shard;
+    other ids belong to no shard). Returns (local_ids, positions, counts):
+    the owned ids sorted by owner with a stable sort (batch order kept within
+    a shard), each as its row within its shard; for each lookup its index in
+    that order (-1 when no shard owns the id); ids per shard."""
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    valid = (ids >= 0) & (ids < shards * rows_per_shard)
+    owner = np.where(valid, ids // rows_per_shard, shards)
+    order = np.argsort(owner, kind="stable")[: int(valid.sum())]
+    local_ids = ids[order] - owner[order] * rows_per_shard
+    positions = np.full(ids.shape[0], -1, dtype=np.int64)
+    positions[order] = np.arange(order.shape[0], dtype=np.int64)
+    counts = np.bincount(owner[valid], minlength=shards).astype(np.int64)
+    return local_ids.astype(np.int64), positions, counts
+
+
+def gather_records(records, rows: int, ids) -> np.ndarray:
+    """The owner's part of a sharded lookup: the packed records of rows
+    ids[k] (uint8[n, R]), a zero record for an id outside [0, rows)."""
+    recs = np.asarray(records, dtype=np.uint8).reshape(rows, -1)
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    ok = (ids >= 0) & (ids < rows)
+    out = np.zeros((ids.shape[0], recs.shape[1]), dtype=np.uint8)
+    out[ok] = recs[ids[ok]]
+    return out
+
+
 def lookup_decode_mixed(lut, records, d: int, kv_of_class, row_class, ids, raw: bool = False,
                         offsets=None, nthreads: int | None = None) -> tuple[np.ndarray, int]:
     """Rows ids[j] of a mixed-rate table, in lookup order; as lookup_decode.

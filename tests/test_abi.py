@@ -236,3 +236,28 @@ def test_touch_ahead_is_for_single_rate_device_tables():
     st, h = cp.cp_table_create_mixed(_mdesc(flags=cp.CP_FLAG_TOUCH_AHEAD), ctypes.addressof(lut),
                                      ctypes.addressof(cls))
     assert (st, h) == (cp.CP_ERR_INVALID_ARGUMENT, 0)
+
+
+def test_shard_entry_points_check_arguments_on_the_host():
+    assert cp.cp_shard_plan_workspace_bytes(0, 4) == 0
+    assert cp.cp_shard_plan_workspace_bytes(1000, 0) == 0
+    assert cp.cp_shard_plan_workspace_bytes(1000, cp.CP_MAX_SHARDS + 1) == 0
+    # 1 tile of 1024 ids: 4-byte counts and 8-byte starts per shard, each padded to 256 bytes
+    assert cp.cp_shard_plan_workspace_bytes(1000, 4) == 512
+    assert cp.cp_shard_plan_workspace_bytes(393_216, 4) == 6_144 + 12_288
+    E = cp.CP_ERR_INVALID_ARGUMENT
+    ws = 1 << 20  # a stand-in address, never dereferenced: every call below fails its checks first
+    plan = lambda n=8, rps=10, shards=4, ids=256, loc=256, pos=256, cnt=256, w=ws, wb=1 << 16: \
+        cp.cp_shard_plan(ids, n, rps, shards, loc, pos, cnt, w, wb, None)
+    assert plan(shards=0) == E
+    assert plan(shards=cp.CP_MAX_SHARDS + 1) == E
+    assert plan(rps=0) == E
+    assert plan(rps=2**63, shards=2) == E          # shards * rows_per_shard overflows
+    assert plan(n=2**31) == E
+    assert plan(cnt=0) == E and plan(cnt=260) == E
+    assert plan(ids=0) == E and plan(ids=260) == E
+    assert plan(loc=0) == E and plan(pos=4) == E
+    assert plan(w=0) == E and plan(w=ws + 16) == E
+    assert plan(wb=511) == E                        # 8 ids over 4 shards need 512 bytes
+    assert cp.cp_table_gather_records(0, 256, 1, 256, None) == E
+    assert cp.cp_lookup_decode_staged(0, 256, 1, 256, 1, 256, None) == E

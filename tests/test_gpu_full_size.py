@@ -16,7 +16,7 @@ import torch
 import oracle
 import trellis_coded_row_amd as cp
 import workload
-from parity import check_lookup, make_table, say
+from parity import assert_scaled_matches, check_lookup, make_table, say
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +79,40 @@ def test_gpu_d512_replays(big_records):
     try:
         check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), "gpu_d512 zipf replay", dedup=True)
         check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.uniform_variant_ids(), "gpu_d512 uniform replay")
+    finally:
+        t.close()
+        torch.cuda.empty_cache()
+
+
+def test_gpu_d512_sharded_replay(big_records):
+    """The benchmark's sharded workload: the 12.70 GB table as shard 0 of 4 x
+    97,690,000 rows, the replay's ids Zipf over all four shards. This GPU's
+    steps in full: the plan of the whole replay (bit-exact), the owner's
+    gather of every planned record from this table (bit-exact) and the
+    decode of the gathered buffer (every row against the oracle)."""
+    cfg, recs = big_records
+    shards, rps = 4, cfg.rows
+    ids = workload.zipf_ids(shards * rps, cfg.n_ids, cfg.ids_seed)
+    t = make_table(LUT, recs, cfg.d, cfg.kv)
+    try:
+        say("sharded replay: plan")
+        loc, pos, cnt = cp.shard_plan(torch.from_numpy(ids).cuda(), rps, shards)
+        e_loc, e_pos, e_cnt = oracle.shard_plan(ids, rps, shards)
+        torch.cuda.synchronize()
+        assert (cnt.cpu().numpy() == e_cnt).all() and (pos.cpu().numpy() == e_pos).all()
+        assert (loc.cpu().numpy() == e_loc).all()
+        say("sharded replay: owner gather of all planned records")
+        recv = t.gather_records(loc)
+        torch.cuda.synchronize()
+        R = t.record_bytes
+        got = recv.cpu().numpy()[: ids.size * R].reshape(ids.size, R)
+        assert (got == oracle.gather_records(recs, rps, e_loc)).all()
+        say("sharded replay: staged decode")
+        out = t.lookup_decode_staged(recv, ids.size, pos)
+        torch.cuda.synchronize()
+        exp, bad = oracle.lookup_decode(LUT, recs, rps, cfg.d, cfg.kv, ids % rps)
+        assert bad == 0 and t.check()
+        assert_scaled_matches(out.view(torch.int16).cpu().numpy().view(np.uint16), exp, "sharded gpu_d512 replay")
     finally:
         t.close()
         torch.cuda.empty_cache()

@@ -741,3 +741,34 @@ def test_rows_with_non_finite_norm_encode_to_the_zero_record(bad):
     assert alpha == 0.0 and (rec == 0).all()
     recs, _ = oracle.encode_rows(e[None, :], d, kv, LUT, oracle.ENC_HEURISTIC)
     assert (recs == 0).all()
+
+
+def test_shard_plan_is_a_stable_grouping_by_owner():
+    """The oracle's shard plan against a construction by hand: walk the
+    shards in order and, within each, the batch in order."""
+    rng = np.random.default_rng(4100)
+    for trial in range(60):
+        shards = int(rng.integers(1, 9))
+        rps = int(rng.integers(1, 50))
+        n = int(rng.integers(0, 300))
+        ids = rng.integers(-5, shards * rps + 10, n).astype(np.int64)
+        local_ids, positions, counts = oracle.shard_plan(ids, rps, shards)
+        exp_local, exp_pos, exp_counts = [], [-1] * n, []
+        for s in range(shards):
+            mine = [j for j in range(n) if 0 <= ids[j] < shards * rps and ids[j] // rps == s]
+            exp_counts.append(len(mine))
+            for j in mine:
+                exp_pos[j] = len(exp_local)
+                exp_local.append(int(ids[j]) - s * rps)
+        assert local_ids.tolist() == exp_local
+        assert positions.tolist() == exp_pos
+        assert counts.tolist() == exp_counts
+
+
+def test_gather_records_copies_rows_and_zeroes_bad_ids():
+    rng = np.random.default_rng(4101)
+    recs = rng.integers(0, 256, (37, 18), dtype=np.uint8)
+    ids = np.array([3, 36, 0, -1, 37, 3, 2**40], dtype=np.int64)
+    got = oracle.gather_records(recs, 37, ids)
+    for k, i in enumerate(ids):
+        assert (got[k] == (recs[i] if 0 <= i < 37 else 0)).all()

@@ -29,6 +29,8 @@ __all__ = [
     "cp_record_bytes", "cp_supported", "cp_table_create", "cp_table_upload", "cp_lookup_decode",
     "cp_lookup_decode_raw", "cp_dedup_workspace_bytes", "cp_lookup_decode_dedup",
     "cp_lookup_decode_dedup_noalloc", "CP_DEDUP_NOALLOC_MAX_IDS",
+    "cp_shard_plan_workspace_bytes", "cp_shard_plan", "cp_table_gather_records", "cp_lookup_decode_staged",
+    "CP_MAX_SHARDS", "shard_plan",
     "cp_table_download", "cp_encode_workspace_bytes", "cp_table_encode",
     "cp_table_set_hot_rows", "cp_table_hot_rows",
     "cp_table_create_mixed", "cp_table_record_range", "cp_table_describe_mixed", "cp_mixed_desc", "MixedTable",
@@ -50,6 +52,7 @@ CP_RESIDENCY_HOST_MAPPED = 1
 CP_FLAG_HOST_NONCOHERENT = 1
 CP_FLAG_TOUCH_AHEAD = 2
 CP_DEDUP_NOALLOC_MAX_IDS = 65536
+CP_MAX_SHARDS = 64
 
 
 class cp_table_desc(ctypes.Structure):
@@ -109,6 +112,11 @@ def load_library() -> ctypes.CDLL:
         "cp_dedup_workspace_bytes": (ctypes.c_uint64, [vp, ctypes.c_uint64]),
         "cp_lookup_decode_dedup": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp]),
         "cp_lookup_decode_dedup_noalloc": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
+        "cp_shard_plan_workspace_bytes": (ctypes.c_uint64, [ctypes.c_uint64, ctypes.c_uint32]),
+        "cp_shard_plan": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32, vp, vp, vp, vp,
+                                         ctypes.c_uint64, vp]),
+        "cp_table_gather_records": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, vp]),
+        "cp_lookup_decode_staged": (ctypes.c_int, [vp, vp, ctypes.c_uint64, vp, ctypes.c_uint64, vp, vp]),
         "cp_table_download": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp]),
         "cp_encode_workspace_bytes": (ctypes.c_uint64, [vp, ctypes.c_uint64]),
         "cp_table_encode": (ctypes.c_int, [vp, ctypes.c_uint64, ctypes.c_uint64, vp, vp, ctypes.c_uint64, vp]),
@@ -206,6 +214,49 @@ def cp_lookup_decode_dedup(table: int, ids_ptr: int, n: int, out_ptr: int, works
 
 def cp_lookup_decode_dedup_noalloc(table: int, ids_ptr: int, n: int, out_ptr: int, stream: int | None) -> int:
     return _L.cp_lookup_decode_dedup_noalloc(table, ids_ptr, n, out_ptr, stream)
+
+
+def cp_shard_plan_workspace_bytes(n: int, shards: int) -> int:
+    return int(_L.cp_shard_plan_workspace_bytes(n, shards))
+
+
+def cp_shard_plan(ids_ptr: int, n: int, rows_per_shard: int, shards: int, local_ids_ptr: int, positions_ptr: int,
+                  counts_ptr: int, workspace_ptr: int, workspace_bytes: int, stream: int | None) -> int:
+    return _L.cp_shard_plan(ids_ptr, n, rows_per_shard, shards, local_ids_ptr, positions_ptr, counts_ptr,
+                            workspace_ptr, workspace_bytes, stream)
+
+
+def cp_table_gather_records(table: int, ids_ptr: int, n: int, dst_ptr: int, stream: int | None) -> int:
+    return _L.cp_table_gather_records(table, ids_ptr, n, dst_ptr, stream)
+
+
+def cp_lookup_decode_staged(table: int, records_ptr: int, nrecords: int, positions_ptr: int, n: int, out_ptr: int,
+                            stream: int | None) -> int:
+    return _L.cp_lookup_decode_staged(table, records_ptr, nrecords, positions_ptr, n, out_ptr, stream)
+
+
+def shard_plan(ids, rows_per_shard: int, shards: int, stream=None):
+    """(local_ids int64[n], positions int64[n], counts int64[shards]) of
+    cp_shard_plan for a contiguous 1-D int64 device tensor of global ids:
+    the ids grouped by owning shard (owner = id // rows_per_shard), each as
+    its row within the shard, in batch order within a shard; for each
+    lookup its index in that grouping (-1 when no shard owns the id); and
+    the number of ids per shard."""
+    if not (ids.is_cuda and ids.dtype == torch.int64 and ids.dim() == 1 and ids.is_contiguous()):
+        raise ValueError("ids must be a contiguous 1-D int64 device tensor")
+    n = ids.shape[0]
+    local_ids = torch.empty(max(n, 1), dtype=torch.int64, device=ids.device)
+    positions = torch.empty(max(n, 1), dtype=torch.int64, device=ids.device)
+    counts = torch.empty(max(shards, 1), dtype=torch.int64, device=ids.device)
+    need = cp_shard_plan_workspace_bytes(n, shards)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=ids.device)
+    st = cp_shard_plan(ids.data_ptr(), n, rows_per_shard, shards, local_ids.data_ptr(), positions.data_ptr(),
+                       counts.data_ptr(), ws.data_ptr(), ws.numel(), _stream_handle(stream))
+    if st != CP_OK:
+        raise CPError(st, "cp_shard_plan")
+    for t in (local_ids, positions, counts, ws):
+        _keep_for_stream(t, stream)
+    return local_ids[:n], positions[:n], counts[:shards]
 
 
 def cp_table_download(table: int, first_row: int, nrows: int, dst_ptr: int) -> int:
@@ -375,6 +426,46 @@ class Table:
         st = cp_lookup_decode_dedup_noalloc(self.handle, ids.data_ptr(), n, out.data_ptr(), _stream_handle(stream))
         if st != CP_OK:
             raise CPError(st, "cp_lookup_decode_dedup_noalloc")
+        return out
+
+    def gather_records(self, ids, dst=None, stream=None):
+        """uint8[n, R] device tensor: the records of rows ids[k], packed (the
+        owner's step of a sharded lookup); 64 bytes of padding follow the
+        last record when allocated here, so the result can be decoded by
+        lookup_decode_staged directly."""
+        if not (ids.is_cuda and ids.dtype == torch.int64 and ids.dim() == 1 and ids.is_contiguous()):
+            raise ValueError("ids must be a contiguous 1-D int64 device tensor")
+        n, R = ids.shape[0], self.record_bytes
+        own = dst is None
+        if own:
+            dst = torch.zeros(n * R + 64, dtype=torch.uint8, device=ids.device)
+        elif not (dst.is_cuda and dst.dtype == torch.uint8 and dst.is_contiguous() and dst.numel() >= n * R):
+            raise ValueError(f"dst must be a contiguous uint8 device tensor of at least {n * R} bytes")
+        st = cp_table_gather_records(self.handle, ids.data_ptr(), n, dst.data_ptr(), _stream_handle(stream))
+        if st != CP_OK:
+            raise CPError(st, "cp_table_gather_records")
+        if own:
+            _keep_for_stream(dst, stream)
+        return dst
+
+    def lookup_decode_staged(self, records, nrecords: int, positions, out=None, stream=None):
+        """bf16[n, d]: row j decodes record positions[j] of the packed
+        buffer `records` (a uint8 device tensor of at least nrecords * R + 64
+        bytes), with this table's codebook (the requester's step of a
+        sharded lookup)."""
+        R = self.record_bytes
+        if not (records.is_cuda and records.dtype == torch.uint8 and records.is_contiguous()
+                and records.numel() >= nrecords * R + 64 and records.data_ptr() % 16 == 0):
+            raise ValueError("records must be a contiguous, 16-byte aligned uint8 device tensor of at least "
+                             f"{nrecords * R + 64} bytes")
+        own = out is None
+        n, out = self._check_io(positions, out, torch.bfloat16)
+        st = cp_lookup_decode_staged(self.handle, records.data_ptr(), nrecords, positions.data_ptr(), n,
+                                     out.data_ptr(), _stream_handle(stream))
+        if st != CP_OK:
+            raise CPError(st, "cp_lookup_decode_staged")
+        if own:
+            _keep_for_stream(out, stream)
         return out
 
     def download(self, first_row: int = 0, nrows: int | None = None) -> np.ndarray:

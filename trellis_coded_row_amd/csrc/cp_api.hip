@@ -715,6 +715,97 @@ cp_status cp_table_encode(cp_table *t, uint64_t first_row, uint64_t nrows, const
     return CP_OK;
 }
 
+uint64_t cp_shard_plan_workspace_bytes(uint64_t n, uint32_t shards)
+{
+    if (n == 0 || shards == 0 || shards > cpk::kMaxShards) return 0;
+    return cpk::shard_plan_workspace_bytes(n, shards);
+}
+
+cp_status cp_shard_plan(const int64_t *ids, uint64_t n, uint64_t rows_per_shard, uint32_t shards, int64_t *local_ids,
+                        int64_t *positions, uint64_t *counts, void *workspace, uint64_t workspace_bytes,
+                        void *stream)
+{
+    if (shards == 0 || shards > cpk::kMaxShards || rows_per_shard == 0) return CP_ERR_INVALID_ARGUMENT;
+    if (!counts || ((uintptr_t)counts & 7u)) return CP_ERR_INVALID_ARGUMENT;
+    if (n > 0x7FFFFFFFull) return CP_ERR_INVALID_ARGUMENT;
+    if (shards > UINT64_MAX / rows_per_shard) return CP_ERR_INVALID_ARGUMENT;  // shards * rows_per_shard overflows
+    if (n > 0) {
+        if (!ids || !local_ids || !positions || ((uintptr_t)ids & 7u) || ((uintptr_t)local_ids & 7u) ||
+            ((uintptr_t)positions & 7u))
+            return CP_ERR_INVALID_ARGUMENT;
+        if (!workspace || ((uintptr_t)workspace & 255u) ||
+            workspace_bytes < cpk::shard_plan_workspace_bytes(n, shards))
+            return CP_ERR_INVALID_ARGUMENT;
+    }
+    (void)hipGetLastError();
+    if (n == 0) {
+        // nothing to sort: the counts are zero (a kernel, so the call stays
+        // capturable and asynchronous like the others)
+        cpk::ShardPlanArgs a{};
+        a.counts = counts;
+        a.shards = shards;
+        a.stream = (hipStream_t)stream;
+        const hipError_t e = cpk::shard_plan_zero_counts(a);
+        return e == hipSuccess ? CP_OK : hip_fail(e);
+    }
+    cpk::ShardPlanArgs a;
+    a.ids = ids;
+    a.n = n;
+    a.rows_per_shard = rows_per_shard;
+    a.shards = shards;
+    a.local_ids = local_ids;
+    a.positions = positions;
+    a.counts = counts;
+    a.workspace = static_cast<uint8_t *>(workspace);
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = cpk::shard_plan(a);
+    return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
+cp_status cp_table_gather_records(cp_table *t, const int64_t *ids, uint64_t n, void *dst, void *stream)
+{
+    if (!t) return CP_ERR_INVALID_ARGUMENT;
+    if (t->mixed) return CP_ERR_UNSUPPORTED;
+    if (n == 0) return CP_OK;
+    if (!ids || !dst || ((uintptr_t)ids & 7u) || ((uintptr_t)dst & 1u)) return CP_ERR_INVALID_ARGUMENT;
+    DeviceGuard guard(t->device);
+    if (guard.err != hipSuccess) return hip_fail(guard.err);
+    // rows with device copies read the same bytes from the host records
+    const hipError_t e = cpk::gather_records_launch(t->records_dev, t->desc.rows, t->record_bytes, ids, n,
+                                                    static_cast<uint8_t *>(dst), t->err_dev, t->num_cus,
+                                                    (hipStream_t)stream);
+    return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
+cp_status cp_lookup_decode_staged(const cp_table *t, const void *records, uint64_t nrecords, const int64_t *positions,
+                                  uint64_t n, uint16_t *out, void *stream)
+{
+    if (!t) return CP_ERR_INVALID_ARGUMENT;
+    if (t->mixed) return CP_ERR_UNSUPPORTED;
+    if (n == 0) return CP_OK;
+    // the kernel's dword loads are aligned relative to the buffer's start
+    if (!records || ((uintptr_t)records & 15u)) return CP_ERR_INVALID_ARGUMENT;
+    if (!positions || !out || ((uintptr_t)out & 15u) || ((uintptr_t)positions & 7u)) return CP_ERR_INVALID_ARGUMENT;
+    DeviceGuard guard(t->device);
+    if (guard.err != hipSuccess) return hip_fail(guard.err);
+    // the gather-decode kernel with the received buffer as the table: row j
+    // of the output decodes record positions[j] (a position outside
+    // [0, nrecords) gives a zero row and raises the flag)
+    cpk::LaunchArgs a;
+    a.records = static_cast<const uint8_t *>(records);
+    a.rows = nrecords;
+    a.lut = t->lut_dev;
+    a.ids = positions;
+    a.n = n;
+    a.by_offset = false;
+    a.out = reinterpret_cast<uint32_t *>(out);
+    a.err = t->err_dev;
+    a.num_cus = t->num_cus;
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = cpk::launch(t->desc.d, t->desc.bits_per_step, false, a);
+    return e == hipSuccess ? CP_OK : hip_fail(e);
+}
+
 cp_status cp_table_check(cp_table *t, void *stream)
 {
     if (!t) return CP_ERR_INVALID_ARGUMENT;

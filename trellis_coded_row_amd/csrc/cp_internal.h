@@ -165,6 +165,32 @@ int mixed_index_build(const uint8_t *row_class, uint64_t rows, uint32_t nclass, 
 // Byte offset (and class) of a row's record, from a host copy of the index.
 uint64_t mixed_record_offset(const MixedEntry *index, const uint32_t R[4], uint64_t row, uint32_t *cls);
 
+// Row-sharded tables (see cp_shard.hip): the requester's plan, a stable
+// counting sort of its ids by owning shard (owner of row i =
+// i / rows_per_shard, for i < shards * rows_per_shard).
+constexpr uint32_t kMaxShards = 64;
+
+struct ShardPlanArgs {
+    const int64_t *ids;
+    uint64_t n;
+    uint64_t rows_per_shard;
+    uint32_t shards;          // 1..kMaxShards
+    int64_t *local_ids;       // n entries: ids within their shard, grouped by shard in batch order
+    int64_t *positions;       // n entries: lookup j's place in local_ids, -1 when no shard owns it
+    uint64_t *counts;         // shards entries
+    uint8_t *workspace;       // shard_plan_workspace_bytes(n, shards), 256-byte aligned
+    hipStream_t stream;
+};
+
+uint64_t shard_plan_workspace_bytes(uint64_t n, uint32_t shards);
+hipError_t shard_plan(const ShardPlanArgs &a);
+// counts[0..shards) = 0 (the plan of an empty batch)
+hipError_t shard_plan_zero_counts(const ShardPlanArgs &a);
+// Copies the records of rows ids[0..n) into dst, packed (record k at byte
+// k * R); zeros and the error flag for an id outside [0, rows).
+hipError_t gather_records_launch(const uint8_t *records, uint64_t rows, uint64_t R, const int64_t *ids, uint64_t n,
+                                 uint8_t *dst, int *err, int num_cus, hipStream_t stream);
+
 // True when a kernel for (d, kv) is compiled in.
 bool supported(uint32_t d, uint32_t kv);
 
