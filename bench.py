@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "single": ("cp_decode.hip", "cp_lane.h"),
     "mixed": ("cp_mixed.hip", "cp_lane.h"),
     "encode": ("cp_encode.hip", "cp_encode_copies.h"),
+    "shard": ("cp_shard.hip", "cp_decode.hip", "cp_lane.h"),
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -74,6 +75,34 @@ def read_counter_summary(config: str, ids_kind: str, kind: str = "single") -> di
     res = {"fetch_bytes": fetch, "write_bytes": write, "bytes": fetch + write, "file": os.path.basename(path)}
     if "PCIE_READ_BYTES_per_dispatch" in vals:
         res["pcie_bytes"] = float(vals["PCIE_READ_BYTES_per_dispatch"])
+    return res
+
+
+def read_shard_counters(G: int) -> dict | None:
+    """HBM bytes per dispatch of each kernel of the sharded workload's steps,
+    from a committed rocprofv3 --pmc summary taken on the current sources."""
+    path = os.path.join(PROFILES, f"counters_shard_steps_sharded_d512_g{G}.txt")
+    if not os.path.exists(path):
+        return None
+    vals: dict[str, str] = {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#") and ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash("shard"):
+        return None
+    try:
+        fs, ws = float(vals["fetch_scale"]), float(vals["write_scale"])
+        res = {}
+        for k in ("shard_count", "shard_scan", "shard_scatter", "gather_records", "gather_decode"):
+            f = float(vals[f"{k}_FETCH_SIZE_KiB_per_dispatch"]) * 1024 * fs
+            w = float(vals[f"{k}_WRITE_SIZE_KiB_per_dispatch"]) * 1024 * ws
+            res[k] = {"fetch_bytes": f, "write_bytes": w, "bytes": f + w}
+    except (KeyError, ValueError):
+        return None
+    res["file"] = os.path.basename(path)
     return res
 
 
@@ -525,6 +554,16 @@ def bench_sharded(args, np, torch, cp, workload) -> int:
             "step_effective_GBps": sum(algo.values()) / (ms / 1e3) / 1e9,
         },
     }
+    counters = read_shard_counters(G)
+    if counters:
+        res["roofline"]["traffic"] = counters["gather_decode"]["bytes"]
+        res["stage_hbm_traffic_bytes"] = {
+            "plan": sum(counters[k]["bytes"] for k in ("shard_count", "shard_scan", "shard_scatter")),
+            "gather": counters["gather_records"]["bytes"], "decode": counters["gather_decode"]["bytes"],
+            "file": counters["file"]}
+    if not args.no_probes:
+        # the 1 GiB copy also calibrates the byte counters of a profiled run
+        res["probes"] = probes(torch)
     if not same_as_direct:
         print("the staged rows differ from the direct lookup's", file=sys.stderr)
         return 1

@@ -179,7 +179,8 @@ __global__ __launch_bounds__(kPlanBlock) void shard_scatter(const int64_t *__res
 constexpr int kGatherPasses = 4;  // records per row in flight together
 constexpr uint32_t kGatherRecords = 4 * kGatherPasses;  // records per wave
 constexpr uint32_t kGatherMaxR = 194;                 // the largest record (d 512, 6 bits per step)
-constexpr uint32_t kGatherLds = (kGatherRecords * kGatherMaxR + 16 + 15) & ~15u;  // bytes per wave
+constexpr uint32_t kGatherStage = (kGatherRecords * kGatherMaxR + 16 + 15) & ~15u;  // staged bytes per wave
+constexpr uint32_t kGatherLds = kGatherStage + 256;  // and a spare dword per lane
 // four dwords at a 4-byte aligned address (one 16-byte access on the GPU),
 // and at a 16-byte aligned one
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
@@ -235,23 +236,23 @@ __global__ __launch_bounds__(256) void gather_records(const uint8_t *__restrict_
             const uint32_t after =
                 (uint32_t)__builtin_amdgcn_update_dpp((int)S[p].x, (int)S[p].x, 0x101 /* row_shl:1 */, 0xF, 0xF, false);
             const uint32_t src6[6] = {before, S[p].x, S[p].y, S[p].z, S[p].w, after};
-            if (j < cnt) {
-                const int r0 = 16 * (int)l - (int)dsh;  // record byte at this lane's first stage byte
-                uint8_t *q = stage + (at - dsh) + 16u * l;
+            // the lane's eight stage half-words, written without branches: a
+            // half-word outside the record (or of a record past the batch)
+            // goes to the lane's spare dword after the stage instead
+            const int r0 = 16 * (int)l - (int)dsh;  // record byte at this lane's first stage byte
+            const uint32_t q = (at - dsh) + 16u * l;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    // stage dword 4l+m starts at source byte 4(4l+m) + sh - dsh
-                    const uint32_t D = sh[p] == dsh ? src6[m + 1]
-                                       : sh[p] > dsh ? (src6[m + 1] >> 16) | (src6[m + 2] << 16)
-                                                     : (src6[m] >> 16) | (src6[m + 1] << 16);
-                    const int r = r0 + 4 * m;
-                    if (r >= 0 && r + 4 <= (int)R) {
-                        *reinterpret_cast<uint32_t *>(q + 4 * m) = D;
-                    } else if (r == -2) {
-                        *reinterpret_cast<uint16_t *>(q + 4 * m + 2) = (uint16_t)(D >> 16);
-                    } else if (r >= 0 && r + 2 == (int)R) {
-                        *reinterpret_cast<uint16_t *>(q + 4 * m) = (uint16_t)D;
-                    }
+            for (int m = 0; m < 4; ++m) {
+                // stage dword 4l+m starts at source byte 4(4l+m) + sh - dsh
+                const uint32_t D = sh[p] == dsh ? src6[m + 1]
+                                   : sh[p] > dsh ? (src6[m + 1] >> 16) | (src6[m + 2] << 16)
+                                                 : (src6[m] >> 16) | (src6[m + 1] << 16);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int r = r0 + 4 * m + 2 * e;
+                    const bool in = j < cnt && r >= 0 && r < (int)R;
+                    *reinterpret_cast<uint16_t *>(stage + (in ? q + 4u * m + 2u * e : kGatherStage + 4u * lane)) =
+                        (uint16_t)(D >> (16 * e));
                 }
             }
         }
