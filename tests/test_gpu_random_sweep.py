@@ -1,8 +1,9 @@
 """Seeded random sweep of the HIP lookup against the CPU oracle: table shape
 (d, kv), table size, batch size (every launch shape), id distribution with
 out-of-range ids sprinkled in, residency, touch-ahead tables, and entry
-point (raw, scaled, dedup), plus mixed-rate tables. Each case runs twice, so a result that
-changed from one launch to the next would fail as well as a wrong one."""
+point (raw, scaled, dedup), plus mixed-rate tables and the steps of a lookup into a
+row-sharded table. Each case runs twice, so a result that changed from one launch to
+the next would fail as well as a wrong one."""
 from __future__ import annotations
 
 import numpy as np
@@ -108,3 +109,55 @@ def test_random_mixed_rate(case):
             assert_scaled_matches(got, exp, f"{label} rows run {rep}")
     finally:
         t.close()
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_random_sharded(case):
+    """This GPU's steps of a lookup into a row-sharded table, chained over
+    shard tables on one GPU (each owner's gather into its own buffer, copied
+    to the requester's received buffer at the plan's offsets, as the exchange
+    would), against the oracle's lookup of the whole table; the plan and the
+    gathered records against the oracle's too."""
+    rng = np.random.default_rng(9800 + case)
+    d = int(rng.choice([64, 128, 256, 512]))
+    kv = int(rng.choice([3, 4, 5, 6]))
+    shards = int(rng.choice([1, 2, 3, 5, 8]))
+    rps = int(rng.choice([1, 7, 1000, 6_007]))
+    rows = shards * rps
+    n = int(rng.choice(sizes()))
+    host = bool(rng.random() < 0.25)
+    recs = workload.random_records(rows, d, kv, seed=int(rng.integers(1 << 30)))
+    ids = draw_ids(rng, rows, n)
+    label = f"sharded case {case}: d{d} kv{kv} {shards} x {rps} rows, n {n} {'host' if host else 'hbm'}"
+    say(label)
+    res = cp.CP_RESIDENCY_HOST_MAPPED if host else cp.CP_RESIDENCY_DEVICE
+    tables = [make_table(LUT, recs[s * rps:(s + 1) * rps], d, kv, residency=res) for s in range(shards)]
+    try:
+        e_loc, e_pos, e_cnt = oracle.shard_plan(ids, rps, shards)
+        exp, nbad = oracle.lookup_decode(LUT, recs, rows, d, kv, ids)
+        R = tables[0].record_bytes
+        for rep in range(2):
+            loc, pos, cnt = cp.shard_plan(torch.from_numpy(ids).cuda(), rps, shards)
+            torch.cuda.synchronize()
+            assert (cnt.cpu().numpy() == e_cnt).all() and (pos.cpu().numpy() == e_pos).all(), label
+            assert (loc.cpu().numpy()[: e_loc.size] == e_loc).all(), label
+            total = int(e_cnt.sum())
+            recv = torch.zeros(total * R + 64, dtype=torch.uint8, device="cuda")
+            start = 0
+            for s, t in enumerate(tables):
+                c = int(e_cnt[s])
+                if c:
+                    sent = t.gather_records(loc[start:start + c])
+                    recv[start * R:(start + c) * R].copy_(sent[: c * R])
+                    part = oracle.gather_records(recs[s * rps:(s + 1) * rps], rps, e_loc[start:start + c])
+                    assert (sent.cpu().numpy()[: c * R].reshape(c, R) == part).all(), f"{label} shard {s}"
+                start += c
+            out = tables[0].lookup_decode_staged(recv, total, pos)
+            torch.cuda.synchronize()
+            assert tables[0].check() == (nbad == 0), label
+            assert_scaled_matches(out.view(torch.int16).cpu().numpy().view(np.uint16), exp, f"{label} run {rep}")
+            for t in tables[1:]:
+                assert t.check(), label  # owners only ever see their own rows
+    finally:
+        for t in tables:
+            t.close()
