@@ -242,9 +242,9 @@ def test_shard_entry_points_check_arguments_on_the_host():
     assert cp.cp_shard_plan_workspace_bytes(0, 4) == 0
     assert cp.cp_shard_plan_workspace_bytes(1000, 0) == 0
     assert cp.cp_shard_plan_workspace_bytes(1000, cp.CP_MAX_SHARDS + 1) == 0
-    # 1 tile of 1024 ids: 4-byte counts and 8-byte starts per shard, each padded to 256 bytes
+    # tiles of 512 ids: 4-byte counts and 8-byte starts per tile and shard, each array padded to 256 bytes
     assert cp.cp_shard_plan_workspace_bytes(1000, 4) == 512
-    assert cp.cp_shard_plan_workspace_bytes(393_216, 4) == 6_144 + 12_288
+    assert cp.cp_shard_plan_workspace_bytes(393_216, 4) == 12_288 + 24_576
     E = cp.CP_ERR_INVALID_ARGUMENT
     ws = 1 << 20  # a stand-in address, never dereferenced: every call below fails its checks first
     plan = lambda n=8, rps=10, shards=4, ids=256, loc=256, pos=256, cnt=256, w=ws, wb=1 << 16: \

@@ -54,6 +54,14 @@ def test_shard_plan_matches_the_oracle(shards):
                "descending")
 
 
+@pytest.mark.parametrize("shards", [3, 64])
+def test_shard_plan_of_a_batch_above_a_million_ids(shards):
+    # more tiles than one thread run per scan thread covers: the chunked scan
+    rps = 50_000_017
+    ids = workload.uniform_ids(shards * rps + 10, 1_300_003, seed=5050 + shards)  # a few ids past the last shard
+    check_plan(ids, rps, shards, "1.3 M ids")
+
+
 def test_shard_plan_of_an_empty_batch_zeroes_the_counts():
     counts = torch.full((8,), 77, dtype=torch.int64, device="cuda")
     st = cp.cp_shard_plan(0, 0, 10, 8, 0, 0, counts.data_ptr(), 0, 0, None)

@@ -23,7 +23,7 @@ namespace cpk {
 
 namespace {
 
-constexpr int kPlanTile = 1024;  // ids per workgroup in the plan kernels
+constexpr int kPlanTile = 512;  // ids per workgroup in the plan kernels
 constexpr int kPlanBlock = 256;  // threads per plan workgroup (4 waves)
 constexpr uint32_t kInvalid = 0xFFFFFFFFu;
 
@@ -43,13 +43,18 @@ __global__ __launch_bounds__(kPlanBlock) void shard_count(const int64_t *__restr
     const uint64_t ntiles = (n + kPlanTile - 1) / kPlanTile;
     for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         for (uint32_t s = threadIdx.x; s < shards; s += kPlanBlock) cnt[s] = 0;
-        __syncthreads();
-        for (int r = 0; r < kPlanTile / kPlanBlock; ++r) {
+        constexpr int ROUNDS = kPlanTile / kPlanBlock;
+        int64_t id[ROUNDS];
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
             const uint64_t j = tile * kPlanTile + r * kPlanBlock + threadIdx.x;
-            if (j < n) {
-                const uint32_t s = owner_of(ids[j], rows_per_shard, shards);
-                if (s != kInvalid) atomicAdd(&cnt[s], 1u);
-            }
+            id[r] = j < n ? ids[j] : -1;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
+            const uint32_t s = owner_of(id[r], rows_per_shard, shards);
+            if (s != kInvalid) atomicAdd(&cnt[s], 1u);
         }
         __syncthreads();
         for (uint32_t s = threadIdx.x; s < shards; s += kPlanBlock) tile_counts[tile * shards + s] = cnt[s];
@@ -57,48 +62,82 @@ __global__ __launch_bounds__(kPlanBlock) void shard_count(const int64_t *__restr
     }
 }
 
+// Inclusive prefix sum of v over the workgroup (kPlanBlock threads, in
+// thread order); *total = the sum over all threads.
+__device__ __forceinline__ uint64_t block_inclusive_sum(uint64_t v, uint64_t *wave_sum, uint64_t *total)
+{
+    constexpr int WAVES = kPlanBlock / 64;
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    uint64_t incl = v;
+    for (int k = 1; k < 64; k <<= 1) {
+        const uint64_t up = __shfl_up(incl, (unsigned)k, 64);
+        if (lane >= (uint32_t)k) incl += up;
+    }
+    if (lane == 63) wave_sum[w] = incl;
+    __syncthreads();
+    uint64_t before = 0, all = 0;
+    for (int q = 0; q < WAVES; ++q) {
+        if (q < (int)w) before += wave_sum[q];
+        all += wave_sum[q];
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl;
+}
+
 // Within shard s, tile t's entries start after those of tiles 0..t-1:
 // tile_start[tile][s] (relative to the shard's first entry); counts[s] the
-// shard totals. One workgroup per shard scans its column of tile counts,
-// 256 tiles at a time.
+// shard totals. One workgroup per shard scans its column of tile counts:
+// each thread a run of up to kScanPer consecutive tiles (all its loads in
+// flight together), or, for more tiles than that covers, 256 tiles at a time.
+constexpr uint32_t kScanPer = 8;
+
 __global__ __launch_bounds__(kPlanBlock) void shard_scan(const uint32_t *__restrict__ tile_counts, uint64_t ntiles,
                                                          uint32_t shards, uint64_t *__restrict__ tile_start,
                                                          uint64_t *__restrict__ counts)
 {
-    constexpr int WAVES = kPlanBlock / 64;
-    __shared__ uint64_t wave_sum[WAVES];
-    const uint32_t s = blockIdx.x, lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
-    uint64_t carry = 0;
-    for (uint64_t t0 = 0; t0 < ntiles; t0 += kPlanBlock) {
-        const uint64_t t = t0 + threadIdx.x;
-        const uint64_t v = t < ntiles ? tile_counts[t * shards + s] : 0;
-        // inclusive prefix sum over the wave
-        uint64_t incl = v;
-        for (int k = 1; k < 64; k <<= 1) {
-            const uint64_t up = __shfl_up(incl, (unsigned)k, 64);
-            if (lane >= (uint32_t)k) incl += up;
+    __shared__ uint64_t wave_sum[kPlanBlock / 64];
+    const uint32_t s = blockIdx.x;
+    uint64_t total = 0;
+    if (ntiles <= (uint64_t)kPlanBlock * kScanPer) {
+        const uint32_t per = (uint32_t)((ntiles + kPlanBlock - 1) / kPlanBlock);
+        const uint64_t t0 = (uint64_t)threadIdx.x * per;
+        uint32_t v[kScanPer];
+        uint64_t mine = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kScanPer; ++k) {
+            v[k] = (k < per && t0 + k < ntiles) ? tile_counts[(t0 + k) * shards + s] : 0u;
+            mine += v[k];
         }
-        if (lane == 63) wave_sum[w] = incl;
-        __syncthreads();
-        uint64_t before = carry, all = 0;
-        for (int q = 0; q < WAVES; ++q) {
-            if (q < (int)w) before += wave_sum[q];
-            all += wave_sum[q];
+        uint64_t run = block_inclusive_sum(mine, wave_sum, &total) - mine;
+#pragma unroll
+        for (uint32_t k = 0; k < kScanPer; ++k) {
+            if (k < per && t0 + k < ntiles) {
+                tile_start[(t0 + k) * shards + s] = run;
+                run += v[k];
+            }
         }
-        if (t < ntiles) tile_start[t * shards + s] = before + incl - v;
-        carry += all;
-        __syncthreads();
+    } else {
+        for (uint64_t t0 = 0; t0 < ntiles; t0 += kPlanBlock) {
+            const uint64_t t = t0 + threadIdx.x;
+            const uint64_t v = t < ntiles ? tile_counts[t * shards + s] : 0;
+            uint64_t all;
+            const uint64_t incl = block_inclusive_sum(v, wave_sum, &all);
+            if (t < ntiles) tile_start[t * shards + s] = total + incl - v;
+            total += all;
+        }
     }
-    if (threadIdx.x == 0) counts[s] = carry;
+    if (threadIdx.x == 0) counts[s] = total;
 }
 
 // Every id's place in its shard's list, in batch order (a stable sort): the
 // shard's first entry (the counts of the shards before it), plus the tile's
-// start within the shard, plus the id's rank within the tile: the tile's ids
-// go in four rounds of 256; in each round a wave ranks its lanes among the
-// lanes of the same shard (ballots), and the round's waves follow one
-// another. positions[j] = place of id j, -1 for an id owned by no shard;
-// local_ids[place] = the id within its shard.
+// start within the shard, plus the id's rank within the tile. Wave w of the
+// workgroup ranks quarter w of the tile, 64 ids per round: each lane among
+// the wave's earlier lanes of the same shard (one ballot per distinct shard
+// present), on top of the wave's running count for that shard; the quarters
+// then follow one another. positions[j] = place of id j, -1 for an id owned
+// by no shard; local_ids[place] = the id within its shard.
 __global__ __launch_bounds__(kPlanBlock) void shard_scatter(const int64_t *__restrict__ ids, uint64_t n,
                                                             uint64_t rows_per_shard, uint32_t shards,
                                                             const uint64_t *__restrict__ tile_start,
@@ -107,9 +146,9 @@ __global__ __launch_bounds__(kPlanBlock) void shard_scatter(const int64_t *__res
                                                             int64_t *__restrict__ positions)
 {
     constexpr int WAVES = kPlanBlock / 64;
+    constexpr int ROUNDS = kPlanTile / kPlanBlock;     // 64-id rounds per wave
     __shared__ uint64_t base[kMaxShards];              // shard s's first entry: counts of shards 0..s-1
-    __shared__ uint32_t seen[kMaxShards];              // tile's ids of shard s placed so far
-    __shared__ uint32_t wave_cnt[WAVES][kMaxShards];  // this round's ids of shard s per wave
+    __shared__ uint32_t wave_cnt[WAVES][kMaxShards];  // ids of shard s ranked by wave w so far
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const uint64_t ntiles = (n + kPlanTile - 1) / kPlanTile;
@@ -120,44 +159,47 @@ __global__ __launch_bounds__(kPlanBlock) void shard_scatter(const int64_t *__res
     __syncthreads();
     if (threadIdx.x < shards) base[threadIdx.x] = my_base;
     for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        for (uint32_t s = threadIdx.x; s < shards; s += kPlanBlock) seen[s] = 0;
-        for (int r = 0; r < kPlanTile / kPlanBlock; ++r) {
-            for (uint32_t i = threadIdx.x; i < WAVES * kMaxShards; i += kPlanBlock) (&wave_cnt[0][0])[i] = 0;
-            __syncthreads();
-            const uint64_t j = tile * kPlanTile + r * kPlanBlock + threadIdx.x;
-            const int64_t id = j < n ? ids[j] : -1;
-            const uint32_t s = j < n ? owner_of(id, rows_per_shard, shards) : kInvalid;
-            // rank among this wave's lanes of the same shard: one ballot per
-            // distinct shard present in the wave
-            uint32_t rank = 0;
+        for (uint32_t i = threadIdx.x; i < WAVES * kMaxShards; i += kPlanBlock) (&wave_cnt[0][0])[i] = 0;
+        // the wave's ids, all loaded before any is ranked
+        const uint64_t j0 = tile * kPlanTile + (uint64_t)w * (64 * ROUNDS) + lane;
+        int64_t id[ROUNDS];
+        uint32_t sh[ROUNDS], rank[ROUNDS];
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) id[r] = j0 + 64u * r < n ? ids[j0 + 64u * r] : -1;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
+            const uint32_t s = j0 + 64u * r < n ? owner_of(id[r], rows_per_shard, shards) : kInvalid;
+            sh[r] = s;
+            rank[r] = 0;
             uint64_t todo = __ballot(s != kInvalid);
             while (todo) {
                 const uint32_t leader = (uint32_t)__builtin_ctzll(todo);
                 const uint32_t sl = (uint32_t)__shfl((int)s, (int)leader, 64);
                 const uint64_t m = __ballot(s == sl);
-                if (s == sl) rank = (uint32_t)__builtin_popcountll(m & below);
-                if (lane == leader) wave_cnt[w][sl] = (uint32_t)__builtin_popcountll(m);
+                const uint32_t prev = wave_cnt[w][sl];
+                if (s == sl) rank[r] = prev + (uint32_t)__builtin_popcountll(m & below);
+                if (lane == leader) wave_cnt[w][sl] = prev + (uint32_t)__builtin_popcountll(m);
                 todo &= ~m;
             }
-            __syncthreads();
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
+            const uint64_t j = j0 + 64u * r;
             if (j < n) {
+                const uint32_t s = sh[r];
                 if (s == kInvalid) {
                     positions[j] = -1;
                 } else {
-                    uint64_t p = base[s] + tile_start[tile * shards + s] + seen[s] + rank;
+                    uint64_t p = base[s] + tile_start[tile * shards + s] + rank[r];
                     for (uint32_t q = 0; q < w; ++q) p += wave_cnt[q][s];
                     positions[j] = (int64_t)p;
-                    if (p < n) local_ids[p] = id - (int64_t)((uint64_t)s * rows_per_shard);
+                    if (p < n) local_ids[p] = id[r] - (int64_t)((uint64_t)s * rows_per_shard);
                 }
             }
-            __syncthreads();
-            for (uint32_t q = threadIdx.x; q < shards; q += kPlanBlock) {
-                uint32_t add = 0;
-                for (int v = 0; v < WAVES; ++v) add += wave_cnt[v][q];
-                seen[q] += add;
-            }
-            __syncthreads();
         }
+        __syncthreads();
     }
 }
 
