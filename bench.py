@@ -585,8 +585,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="gpu_d512",
-                    help="workload: gpu_d512 (default), host_d512, mixed_d512, small_d256, rate_d512_kv{3,4,5,6}, "
-                         "tiny_d64")
+                    help="workload: gpu_d512 (default), host_d512, mixed_d512, host_mixed_d512, small_d256, "
+                         "rate_d512_kv{3,4,5,6}, tiny_d64")
     ap.add_argument("--ids", default=None, choices=["zipf", "uniform", "slice96"],
                     help="id stream (default: the config's own)")
     ap.add_argument("--noncoherent", action="store_true", help="host_d512: non-coherent pinned memory")
@@ -822,10 +822,14 @@ def main() -> int:
         if hot_rows:
             uniq = uniq[~np.isin(uniq, hot_set_np)]
             res["lookups_served_from_hbm_copies"] = hot_lookups
-        pcie_bytes = int(uniq.size) * R
+        if mixed:
+            starts, sizes = offsets[uniq].astype(np.int64), class_bytes[classes[uniq]]
+        else:
+            starts, sizes = uniq * R, np.full(uniq.size, R, dtype=np.int64)
+        pcie_bytes = int(sizes.sum())
         # granules of 64 bytes the distinct records touch: what the reads move
         # if every distinct record is fetched once
-        first, last = uniq * R // 64, (uniq * R + R - 1) // 64
+        first, last = starts // 64, (starts + sizes - 1) // 64
         res["pcie_distinct_records"] = int(uniq.size)
         res["pcie_distinct_64B_granule_bytes"] = int((last - first + 1).sum()) * 64
         res["pcie_per_lookup_record_GBps"] = (n - hot_lookups) * R / (launch_ms / 1e3) / 1e9

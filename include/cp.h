@@ -166,8 +166,9 @@ cp_status cp_table_create(const cp_table_desc *desc, const uint16_t *lut_fp16, c
  * cp_lookup_decode / cp_lookup_decode_raw / cp_table_check /
  * cp_table_destroy work as for single-rate tables (record ranges given by the
  * rows' own sizes); cp_table_encode codes each row at its own class's rate;
- * cp_table_describe reports bits_per_step = 0; cp_lookup_decode_dedup returns
- * UNSUPPORTED.
+ * cp_table_describe reports bits_per_step = 0; cp_lookup_decode_dedup and
+ * cp_lookup_decode_dedup_noalloc stage the batch's distinct records, each at
+ * its own size, as a mixed-rate table of their own and decode that.
  * Errors: INVALID_ARGUMENT (NULL pointers, struct_size, rows == 0, nclass, a
  * codebook entry that is +-inf or NaN,
  * a class's rate without whole-byte records, a nonzero unused rate, a row
@@ -212,7 +213,8 @@ cp_status cp_lookup_decode_raw(const cp_table *table, const int64_t *ids, uint64
 
 /* Device workspace bytes that cp_lookup_decode_dedup needs for a batch of n
  * lookups on this table (0 for a NULL table). About 36 bytes per lookup plus
- * n records: 71 MB for n = 393,216 at d = 512, kv = 4. */
+ * n records: 71 MB for n = 393,216 at d = 512, kv = 4 (a mixed-rate table:
+ * about 37 bytes per lookup plus n of its largest records). */
 uint64_t cp_dedup_workspace_bytes(const cp_table *table, uint64_t n);
 
 /* Same result as cp_lookup_decode, fetching each distinct record of the batch
@@ -222,6 +224,9 @@ uint64_t cp_dedup_workspace_bytes(const cp_table *table, uint64_t n);
  * order. Meant for a table in pinned host memory, where every record read
  * crosses PCIe (the pages find that regime dominated by the fetch and the
  * row-wise layout's advantage growing there: "Assumptions and limits").
+ * Mixed-rate tables too: the distinct records are staged packed, each at its
+ * own class's size, with an index of their own, and decoded by the
+ * mixed-rate kernel.
  *   workspace       - device memory, 256-byte aligned, at least
  *                     cp_dedup_workspace_bytes(table, n) bytes, caller-owned;
  *                     its contents are scratch (undefined after the call).
@@ -242,7 +247,8 @@ cp_status cp_lookup_decode_dedup(const cp_table *table, const int64_t *ids, uint
  * result as cp_lookup_decode_dedup, with its scratch (hash table, staging
  * area) in a fixed device array that the library holds on each device it
  * runs on until the process ends (about 16.8 MB per device, enough for
- * CP_DEDUP_NOALLOC_MAX_IDS lookups of any supported record size). The call
+ * CP_DEDUP_NOALLOC_MAX_IDS lookups of any supported record size, single- or
+ * mixed-rate). The call
  * allocates nothing: no hipMalloc, no hipFree, no memset; it launches kernels
  * on `stream` only (the first call on a device also looks up the array's
  * address once).
@@ -251,7 +257,7 @@ cp_status cp_lookup_decode_dedup(const cp_table *table, const int64_t *ids, uint
  * contents: calls that overlap on one device (concurrent streams or host
  * threads) race and give undefined rows; serialise them.
  * Errors: INVALID_ARGUMENT (as cp_lookup_decode_dedup, or n above
- * CP_DEDUP_NOALLOC_MAX_IDS), UNSUPPORTED (a mixed-rate table), HIP. */
+ * CP_DEDUP_NOALLOC_MAX_IDS), HIP. */
 cp_status cp_lookup_decode_dedup_noalloc(const cp_table *table, const int64_t *ids, uint64_t n, uint16_t *out,
                                          void *stream);
 

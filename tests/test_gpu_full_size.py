@@ -16,7 +16,7 @@ import torch
 import oracle
 import trellis_coded_row_amd as cp
 import workload
-from parity import assert_scaled_matches, check_lookup, make_table, say
+from parity import assert_scaled_matches, check_lookup, device_lookup, make_table, say
 
 pytestmark = pytest.mark.gpu
 
@@ -146,6 +146,32 @@ def test_mixed_d512_replay():
         for r in (0, 12_345_678, cfg.rows - 1):
             assert t.record_range(r) == (int(off[r]), int(off[r + 1] - off[r]))
         check_mixed(t, cfg.d, kvs, cls, packed, cfg.ids(), "mixed_d512 zipf replay", offsets=off)
+        say("mixed_d512 zipf replay, each distinct record fetched once")
+        exp, _ = oracle.lookup_decode_mixed(LUT, packed, cfg.d, kvs, cls, cfg.ids(), offsets=off)
+        got = device_lookup(t, cfg.ids(), dedup=True)
+        assert t.check()
+        assert_scaled_matches(got, exp, "mixed_d512 zipf replay, dedup")
+    finally:
+        t.close()
+
+
+def test_host_mixed_d512_replay_dedup():
+    """The same mixed-rate table in pinned host memory, the replay with each
+    distinct record fetched once over PCIe, against the oracle."""
+    from test_gpu_mixed import make_mixed
+
+    cfg = workload.CONFIGS["host_mixed_d512"]
+    kvs = cfg.extra["kv_of_class"]
+    say("building the 97,690,000-row mixed-rate table in pinned host memory")
+    cls = workload.rank_classes(cfg.rows, cfg.ids_seed, cfg.extra["shares"])
+    packed = workload.random_mixed_records(cfg.d, kvs, cls, cfg.table_seed)
+    off = oracle.mixed_offsets(cfg.d, kvs, cls)
+    t = make_mixed(cfg.d, kvs, cls, packed, residency=cp.CP_RESIDENCY_HOST_MAPPED, chunk=1 << 24)
+    try:
+        exp, _ = oracle.lookup_decode_mixed(LUT, packed, cfg.d, kvs, cls, cfg.ids(), offsets=off)
+        got = device_lookup(t, cfg.ids(), dedup=True)
+        assert t.check()
+        assert_scaled_matches(got, exp, "host_mixed_d512 zipf replay, dedup")
     finally:
         t.close()
 

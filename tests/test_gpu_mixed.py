@@ -105,17 +105,49 @@ def test_mixed_host_resident():
     t.close()
 
 
-def test_mixed_dedup_is_unsupported():
-    d, kvs = 64, (4, 3)
-    cls = np.zeros(64, dtype=np.uint8)
-    t = cp.MixedTable(d, kvs, cls, LUT)
-    assert t.dedup_workspace_bytes(10) == 0
-    ids = torch.zeros(4, dtype=torch.int64, device="cuda")
-    out = torch.empty((4, d), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
-    assert cp.cp_lookup_decode_dedup(t.handle, ids.data_ptr(), 4, out.data_ptr(), ws.data_ptr(), 1 << 20,
-                                     None) == cp.CP_ERR_UNSUPPORTED
-    t.close()
+@pytest.mark.parametrize("d,kvs,host", [(64, (4, 3), False), (128, (6, 5, 4, 3), True), (256, (3, 6), False),
+                                         (512, (6, 4, 3), False), (512, (5,), True)])
+def test_mixed_dedup_matches_oracle(d, kvs, host):
+    """Each distinct record fetched once (cp_lookup_decode_dedup on a
+    mixed-rate table): rows against the oracle and bit-identical to the
+    direct lookup, for batches whose distinct rows span several blocks of 32
+    and several tiles of 8,192 staged rows, heavy repeats, one id, all ids the
+    same, ids outside the table; each batch twice."""
+    rows = 40_009
+    rng = np.random.default_rng(d + 31 * len(kvs) + host)
+    cls = rng.integers(0, len(kvs), size=rows).astype(np.uint8)
+    packed = workload.random_mixed_records(d, kvs, cls, seed=d + 41)
+    t = make_mixed(d, kvs, cls, packed, residency=cp.CP_RESIDENCY_HOST_MAPPED if host else cp.CP_RESIDENCY_DEVICE)
+    try:
+        off = oracle.mixed_offsets(d, kvs, cls)
+        cases = {
+            "zipf": workload.zipf_ids(rows, 30_000, seed=d),
+            "uniform (18,000 distinct)": rng.integers(0, rows, 30_000).astype(np.int64),
+            "one id": np.array([rows - 1], dtype=np.int64),
+            "one row repeated": np.full(777, 12345, dtype=np.int64),
+            "ragged with bad ids": rng.integers(-3, rows + 3, 5_003).astype(np.int64),
+            "all bad": np.array([-1, rows, 2**40], dtype=np.int64),
+        }
+        for label, ids in cases.items():
+            exp, nbad = oracle.lookup_decode_mixed(LUT, packed, d, kvs, cls, ids, offsets=off)
+            direct = device_lookup(t, ids)
+            assert t.check() == (nbad == 0)
+            for rep in range(2):
+                say(f"mixed dedup d{d} {kvs} {'host' if host else 'hbm'}: {label}, n={ids.size}, run {rep}")
+                got = device_lookup(t, ids, dedup=True)
+                assert t.check() == (nbad == 0), label
+                assert_scaled_matches(got, exp, f"mixed dedup {label}")
+                assert_bit_exact(got, direct, f"mixed dedup vs direct {label}")
+        assert t.dedup_workspace_bytes(30_000) > 0
+        # a workspace one byte short is refused
+        ids = torch.zeros(4, dtype=torch.int64, device="cuda")
+        out = torch.empty((4, d), dtype=torch.bfloat16, device="cuda")
+        need = t.dedup_workspace_bytes(4)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        assert cp.cp_lookup_decode_dedup(t.handle, ids.data_ptr(), 4, out.data_ptr(), ws.data_ptr(), need - 1,
+                                         None) == cp.CP_ERR_INVALID_ARGUMENT
+    finally:
+        t.close()
 
 
 @pytest.mark.parametrize("d,kvs", [(64, (6, 5, 4, 3)), (128, (3, 5)), (512, (6, 4, 3))])

@@ -107,6 +107,9 @@ def test_random_mixed_rate(case):
             got = device_lookup(t, ids)
             assert t.check() == (nbad == 0), label
             assert_scaled_matches(got, exp, f"{label} rows run {rep}")
+            got_d = device_lookup(t, ids, dedup=True)
+            assert t.check() == (nbad == 0), label
+            assert_bit_exact(got_d, got, f"{label} dedup run {rep}")
     finally:
         t.close()
 

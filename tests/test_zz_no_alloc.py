@@ -69,6 +69,31 @@ def test_noalloc_dedup_matches_the_workspace_dedup(d, kv, residency):
         t.close()
 
 
+@pytest.mark.parametrize("d,kvs", [(512, (6, 5, 4, 3)), (128, (3, 6))])
+def test_noalloc_dedup_of_a_mixed_rate_table(d, kvs):
+    rows = 30011
+    cls = np.random.default_rng(d).integers(0, len(kvs), size=rows).astype(np.uint8)
+    packed = workload.random_mixed_records(d, kvs, cls, seed=1400 + d)
+    t = cp.MixedTable(d, kvs, cls, LUT)
+    try:
+        t.upload_bytes(packed, 0, rows)
+        big = workload.zipf_ids(rows, cp.CP_DEDUP_NOALLOC_MAX_IDS, seed=d + 1)
+        big[5] = -1
+        small = workload.uniform_ids(rows, 3001, seed=d + 2)
+        for label, ids, bad in (("largest batch", big, 1), ("smaller batch after it", small, 0)):
+            say(f"no-alloc dedup, mixed d={d} rates={kvs}: {label}, n={ids.size}")
+            got = noalloc(t, ids)
+            assert t.check() == (bad == 0)
+            ref = with_workspace(t, ids)
+            assert t.check() == (bad == 0)
+            assert_bit_exact(got, ref, f"no-alloc vs workspace dedup (mixed), {label}")
+            exp, nbad = oracle.lookup_decode_mixed(LUT, packed, d, kvs, cls, ids)
+            assert nbad == bad
+            assert_scaled_matches(got, exp, f"no-alloc vs oracle (mixed), {label}")
+    finally:
+        t.close()
+
+
 def test_noalloc_dedup_refuses_batches_above_the_limit():
     d, kv, rows = 64, 4, 100
     t = make_table(LUT, workload.random_records(rows, d, kv, seed=3), d, kv)

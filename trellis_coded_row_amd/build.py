@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "cp_decode.hip"), os.path.join(CSRC, "cp_dedup.hip"),
            os.path.join(CSRC, "cp_encode.hip"), os.path.join(CSRC, "cp_mixed.hip"),
-           os.path.join(CSRC, "cp_shard.hip"), os.path.join(CSRC, "cp_api.hip")]
+           os.path.join(CSRC, "cp_shard.hip"), os.path.join(CSRC, "cp_dedup_mixed.hip"),
+           os.path.join(CSRC, "cp_api.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, "cp_internal.h"), os.path.join(CSRC, "cp_lane.h"),
                   os.path.join(CSRC, "cp_encode_copies.h"),
                   os.path.join(ROOT, "include", "cp.h")]

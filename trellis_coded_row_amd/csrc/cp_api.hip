@@ -442,10 +442,24 @@ cp_status cp_lookup_decode_raw(const cp_table *t, const int64_t *ids, uint64_t n
     return lookup(t, ids, n, out_fp16, stream, true);
 }
 
+// largest record of a mixed-rate table's classes
+static uint64_t mixed_max_record(const cp_table *t)
+{
+    uint64_t r = 0;
+    for (uint32_t c = 0; c < 4; ++c) r = t->rates.R[c] > r ? t->rates.R[c] : r;
+    return r;
+}
+
+static uint64_t dedup_total_bytes(const cp_table *t, uint64_t n)
+{
+    return t->mixed ? cpk::mixed_dedup_layout(n, mixed_max_record(t), kTailPad).total
+                    : cpk::dedup_layout(n, t->record_bytes, kTailPad).total;
+}
+
 uint64_t cp_dedup_workspace_bytes(const cp_table *t, uint64_t n)
 {
-    if (!t || t->mixed) return 0;
-    return cpk::dedup_layout(n, t->record_bytes, kTailPad).total;
+    if (!t) return 0;
+    return dedup_total_bytes(t, n);
 }
 
 // Shared body of the two dedup entry points: `ws` is device memory of at
@@ -454,6 +468,41 @@ uint64_t cp_dedup_workspace_bytes(const cp_table *t, uint64_t n)
 static cp_status dedup_lookup(const cp_table *t, const int64_t *ids, uint64_t n, uint16_t *out, uint8_t *ws,
                               void *stream)
 {
+    if (t->mixed) {
+        // the distinct records staged as a mixed-rate table of their own,
+        // decoded by staged row with the table's codebook and rates
+        const cpk::MixedDedupLayout M = cpk::mixed_dedup_layout(n, mixed_max_record(t), kTailPad);
+        cpk::MixedDedupArgs d;
+        d.hash.records = t->records_dev;
+        d.hash.rows = t->desc.rows;
+        d.hash.record_bytes = 0;
+        d.hash.ids = ids;
+        d.hash.n = n;
+        d.hash.workspace = ws;
+        d.hash.layout = M.hash;
+        d.hash.num_cus = t->num_cus;
+        d.hash.stream = (hipStream_t)stream;
+        d.layout = M;
+        d.index = t->index_dev;
+        d.rates = t->rates;
+        d.tail_pad = kTailPad;
+        hipError_t e = cpk::mixed_dedup_prepare(d);
+        if (e != hipSuccess) return hip_fail(e);
+        cpk::MixedLaunchArgs m;
+        m.records = ws + M.staging;
+        m.rows = n;  // staged rows are numbered below the batch size
+        m.lut = t->lut_dev;
+        m.ids = reinterpret_cast<const int64_t *>(ws + M.hash.staged_ids);
+        m.n = n;
+        m.out = reinterpret_cast<uint32_t *>(out);
+        m.err = t->err_dev;
+        m.index = reinterpret_cast<const cpk::MixedEntry *>(ws + M.index);
+        m.rates = t->rates;
+        m.num_cus = t->num_cus;
+        m.stream = (hipStream_t)stream;
+        e = cpk::launch_mixed(t->desc.d, false, m);
+        return e == hipSuccess ? CP_OK : hip_fail(e);
+    }
     const cpk::DedupLayout L = cpk::dedup_layout(n, t->record_bytes, kTailPad);
     cpk::DedupArgs d;
     d.records = t->records_dev;
@@ -486,7 +535,6 @@ static cp_status dedup_check(const cp_table *t, const int64_t *ids, uint64_t n, 
 {
     if (!ids || !out || ((uintptr_t)out & 15u) || ((uintptr_t)ids & 7u)) return CP_ERR_INVALID_ARGUMENT;
     if (n > 0x7FFFFFFFull) return CP_ERR_INVALID_ARGUMENT;  // staging indices are 32-bit
-    if (t->mixed) return CP_ERR_UNSUPPORTED;
     return CP_OK;
 }
 
@@ -497,8 +545,8 @@ cp_status cp_lookup_decode_dedup(const cp_table *t, const int64_t *ids, uint64_t
     if (n == 0) return CP_OK;
     const cp_status st = dedup_check(t, ids, n, out);
     if (st != CP_OK) return st;
-    const cpk::DedupLayout L = cpk::dedup_layout(n, t->record_bytes, kTailPad);
-    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total) return CP_ERR_INVALID_ARGUMENT;
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < dedup_total_bytes(t, n))
+        return CP_ERR_INVALID_ARGUMENT;
     DeviceGuard guard(t->device);
     if (guard.err != hipSuccess) return hip_fail(guard.err);
     return dedup_lookup(t, ids, n, out, static_cast<uint8_t *>(workspace), stream);
@@ -516,6 +564,9 @@ cp_status cp_lookup_decode_dedup(const cp_table *t, const int64_t *ids, uint64_t
 static constexpr uint64_t kNoallocMaxRecordBytes = 194;
 static constexpr uint64_t kNoallocScratchBytes =
     cpk::dedup_layout(CP_DEDUP_NOALLOC_MAX_IDS, kNoallocMaxRecordBytes, kTailPad).total;
+static_assert(cpk::mixed_dedup_layout(CP_DEDUP_NOALLOC_MAX_IDS, kNoallocMaxRecordBytes, kTailPad).total <=
+                  kNoallocScratchBytes,
+              "a mixed-rate table's dedup workspace fits the no-allocation scratch");
 static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
 
 // Device address of `scratch` on the current device, looked up once per
@@ -548,7 +599,7 @@ cp_status cp_lookup_decode_dedup_noalloc(const cp_table *t, const int64_t *ids, 
     const cp_status st = dedup_check(t, ids, n, out);
     if (st != CP_OK) return st;
     if (n > CP_DEDUP_NOALLOC_MAX_IDS) return CP_ERR_INVALID_ARGUMENT;
-    if (cpk::dedup_layout(n, t->record_bytes, kTailPad).total > kNoallocScratchBytes)
+    if (dedup_total_bytes(t, n) > kNoallocScratchBytes)
         return CP_ERR_INVALID_ARGUMENT;  // not reached: every supported record fits
     DeviceGuard guard(t->device);
     if (guard.err != hipSuccess) return hip_fail(guard.err);

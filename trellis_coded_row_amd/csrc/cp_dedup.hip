@@ -210,7 +210,14 @@ __global__ __launch_bounds__(256) void dedup_resolve(const uint32_t *__restrict_
     }
 }
 
-hipError_t dedup_prepare(const DedupArgs &a)
+static unsigned dedup_grid(uint64_t items, uint64_t per_block, int num_cus)
+{
+    const uint64_t b = (items + per_block - 1) / per_block;
+    const uint64_t cap = (uint64_t)(num_cus > 0 ? num_cus : 256) * 8;
+    return (unsigned)(b < 1 ? 1 : (b > cap ? cap : b));
+}
+
+hipError_t dedup_hash(const DedupArgs &a, uint8_t *pad, uint64_t pad_bytes)
 {
     const DedupLayout &L = a.layout;
     uint8_t *ws = a.workspace;
@@ -218,26 +225,31 @@ hipError_t dedup_prepare(const DedupArgs &a)
     uint32_t *sidx = reinterpret_cast<uint32_t *>(ws + L.sidx);
     uint32_t *slot_of = reinterpret_cast<uint32_t *>(ws + L.slot_of);
     int64_t *uniq = reinterpret_cast<int64_t *>(ws + L.uniq);
+    unsigned long long *count = reinterpret_cast<unsigned long long *>(ws + L.count);
+    hipLaunchKernelGGL(dedup_clear, dim3(dedup_grid(L.slots, 256, a.num_cus)), dim3(256), 0, a.stream, keys, L.slots,
+                       count, pad, pad_bytes);
+    hipLaunchKernelGGL(dedup_insert, dim3(dedup_grid(a.n, kTile, a.num_cus)), dim3(256), 0, a.stream, a.ids, a.n,
+                       a.rows, keys, sidx, L.slots - 1, slot_of, uniq, count);
+    return hipGetLastError();
+}
+
+hipError_t dedup_prepare(const DedupArgs &a)
+{
+    const DedupLayout &L = a.layout;
+    uint8_t *ws = a.workspace;
+    uint32_t *sidx = reinterpret_cast<uint32_t *>(ws + L.sidx);
+    uint32_t *slot_of = reinterpret_cast<uint32_t *>(ws + L.slot_of);
+    int64_t *uniq = reinterpret_cast<int64_t *>(ws + L.uniq);
     int64_t *staged = reinterpret_cast<int64_t *>(ws + L.staged_ids);
     unsigned long long *count = reinterpret_cast<unsigned long long *>(ws + L.count);
     uint8_t *staging = ws + L.staging;
-    const int cus = a.num_cus > 0 ? a.num_cus : 256;
-    auto grid = [&](uint64_t items, uint64_t per_block) {
-        uint64_t b = (items + per_block - 1) / per_block;
-        const uint64_t cap = (uint64_t)cus * 8;
-        return (unsigned)(b < 1 ? 1 : (b > cap ? cap : b));
-    };
-    uint8_t *pad = staging + a.n * L.slot_bytes;
-    const uint64_t pad_bytes = L.total - L.staging - a.n * L.slot_bytes;
-    hipLaunchKernelGGL(dedup_clear, dim3(grid(L.slots, 256)), dim3(256), 0, a.stream, keys, L.slots, count, pad,
-                       pad_bytes);
-    hipLaunchKernelGGL(dedup_insert, dim3(grid(a.n, kTile)), dim3(256), 0, a.stream, a.ids, a.n, a.rows, keys,
-                       sidx, L.slots - 1, slot_of, uniq, count);
+    hipError_t e = dedup_hash(a, staging + a.n * L.slot_bytes, L.total - L.staging - a.n * L.slot_bytes);
+    if (e != hipSuccess) return e;
     const uint32_t units = dedup_window_units(a.record_bytes);
-    hipLaunchKernelGGL(dedup_gather, dim3(grid(a.n * units, 256)), dim3(256), 0, a.stream, a.records,
-                       a.record_bytes, uniq, count, staging, a.n, units, L.slot_bytes);
-    hipLaunchKernelGGL(dedup_resolve, dim3(grid(a.n, 256)), dim3(256), 0, a.stream, slot_of, a.n, sidx, uniq,
-                       a.record_bytes, L.slot_bytes, staged);
+    hipLaunchKernelGGL(dedup_gather, dim3(dedup_grid(a.n * units, 256, a.num_cus)), dim3(256), 0, a.stream,
+                       a.records, a.record_bytes, uniq, count, staging, a.n, units, L.slot_bytes);
+    hipLaunchKernelGGL(dedup_resolve, dim3(dedup_grid(a.n, 256, a.num_cus)), dim3(256), 0, a.stream, slot_of, a.n,
+                       sidx, uniq, a.record_bytes, L.slot_bytes, staged);
     return hipGetLastError();
 }
 

@@ -104,6 +104,11 @@ constexpr DedupLayout dedup_layout(uint64_t n, uint64_t record_bytes, uint64_t t
 // it, staged_ids[j] is the byte offset of lookup j's record in the staging
 // area (or -1 for a bad id).
 hipError_t dedup_prepare(const DedupArgs &a);
+// The hash step alone (clear, insert): afterwards uniq[0 .. *count) are the
+// distinct valid ids in a fixed order, sidx[slot] the index in uniq of the
+// id in hash slot `slot`, and slot_of[j] lookup j's slot (0xFFFFFFFF for an
+// id outside [0, rows)); pad[0 .. pad_bytes) is zeroed.
+hipError_t dedup_hash(const DedupArgs &a, uint8_t *pad, uint64_t pad_bytes);
 
 // Launch parameters of one encode call (see cp_encode.hip).
 struct EncodeArgs {
@@ -164,6 +169,54 @@ int mixed_index_build(const uint8_t *row_class, uint64_t rows, uint32_t nclass, 
                       MixedEntry *index, uint64_t *total_bytes);
 // Byte offset (and class) of a row's record, from a host copy of the index.
 uint64_t mixed_record_offset(const MixedEntry *index, const uint32_t R[4], uint64_t row, uint32_t *cls);
+
+// Dedup lookups on a mixed-rate table (see cp_dedup_mixed.hip). Workspace:
+// the hash regions of a single-rate dedup (keys, sidx, slot_of, uniq, count;
+// staged_ids holds each lookup's staged row), then a mixed-rate index over
+// the staged rows (16 bytes per 32), the record bytes per 32 staged rows and
+// per tile of kMixedDedupTile such blocks, and the staging area: the distinct
+// records packed in staged order (at most n of the largest record, plus the
+// tail pad), each region 256-byte aligned.
+constexpr uint32_t kMixedDedupTile = 8;  // blocks of 32 staged rows per tile (one 256-thread workgroup)
+
+struct MixedDedupLayout {
+    DedupLayout hash;  // staging and slot_bytes unused
+    uint64_t blocks, tiles;
+    uint64_t index, bsum, tsum, staging, total;
+};
+
+constexpr MixedDedupLayout mixed_dedup_layout(uint64_t n, uint64_t max_record_bytes, uint64_t tail_pad)
+{
+    MixedDedupLayout M{};
+    M.hash = dedup_layout(n, 0, 0);
+    M.blocks = (n + 31) / 32;
+    M.tiles = (M.blocks + kMixedDedupTile - 1) / kMixedDedupTile;
+    uint64_t off = M.hash.staging;  // the single-rate staging area is not used
+    M.index = off;
+    off = dedup_align256(off + 16 * M.blocks);
+    M.bsum = off;
+    off = dedup_align256(off + 8 * M.blocks);
+    M.tsum = off;
+    off = dedup_align256(off + 8 * M.tiles);
+    M.staging = off;
+    off = dedup_align256(off + n * max_record_bytes + tail_pad);
+    M.total = off;
+    return M;
+}
+
+struct MixedDedupArgs {
+    DedupArgs hash;  // records (the table's), rows, ids, n, workspace, num_cus, stream; layout = M.hash
+    MixedDedupLayout layout;
+    const MixedEntry *index;  // the table's index (device)
+    MixedRates rates;
+    uint64_t tail_pad;
+};
+
+// Stages each distinct record of the batch once; afterwards the staging area
+// holds a mixed-rate table of the staged rows, indexed by the workspace's
+// own index, and staged_ids[j] is lookup j's staged row (-1 for a bad id),
+// ready for the mixed-rate decode kernel.
+hipError_t mixed_dedup_prepare(const MixedDedupArgs &a);
 
 // Row-sharded tables (see cp_shard.hip): the requester's plan, a stable
 // counting sort of its ids by owning shard (owner of row i =

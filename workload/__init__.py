@@ -340,6 +340,10 @@ CONFIGS["mixed_d512"] = TableConfig(
     description="97,690,000 x d512 mixed-rate table: rows coded at 3 / 2.5 / 2 / 1.5 bits per element "
                 "by Zipf access rank (5% / 15% / 30% / 50% of rows), ~11.5 GB in HBM; the Zipf(1.1) replay",
     extra={"kv_of_class": MIXED_KV, "shares": MIXED_SHARES})
+CONFIGS["host_mixed_d512"] = TableConfig(
+    "host_mixed_d512", 97_690_000, 512, 0, 104, "zipf", REPLAY_IDS, 202, encoded_rows=0, host_resident=True,
+    description="the mixed-rate d512 table (mixed_d512) in pinned host memory, read over PCIe",
+    extra={"kv_of_class": MIXED_KV, "shares": MIXED_SHARES})
 for _kv in (3, 4, 5, 6):
     CONFIGS[f"rate_d512_kv{_kv}"] = TableConfig(
         f"rate_d512_kv{_kv}", 1 << 22, 512, _kv, 103, "zipf", REPLAY_IDS, 203,
