@@ -150,6 +150,27 @@ def test_mixed_dedup_matches_oracle(d, kvs, host):
         t.close()
 
 
+def test_mixed_dedup_beyond_one_pass_of_the_staging_grid():
+    """More distinct rows than one pass of the staging copy's capped grid
+    (32 workgroups of 4 waves per CU, 16 records a wave: 524,288 on 256 CUs)
+    and than one round of the tile scan cover (d = 64, four rates)."""
+    d, kvs, rows = 64, (6, 5, 4, 3), 2_000_003
+    rng = np.random.default_rng(77)
+    cls = rng.integers(0, len(kvs), size=rows).astype(np.uint8)
+    packed = workload.random_mixed_records(d, kvs, cls, seed=78)
+    t = make_mixed(d, kvs, cls, packed, chunk=1 << 22)
+    try:
+        ids = workload.uniform_ids(rows, 700_001, seed=79)
+        assert np.unique(ids).size > 524_288
+        exp, nbad = oracle.lookup_decode_mixed(LUT, packed, d, kvs, cls, ids)
+        say(f"mixed dedup, {np.unique(ids).size} distinct rows")
+        got = device_lookup(t, ids, dedup=True)
+        assert t.check() and nbad == 0
+        assert_scaled_matches(got, exp, "mixed dedup, 590 K distinct rows")
+    finally:
+        t.close()
+
+
 @pytest.mark.parametrize("d,kvs", [(64, (6, 5, 4, 3)), (128, (3, 5)), (512, (6, 4, 3))])
 def test_mixed_encode_matches_oracle(d, kvs):
     """Rows encoded on the GPU into a mixed-rate table: each row's record equals

@@ -103,6 +103,24 @@ def test_gather_records_matches_the_oracle(d, kv, host):
         t.close()
 
 
+def test_gather_records_beyond_one_pass_of_the_grid():
+    # more records than one pass of the capped grid covers (32 workgroups of 4
+    # waves per CU, 16 records a wave): the group loop strides over the rest
+    d, kv, rows = 64, 3, 1_000_003
+    recs = workload.random_records(rows, d, kv, seed=5150)
+    t = make_table(LUT, recs, d, kv)
+    try:
+        ids = workload.uniform_ids(rows, 700_001, seed=5151)
+        say(f"gather records, n={ids.size}")
+        got = t.gather_records(torch.from_numpy(ids).cuda())
+        torch.cuda.synchronize()
+        R = t.record_bytes
+        assert (got.cpu().numpy()[: ids.size * R].reshape(ids.size, R) == oracle.gather_records(recs, rows, ids)).all()
+        assert t.check()
+    finally:
+        t.close()
+
+
 @pytest.mark.parametrize("d,kv", [(512, 4), (512, 6), (128, 3), (64, 4)])
 def test_staged_decode_matches_the_oracle(d, kv):
     nrec = 4_099
