@@ -392,16 +392,23 @@ __device__ __forceinline__ uint32_t argmin_memory(Shared<KV> &sh, const double *
 
 // Walk of the back-pointers from the next memory `end` after the last step
 // down to step 0, run by one whole wave (every lane follows the same path).
-// Two steps per load latency: while the back-pointer r of step k loads, lane
-// j < BR loads the back-pointer at step k - 1 of the memory that r = j leads
-// to, and r then picks the lane. Returns the memory held after step kw; with
-// `emit` sets each step's kv new bits in the code, without it the walk ends
-// once step kw is reached.
+// Several steps per load latency: while the back-pointer r of step k loads,
+// lane j < BR loads the back-pointer at step k - 1 of the memory that r = j
+// leads to, and (when BR^2 <= 64) lane j * BR + i the back-pointer at step
+// k - 2 of the memory that the choices j at step k and i at step k - 1 lead
+// to; r then picks the lane, and the two choices the lane of the next. Returns the memory held after step kw; with `emit`
+// sets each step's kv new bits in the code, without it the walk ends once
+// step kw is reached.
 template <int KV>
 __device__ __forceinline__ uint32_t walk_back(const uint8_t *bp, uint32_t T, uint32_t end, uint32_t kw, bool emit,
                                               uint8_t *code)
 {
     using P = Tcq<KV>;
+    constexpr uint32_t BR = P::BR;
+    // three steps per load latency when the BR^2 step k - 2 loads take one per
+    // lane (kv 3); four a lane (kv 4) measured slower than two steps
+    constexpr bool DEEP = BR * BR <= 64;
+    constexpr uint32_t PER = 1;  // step k - 2 loads per lane
     const uint32_t lane = threadIdx.x & 63u;
     uint32_t m2 = end, w = 0;
     auto step = [&](uint32_t k, uint32_t r) {
@@ -417,14 +424,36 @@ __device__ __forceinline__ uint32_t walk_back(const uint8_t *bp, uint32_t T, uin
         }
         m2 = s & (P::S - 1);
     };
-    for (int32_t k = (int32_t)T - 1; k >= 0; k -= 2) {
+    auto next = [&](uint32_t m, uint32_t r) { return ((m << KV) | r) & (P::S - 1); };
+    constexpr int32_t STRIDE = DEEP ? 3 : 2;
+    for (int32_t k = (int32_t)T - 1; k >= 0; k -= STRIDE) {
         if (!emit && (uint32_t)k < kw) break;  // step kw is done: w is set
         const uint32_t rk = bp[(uint64_t)k * P::S + bp_pos<KV>(m2)];
         uint32_t cand = 0;
-        if (k >= 1 && lane < P::BR)
-            cand = bp[(uint64_t)(k - 1) * P::S + bp_pos<KV>(((m2 << KV) | lane) & (P::S - 1))];
+        if (k >= 1 && lane < BR) cand = bp[(uint64_t)(k - 1) * P::S + bp_pos<KV>(next(m2, lane))];
+        // pair p = q * 64 + lane: the choices j = p / BR at step k and
+        // i = p % BR at step k - 1
+        uint32_t cand2[PER];
+#pragma unroll
+        for (uint32_t q = 0; q < PER; ++q) {
+            const uint32_t pidx = q * 64 + lane;
+            cand2[q] = 0;
+            if (DEEP && k >= 2 && pidx < BR * BR)
+                cand2[q] = bp[(uint64_t)(k - 2) * P::S + bp_pos<KV>(next(next(m2, pidx / BR), pidx % BR))];
+        }
         step((uint32_t)k, rk);
-        if (k >= 1) step((uint32_t)k - 1, (uint32_t)__shfl((int)cand, (int)rk, 64));
+        if (k >= 1) {
+            const uint32_t rk1 = (uint32_t)__shfl((int)cand, (int)rk, 64);
+            step((uint32_t)k - 1, rk1);
+            if (DEEP && k >= 2) {
+                const uint32_t pidx = rk * BR + rk1;  // wave-uniform
+                uint32_t v = cand2[0];
+#pragma unroll
+                for (uint32_t q = 1; q < PER; ++q)
+                    if (pidx / 64 == q) v = cand2[q];
+                step((uint32_t)k - 2, (uint32_t)__shfl((int)v, (int)(pidx % 64), 64));
+            }
+        }
     }
     return w;
 }
