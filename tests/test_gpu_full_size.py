@@ -189,3 +189,18 @@ def test_host_d512_replay_with_hot_rows(big_records):
         check_lookup(t, LUT, recs, cfg.d, cfg.kv, cfg.ids(), "host_d512 zipf replay, hot rows")
     finally:
         t.close()
+
+
+@pytest.mark.parametrize("kv", [3, 4, 5, 6])
+def test_encode_of_the_benchmark_batch(kv):
+    """The encoder benchmark's batch (4,096 Gaussian rows of d = 512, the
+    benchmark's seed), encoded in the benchmark's launch: every record against
+    the oracle's encoding of the same rows."""
+    from test_gpu_encode import check_records, gpu_encode, oracle_encode
+
+    d, n = 512, 4096
+    e = workload.gaussian_rows(n, d, seed=9100).astype(np.float32)
+    say(f"encode of the benchmark batch, kv={kv}")
+    t, got = gpu_encode(e, d, kv)
+    t.close()
+    check_records(got, oracle_encode(e, d, kv), f"benchmark batch kv{kv}")
