@@ -384,7 +384,9 @@ cp_status cp_shard_plan(const int64_t *ids, uint64_t n, uint64_t rows_per_shard,
  * `dst` (device, 2-byte aligned), packed: record k at bytes [k R, k R + R).
  * An id outside [0, rows) writes a zero record and raises the table's flag
  * (cp_table_check). Rows of a pinned-host table are read over PCIe (its
- * device copies of hot rows hold the same bytes). Asynchronous on `stream`.
+ * device copies of hot rows hold the same bytes). A 16-byte aligned `dst` is
+ * written in whole 16-byte stores only (else each group of 16 records also
+ * has two partial ones). Asynchronous on `stream`.
  * Errors: INVALID_ARGUMENT (NULL table, NULL or misaligned ids / dst),
  * UNSUPPORTED (a mixed-rate table), HIP. */
 cp_status cp_table_gather_records(cp_table *table, const int64_t *ids, uint64_t n, void *dst, void *stream);

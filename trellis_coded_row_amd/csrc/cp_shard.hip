@@ -205,128 +205,159 @@ __global__ __launch_bounds__(kPlanBlock) void shard_scatter(const int64_t *__res
 
 // dst record k = the table's record of row ids[k] (R bytes, 2-byte aligned
 // both sides), or zeros for an id outside [0, rows) (which raises the flag).
-// A wave copies 16 records, the bytes [16 g R, 16 g R + 16 R) of dst:
-//   - each 16-lane row loads one record per pass, four passes with all
-//     loads in flight together: lane l loads the record's aligned source
-//     dwords 4l..4l+3 (one 16-byte load);
-//   - the row writes the record into the wave's LDS area where it sits in
-//     dst relative to a 16-byte boundary, dword by dword: when source and
-//     destination start at different offsets within a dword, a dword takes
-//     one half from the next or previous source dword, which may be the
-//     neighbouring lane's (a row shift), and a dword shared with the next
-//     record gets its own half only (16-bit LDS writes);
-//   - the wave then stores its range from LDS as aligned 16-byte chunks,
-//     half-words only at the range's two ends (shared with the
-//     neighbouring waves' ranges).
-constexpr int kGatherPasses = 4;  // records per row in flight together
-constexpr uint32_t kGatherRecords = 4 * kGatherPasses;  // records per wave
+// A wave copies groups of 16 records, the bytes [16 g R, 16 g R + 16 R) of
+// dst, in two phases with the wave's LDS between them:
+//   - loads: each 16-lane row loads one record per pass, four passes in
+//     flight together; lane l loads the 16 bytes at 16 l from the record's
+//     first aligned dword (lanes past the record's end load its last piece
+//     again) and writes them unchanged to the record's 256-byte LDS slot, so
+//     byte b of record j sits at slot j + b, plus 2 when the record starts
+//     mid-dword (bit j of a per-group mask);
+//   - stores: the range is written as aligned 16-byte chunks; chunk byte 2h
+//     is byte t0 + 2h of the group's records, a half-word read from the slot
+//     of the record it falls in (a chunk touches two records at most, three
+//     when R < 16). Chunks that the range only partly covers (a destination
+//     not 16-byte aligned, the batch's last group) write their half-words
+//     inside it.
+// The loads' pieces go to LDS as they came, so the per-byte work is one
+// half-word read and a select per output half-word: the copy is bound by
+// memory, not by instruction issue.
+constexpr int kGatherPasses = 4;                      // records per row in flight together
+constexpr uint32_t kGatherRecords = 4 * kGatherPasses;  // records per wave group
+constexpr uint32_t kGatherMinR = 14;                  // the smallest record (d 64, 3 bits per step)
 constexpr uint32_t kGatherMaxR = 194;                 // the largest record (d 512, 6 bits per step)
-constexpr uint32_t kGatherStage = (kGatherRecords * kGatherMaxR + 16 + 15) & ~15u;  // staged bytes per wave
-constexpr uint32_t kGatherLds = kGatherStage + 256;  // and a spare dword per lane
+constexpr uint32_t kGatherSlot = 256;                 // LDS bytes per record (16 lanes x 16 bytes)
+constexpr uint32_t kGatherPad = 16;                   // before slot 0: a range's first chunk may start 14 bytes early
+// two spare slots: the last chunk's half-words past the group's records read there
+constexpr uint32_t kGatherWaveLds = kGatherPad + (kGatherRecords + 2) * kGatherSlot;
+static_assert(kGatherMaxR + 15 <= kGatherSlot, "a record's pieces fit its slot");
 // four dwords at a 4-byte aligned address (one 16-byte access on the GPU),
 // and at a 16-byte aligned one
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// SPAN: records a 16-byte chunk can touch (2 for R >= 16, 3 below);
+// BIGROWS: ids of 2^32 rows and more. Rmagic = ceil(2^32 / R): t / R is the
+// high half of t Rmagic for every t below 2^32 / R.
+template <int SPAN, bool BIGROWS>
 __global__ __launch_bounds__(256) void gather_records(const uint8_t *__restrict__ tab, uint64_t rows, uint32_t R,
-                                                      const int64_t *__restrict__ ids, uint64_t n,
+                                                      uint32_t Rmagic, const int64_t *__restrict__ ids, uint64_t n,
                                                       uint8_t *__restrict__ dst, int *__restrict__ err)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t s_stage[4][kGatherLds];
+    __shared__ __attribute__((aligned(16))) uint8_t s_lds[4 * kGatherWaveLds];
     const uint32_t lane = threadIdx.x & 63u, row = lane >> 4, l = lane & 15u;
     const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t wave = (uint64_t)blockIdx.x * 4 + w;
     const uint64_t waves = (uint64_t)gridDim.x * 4;
     const uint64_t ngroups = (n + kGatherRecords - 1) / kGatherRecords;
-    uint8_t *stage = s_stage[w];
+    const uint32_t wbase = w * kGatherWaveLds + kGatherPad;  // slot 0's byte offset in s_lds
+    // this lane's piece of record j (row j % 4, pass j / 4): + (j / 4) 4 slots
+    uint8_t *const mypiece = s_lds + wbase + 16u * lane;
     bool bad = false;
     for (uint64_t g = wave; g < ngroups; g += waves) {
         const uint64_t k0 = g * kGatherRecords;
         const uint32_t cnt = (uint32_t)((n - k0) < kGatherRecords ? (n - k0) : kGatherRecords);
+        const int64_t *gids = ids + k0;
         int64_t id[kGatherPasses];
 #pragma unroll
         for (int p = 0; p < kGatherPasses; ++p) {
             const uint32_t j = 4u * p + row;
-            id[p] = j < cnt ? ids[k0 + j] : 0;
+            id[p] = gids[j < cnt ? j : cnt - 1];
         }
-        u32x4a4 S[kGatherPasses];
-        uint32_t sh[kGatherPasses];
+        // lane j < 16 takes record j's id once more for the group's masks:
+        // which records start mid-dword, which ids are outside the table
+        const int64_t idj = gids[l < cnt ? l : cnt - 1];
+        const bool okj = (uint64_t)idj < rows;
+        const uint64_t offj = (okj ? (uint64_t)idj : 0) * R;
+        const uint32_t shb = (uint32_t)__ballot(((uint32_t)offj & 2u) != 0) & 0xFFFFu;
+        const uint32_t badg = (uint32_t)__ballot(!okj && l < cnt) & 0xFFFFu;
+        bad |= badg != 0;
 #pragma unroll
         for (int p = 0; p < kGatherPasses; ++p) {
-            const uint32_t j = 4u * p + row;
+            // an id outside the table reads record 0 (zeroed below)
             const bool ok = (uint64_t)id[p] < rows;
-            bad |= j < cnt && !ok;
-            const uint8_t *rec = tab + (ok ? (uint64_t)id[p] : 0) * R;
-            sh[p] = (uint32_t)((uintptr_t)rec & 3u);
-            const uint32_t nsrc = (sh[p] + R + 3) >> 2;  // aligned source dwords holding the record
-            // lanes past the record load the record's first 16 bytes again
-            const u32x4a4 *src = reinterpret_cast<const u32x4a4 *>(rec - sh[p]) + (4 * l < nsrc ? l : 0);
-            S[p] = *src;
-            if (!ok || j >= cnt) S[p] = u32x4a4{0, 0, 0, 0};
-        }
-        // the range [start, end) of dst, staged from the 16-byte boundary below start
-        const uint64_t start = (uint64_t)(uintptr_t)dst + k0 * R;
-        const uint32_t o0 = (uint32_t)(start & 15u);  // even
-#pragma unroll
-        for (int p = 0; p < kGatherPasses; ++p) {
-            const uint32_t j = 4u * p + row;
-            const uint32_t at = o0 + j * R;  // the record's first byte in the stage
-            const uint32_t dsh = at & 3u;
-            // the source dwords before and after this lane's four
-            const uint32_t before =
-                (uint32_t)__builtin_amdgcn_update_dpp((int)S[p].w, (int)S[p].w, 0x111 /* row_shr:1 */, 0xF, 0xF, false);
-            const uint32_t after =
-                (uint32_t)__builtin_amdgcn_update_dpp((int)S[p].x, (int)S[p].x, 0x101 /* row_shl:1 */, 0xF, 0xF, false);
-            const uint32_t src6[6] = {before, S[p].x, S[p].y, S[p].z, S[p].w, after};
-            // the lane's eight stage half-words, written without branches: a
-            // half-word outside the record (or of a record past the batch)
-            // goes to the lane's spare dword after the stage instead
-            const int r0 = 16 * (int)l - (int)dsh;  // record byte at this lane's first stage byte
-            const uint32_t q = (at - dsh) + 16u * l;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                // stage dword 4l+m starts at source byte 4(4l+m) + sh - dsh
-                const uint32_t D = sh[p] == dsh ? src6[m + 1]
-                                   : sh[p] > dsh ? (src6[m + 1] >> 16) | (src6[m + 2] << 16)
-                                                 : (src6[m] >> 16) | (src6[m + 1] << 16);
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int r = r0 + 4 * m + 2 * e;
-                    const bool in = j < cnt && r >= 0 && r < (int)R;
-                    *reinterpret_cast<uint16_t *>(stage + (in ? q + 4u * m + 2u * e : kGatherStage + 4u * lane)) =
-                        (uint16_t)(D >> (16 * e));
-                }
-            }
+            uint64_t off;
+            if constexpr (BIGROWS) off = (ok ? (uint64_t)id[p] : 0) * R;
+            else off = (uint64_t)(ok ? (uint32_t)id[p] : 0u) * R;
+            const uint32_t sh = (uint32_t)off & 2u;  // records are 2-byte aligned
+            const uint32_t lastoff = (sh + R - 1) & ~15u;
+            const uint32_t loff = 16u * l < lastoff ? 16u * l : lastoff;
+            const u32x4a4 S = *reinterpret_cast<const u32x4a4 *>(tab + (off - sh) + loff);
+            *reinterpret_cast<u32x4 *>(mypiece + 4u * p * kGatherSlot) = (u32x4)S;
         }
         // the wave's LDS writes before its reads (one wave: in order once issued)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint32_t last = o0 + cnt * R;  // stage offset of end
+        // the range [start, end) of dst, from the 16-byte boundary below start
+        const uint64_t start = (uint64_t)(uintptr_t)dst + k0 * R;
+        const uint32_t o0 = (uint32_t)(start & 15u);  // even
+        const uint32_t last = o0 + cnt * R;
         const uint32_t chunks = (last + 15) >> 4;
-        uint8_t *base = dst + k0 * R - o0;
-        for (uint32_t c = lane; c < chunks; c += 64) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + 16u * c);
-            const uint32_t c0 = 16u * c;
-            if (c0 >= o0 && c0 + 16 <= last) {
-                *reinterpret_cast<u32x4 *>(base + c0) = v;
-            } else {
-                // a chunk at an end of the range: its half-words inside it
+        uint8_t *const base = dst + k0 * R - o0;
+        // LDS offsets of chunk byte 0 as read from records j0, j0 + 1 and
+        // j0 + 2 (b0: the chunk's first byte in record j0; may be negative for
+        // a range's first chunk), and the half-word read for chunk byte 2h
+        auto chunk_bytes = [&](uint32_t j0, int32_t b0) -> u32x4 {
+            uint32_t a0 = wbase + j0 * kGatherSlot + 2u * ((shb >> j0) & 1u) + (uint32_t)b0;
+            uint32_t a1 = wbase + (j0 + 1) * kGatherSlot + 2u * ((shb >> (j0 + 1)) & 1u) + (uint32_t)b0 - R;
+            uint32_t a2 = 0;
+            if constexpr (SPAN == 3)
+                a2 = wbase + (j0 + 2) * kGatherSlot + 2u * ((shb >> (j0 + 2)) & 1u) + (uint32_t)b0 - 2 * R;
+            // kept apart, so that each half-word's address is one select
+            asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2));
+            const int32_t e1 = (int32_t)R - b0;  // chunk bytes below e1 are record j0's
+            uint32_t hw[8];
 #pragma unroll
-                for (int h = 0; h < 8; ++h) {
-                    const uint32_t b = c0 + 2u * h;
-                    const uint32_t word = h < 2 ? v.x : h < 4 ? v.y : h < 6 ? v.z : v.w;
-                    if (b >= o0 && b < last)
-                        *reinterpret_cast<uint16_t *>(base + b) = (uint16_t)(word >> (16 * (h & 1)));
+            for (int h = 0; h < 8; ++h) {
+                uint32_t a = 2 * h < e1 ? a0 : a1;
+                if constexpr (SPAN == 3) a = 2 * h < e1 + (int32_t)R ? a : a2;
+                hw[h] = *reinterpret_cast<const uint16_t *>(s_lds + a + 2 * h);
+            }
+            return u32x4{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16)};
+        };
+        if (o0 == 0 && cnt == kGatherRecords) {
+            // a whole group from a 16-byte boundary: R whole chunks
+            for (uint32_t c = lane; c < chunks; c += 64) {
+                const uint32_t t0 = 16u * c;
+                const uint32_t j0 = (uint32_t)(((uint64_t)t0 * Rmagic) >> 32);
+                *reinterpret_cast<u32x4 *>(base + t0) = chunk_bytes(j0, (int32_t)(t0 - j0 * R));
+            }
+        } else {
+            for (uint32_t c = lane; c < chunks; c += 64) {
+                const int32_t t0 = (int32_t)(16u * c) - (int32_t)o0;
+                const uint32_t j0 = (uint32_t)(((uint64_t)(uint32_t)(t0 > 0 ? t0 : 0) * Rmagic) >> 32);
+                const u32x4 v = chunk_bytes(j0, t0 - (int32_t)(j0 * R));
+                const uint32_t c0 = 16u * c;
+                if (c0 >= o0 && c0 + 16 <= last) {
+                    *reinterpret_cast<u32x4 *>(base + c0) = v;
+                } else {
+                    // a chunk at an end of the range: its half-words inside it
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) {
+                        const uint32_t b = c0 + 2u * h;
+                        const uint32_t word = h < 2 ? v.x : h < 4 ? v.y : h < 6 ? v.z : v.w;
+                        if (b >= o0 && b < last)
+                            *reinterpret_cast<uint16_t *>(base + b) = (uint16_t)(word >> (16 * (h & 1)));
+                    }
                 }
             }
+        }
+        if (__builtin_expect(badg != 0, 0)) {
+            // records of ids outside the table are zeros: written once this
+            // group's stores have completed (same addresses)
+            __builtin_amdgcn_s_waitcnt(0);
+            for (uint32_t j = 0; j < kGatherRecords; ++j)
+                if ((badg >> j) & 1u)
+                    for (uint32_t b = 2u * lane; b < R; b += 128)
+                        *reinterpret_cast<uint16_t *>(dst + (k0 + j) * R + b) = 0;
         }
         // this group's LDS reads before the next group's writes
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    if (bad) atomicOr(err, 1);
+    if (bad && lane == 0) atomicOr(err, 1);
 }
 
 }  // namespace
@@ -372,13 +403,20 @@ hipError_t gather_records_launch(const uint8_t *records, uint64_t rows, uint64_t
                                  uint8_t *dst, int *err, int num_cus, hipStream_t stream)
 {
     if (n == 0) return hipSuccess;
-    if (R > kGatherMaxR || (R & 1u)) return hipErrorInvalidValue;
+    if (R < kGatherMinR || R > kGatherMaxR || (R & 1u)) return hipErrorInvalidValue;
+    const uint32_t r = (uint32_t)R;
+    const uint32_t magic = (uint32_t)(((1ull << 32) + r - 1) / r);
     // one wave per 16 records, at most 32 workgroups of 4 waves per CU (the
     // group loop strides over the rest)
     const uint64_t cap = (uint64_t)(num_cus > 0 ? num_cus : 256) * 32;
     const uint64_t blocks = ((n + kGatherRecords - 1) / kGatherRecords + 3) / 4;
-    hipLaunchKernelGGL(gather_records, dim3((unsigned)(blocks < cap ? blocks : cap)), dim3(256), 0, stream, records,
-                       rows, (uint32_t)R, ids, n, dst, err);
+    const dim3 grid((unsigned)(blocks < cap ? blocks : cap));
+    typedef void (*gather_fn)(const uint8_t *, uint64_t, uint32_t, uint32_t, const int64_t *, uint64_t, uint8_t *,
+                              int *);
+    const bool big = rows > 0xFFFFFFFFull;
+    const gather_fn fn = r >= 16 ? (big ? gather_records<2, true> : gather_records<2, false>)
+                                 : (big ? gather_records<3, true> : gather_records<3, false>);
+    hipLaunchKernelGGL(fn, grid, dim3(256), 0, stream, records, rows, r, magic, ids, n, dst, err);
     return hipGetLastError();
 }
 
