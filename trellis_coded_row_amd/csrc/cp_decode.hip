@@ -100,8 +100,9 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
     // the first chunk's ids are requested before the codebook is staged, so
     // the two loads' latencies overlap (what a small batch waits for)
     int64_t my_id = load_id(wave);
-    // Workgroups of the first residency round (blockIdx < gen: one workgroup
-    // per CU) also read the ids, and touch the record lines, of the chunks
+    // Workgroups of the first residency round (blockIdx < gen: the
+    // workgroups one CU holds, times the CUs) also read the ids, and touch
+    // the record lines, of the chunks
     // that workgroups gen, 2 gen, ... later take with the same wave index (up
     // to kPrefetchRounds rounds). Those run on the same XCD (workgroups are
     // dealt to the XCDs in turn, and gen is a multiple of their count), so
@@ -292,27 +293,32 @@ __global__ __launch_bounds__(BLOCK) void gather_decode(const uint8_t *__restrict
 // dispatch
 // ---------------------------------------------------------------------------
 
-// Launch shape (measured on MI355X, d = 512 replay): 1024-thread workgroups
-// with the codebook in LDS as 16 copies x 2 signs (64 KB); one wave holds a
-// chunk of up to 16 lookups (fewer for small batches, lookup_chunk_rows); the
-// grid covers all chunks (no persistent cap), which balances the tail better
-// than a fixed number of workgroups per CU. How many workgroups a CU runs at
-// once depends on the instance's registers: the d = 512 kernels hold 16 rows'
-// record offsets and scales in SGPRs, which leaves room for one 1024-thread
-// workgroup per CU (16 waves), the next one starting as its waves retire.
+// Launch shape (measured on MI355X, d = 512 replay): the codebook in LDS as
+// 16 copies x 2 signs (64 KB); one wave holds a chunk of up to 16 lookups
+// (fewer for small batches, lookup_chunk_rows); the grid covers all chunks
+// (no persistent cap), which balances the tail better than a fixed number of
+// workgroups per CU. A CU runs 16 waves: one 1024-thread workgroup, or two of
+// 512 (the LDS holds two codebooks), which run out of step: one decodes and
+// writes while the other waits for its records. Two of 512 are faster for the
+// touch-ahead kernels (warm and cold: 72.6 / 79.0 against 73.1 / 80.2 us at
+// kv 4, 69.3 / 76.7 against 75.7 / 86.8 at kv 3) and for the default kernels
+// at kv 4 (69.2 against 69.9 us warm, cold the same; 35.2 against 38.0 at
+// d = 256); one of 1024 for the default kernels at kv 3, 5 and 6 (cold 99-101
+// against 107-109 us), the host-table kernels and the mixed-rate kernel.
 template <int D, int KV, bool RAW, bool HOT, bool AHEAD, int CHUNK_ROWS>
 static hipError_t launch_shape(const LaunchArgs &a)
 {
     constexpr int GROUPS = 64 / (D / 8);
     // lookups per wave chunk: a multiple of the rows decoded side by side, <= 64
     constexpr int CHUNK = (CHUNK_ROWS / GROUPS > 0 ? CHUNK_ROWS / GROUPS : 1) * GROUPS;
+    constexpr int BLOCK = (AHEAD || (KV == 4 && !HOT)) ? kBlockPair : kBlock;
     const uint64_t nchunks = (a.n + CHUNK - 1) / CHUNK;
-    uint64_t blocks = (nchunks + kBlock / 64 - 1) / (kBlock / 64);
+    uint64_t blocks = (nchunks + BLOCK / 64 - 1) / (BLOCK / 64);
     if (blocks > 0x7FFFFFFFull) blocks = 0x7FFFFFFFull;  // the chunk loop strides over any excess
-    // workgroups of one residency round: one per CU
-    const uint32_t gen = (uint32_t)(a.num_cus > 0 ? a.num_cus : 256);
-    hipLaunchKernelGGL((gather_decode<D, KV, RAW, kCopies, kBlock, CHUNK, HOT, AHEAD>), dim3((unsigned)blocks),
-                       dim3(kBlock), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err, a.by_offset,
+    // workgroups of one residency round
+    const uint32_t gen = (uint32_t)(a.num_cus > 0 ? a.num_cus : 256) * (uint32_t)(kBlock / BLOCK);
+    hipLaunchKernelGGL((gather_decode<D, KV, RAW, kCopies, BLOCK, CHUNK, HOT, AHEAD>), dim3((unsigned)blocks),
+                       dim3(BLOCK), 0, a.stream, a.records, a.rows, a.lut, a.ids, a.n, a.out, a.err, a.by_offset,
                        a.hot_index, a.host_off0, a.hot_off0, gen);
     return hipGetLastError();
 }

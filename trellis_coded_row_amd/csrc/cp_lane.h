@@ -10,9 +10,12 @@
 namespace cpk {
 
 // Launch shape of the gather-decode kernels (measured on MI355X, d = 512
-// replay): 1024-thread workgroups, the codebook in LDS as 16 copies per sign,
-// wave chunks of up to 16 lookups.
+// replay): the codebook in LDS as 16 copies per sign (64 KB), wave chunks of
+// up to 16 lookups, workgroups of 1024 threads or, for the instances where
+// that measured faster, two workgroups of 512 per CU (the LDS holds two
+// codebooks; 16 waves per CU either way).
 constexpr int kBlock = 1024;
+constexpr int kBlockPair = 512;
 constexpr int kCopies = 16;
 constexpr int kChunk = 16;
 // Residency rounds ahead whose chunks the first round touches (the replay of
