@@ -131,8 +131,19 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
             if constexpr (GROUPS == 1) return readlane_u64(my_off, i);
             else return __shfl(my_off, (int)(i * GROUPS + g), 64);
         };
+        // d = 512: the rows' rates as three bit planes (bit i of plane b is bit b
+        // of row i's kv), from which a row's rate is taken again where it is
+        // used rather than held in a register for the whole chunk
+        uint64_t kvb0 = 0, kvb1 = 0, kvb2 = 0;
+        if constexpr (GROUPS == 1) {
+            kvb0 = __ballot(my_kv & 1u);
+            kvb1 = __ballot((my_kv >> 1) & 1u);
+            kvb2 = __ballot((my_kv >> 2) & 1u);
+        }
         auto row_kv = [&](uint32_t i) -> uint32_t {
-            if constexpr (GROUPS == 1) return (uint32_t)__builtin_amdgcn_readlane((int)my_kv, (int)i);
+            if constexpr (GROUPS == 1)
+                return (uint32_t)((kvb0 >> i) & 1u) | ((uint32_t)((kvb1 >> i) & 1u) << 1) |
+                       ((uint32_t)((kvb2 >> i) & 1u) << 2);
             else return (uint32_t)__shfl((int)my_kv, (int)(i * GROUPS + g), 64);
         };
         // smallest exponent field (in place) among the chunk's scales
@@ -146,10 +157,12 @@ __global__ __launch_bounds__(BLOCK) void gather_decode_mixed(const uint8_t *__re
                 nb[i] = lane_bits(tab, o, 4u * kv[i], l);
                 ab[i] = scale_bits(tab, o, kv[i] * (uint32_t)(D / 16));
             }
+            if constexpr (GROUPS == 1) asm volatile("" : "+s"(kvb0), "+s"(kvb1), "+s"(kvb2));
 #pragma unroll
             for (int i = 0; i < CI; ++i) {
                 const uint32_t r = i * GROUPS + g;
-                const u32x4 v = decode_any_rate<D, RAW ? kRaw : kScaled, (GROUPS == 1)>(nb[i], kv[i], ab[i], l, g,
+                const uint32_t kvi = GROUPS == 1 ? row_kv((uint32_t)i) : kv[i];
+                const u32x4 v = decode_any_rate<D, RAW ? kRaw : kScaled, (GROUPS == 1)>(nb[i], kvi, ab[i], l, g,
                                                                                           s_lut, lds_off);
                 if (r < cn) store16(out + row_of(c, r) * (D / 2) + 4u * l, v);
                 if constexpr (!RAW) {
